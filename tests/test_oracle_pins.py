@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one part of the oracle to a library routine, a closed form, an invariant,
+brute force on a tiny input or finite differences, so that a dropped term, a wrong sign,
+index or transposed operand in the oracle fails at least one of them.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gca_oracle as O
+from long_context_lm_amd import inputs as I
+
+
+# ----------------------------------------------------------------------------- Philox
+def test_philox_matches_numpy_bit_generator():
+    """numpy.random.Philox is Philox4x64-10; its first block is for counter + 1."""
+    rng = np.random.default_rng(123)
+    for _ in range(64):
+        ctr = rng.integers(0, 2**64, size=4, dtype=np.uint64)
+        ctr[0] |= np.uint64(1)  # odd, so word 0 - 1 does not borrow
+        key = rng.integers(0, 2**64, size=2, dtype=np.uint64)
+        prev = ctr.copy()
+        prev[0] -= np.uint64(1)
+        ref = np.random.Philox(counter=prev, key=key).random_raw(4)
+        mine = O.philox4x64_10(ctr[None, :], key)[0]
+        assert [int(x) for x in mine] == [int(x) for x in ref]
+
+
+def test_philox_vectorised_matches_scalar():
+    ctrs = np.array([[j, 7, (1 << 32) | 3, 0] for j in range(1, 50)], dtype=np.uint64)
+    out = O.philox4x64_10(ctrs, (11, 0))
+    for row, c in zip(out, ctrs):
+        prev = c.copy()
+        prev[0] -= np.uint64(1)
+        ref = np.random.Philox(counter=prev, key=np.array([11, 0], dtype=np.uint64)).random_raw(4)
+        assert [int(x) for x in row] == [int(x) for x in ref]
+
+
+# ----------------------------------------------------------------------------- ln_s
+def _ulp_diff(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.abs(a - b) / np.spacing(np.abs(b))
+
+
+def test_ln_s_within_4_ulp_of_libm():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        np.exp(rng.uniform(-700, 700, size=400_000)),
+        rng.uniform(0.5, 2.0, size=400_000),
+        1.0 + rng.uniform(-1e-6, 1e-6, size=100_000),
+        # the two arguments the Gumbel transform feeds it
+        ((rng.integers(0, 2**52, size=200_000).astype(np.float64) + 0.5) * 2.0**-52),
+    ])
+    x = x[x != 1.0]
+    ref = np.log(x)
+    got = O.ln_s(x)
+    ok = np.abs(ref) > 0
+    assert np.max(_ulp_diff(got[ok], ref[ok])) <= 4.0
+    # exact special cases of the reduction
+    assert O.ln_s(np.array([1.0]))[0] == 0.0
+    assert O.ln_s(np.array([2.0]))[0] == float.fromhex("0x1.62e42fefa39efp-1")
+    for v in (0.5, 4.0, 1e-300, 1e300, 0.7071067811865476, 1.4142135623730951):
+        assert _ulp_diff(O.ln_s(np.array([v]))[0], math.log(v)) <= 4.0
+
+
+# ----------------------------------------------------------------------------- Gumbel
+def test_gumbel_moments():
+    i = np.arange(1_000_000) // 1000 + 5000
+    j = np.arange(1_000_000) % 1000
+    g = O.gumbel_noise(7, 1, 3, i, j).astype(np.float64)
+    euler_gamma = 0.5772156649015329
+    se = math.sqrt(math.pi**2 / 6 / g.size)
+    assert abs(g.mean() - euler_gamma) < 6 * se
+    assert abs(g.var() - math.pi**2 / 6) < 0.02
+    # P(g <= 0) = exp(-1) for the standard Gumbel law
+    assert abs((g <= 0).mean() - math.exp(-1)) < 0.003
+
+
+def test_gumbel_depends_on_every_counter_field():
+    base = O.gumbel_noise(1, 0, 0, np.array([10]), np.array([3]))[0]
+    assert O.gumbel_noise(2, 0, 0, np.array([10]), np.array([3]))[0] != base
+    assert O.gumbel_noise(1, 1, 0, np.array([10]), np.array([3]))[0] != base
+    assert O.gumbel_noise(1, 0, 1, np.array([10]), np.array([3]))[0] != base
+    assert O.gumbel_noise(1, 0, 0, np.array([11]), np.array([3]))[0] != base
+    assert O.gumbel_noise(1, 0, 0, np.array([10]), np.array([4]))[0] != base
+
+
+@pytest.mark.parametrize("tau", [1.0, 2.0])
+def test_gumbel_max_frequencies_follow_softmax(tau):
+    """Gumbel-max: with K = 1 and fixed scores, P(select j) = softmax(s / tau)_j."""
+    n_cand, n_rows = 5, 20000
+    dl = 64
+    lk = np.zeros((1, 1, n_cand, dl), dtype=np.float32)
+    target = np.array([0.0, 0.5, 1.0, -0.5, 0.25], dtype=np.float32)
+    lk[0, 0, :, 0] = target * 8.0  # score = lq . lk / 8 with lq = e_0
+    lq = np.zeros((1, 1, n_rows, dl), dtype=np.float32)
+    lq[..., 0] = 1.0
+    idx, score = O.retrieve(lq, lk, 1, use_gumbel=True, seed=3, tau=tau,
+                            q_chunk_base=n_cand, n_kv=n_cand)
+    s = score[0, 0, 0, 0]
+    assert s == target[idx[0, 0, 0, 0]]
+    counts = np.bincount(idx[0, 0, :, 0], minlength=n_cand)
+    p = np.exp(target.astype(np.float64) / tau)
+    p /= p.sum()
+    chi2 = float(((counts - n_rows * p) ** 2 / (n_rows * p)).sum())
+    assert chi2 < 25.0  # 4 degrees of freedom: P(chi2 > 25) < 1e-4
+
+
+# ----------------------------------------------------------------------------- scores
+def test_canonical_score_equals_rounded_exact_dot():
+    rng = np.random.default_rng(9)
+    lq = torch.from_numpy(rng.standard_normal((40, 64), dtype=np.float32) / 8).to(torch.bfloat16)
+    lk = torch.from_numpy(rng.standard_normal((50, 64), dtype=np.float32) / 8).to(torch.bfloat16)
+    lq64, lk64 = I.as_f64(lq), I.as_f64(lk)
+    s = O.canonical_scores(lq64, lk64, 0.125)
+    for i in range(0, 40, 3):
+        for j in range(0, 50, 7):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(lq64[i], lk64[j]))
+            assert s[i, j] == np.float32(float(exact)) * np.float32(0.125)
+    # fp32 inputs: products are exact in float64 as well
+    lq32 = rng.standard_normal((8, 64)).astype(np.float32)
+    lk32 = rng.standard_normal((8, 64)).astype(np.float32)
+    s32 = O.canonical_scores(lq32, lk32, 1.0)
+    for i in range(8):
+        for j in range(8):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(lq32[i], lk32[j]))
+            assert s32[i, j] == np.float32(float(exact))
+
+
+def test_canonical_score_has_no_negative_zero():
+    lq = np.zeros((1, 64))
+    lk = np.zeros((2, 64))
+    lq[0, 0], lk[1, 0] = 1.0, -0.0
+    s = O.canonical_scores(lq, lk, 0.125)
+    assert not np.signbit(s).any()
+
+
+# ----------------------------------------------------------------------------- top-k
+def _brute_topk(lq, lk, K, use_gumbel, seed, tau, base, n_kv, scale=0.125):
+    """Pure-Python selection: every candidate, Python sorted by (-r, j)."""
+    G, B, n_q, dl = lq.shape
+    idx = np.full((G, B, n_q, K), -1, dtype=np.int32)
+    sc = np.full((G, B, n_q, K), -np.inf, dtype=np.float32)
+    for g in range(G):
+        for b in range(B):
+            for r in range(n_q):
+                i = base + r
+                cands = []
+                for j in range(min(i, n_kv)):
+                    acc = 0.0
+                    for d in range(dl):
+                        acc = acc + float(lq[g, b, r, d]) * float(lk[g, b, j, d])
+                    s = np.float32(np.float32(acc) * np.float32(scale)) + np.float32(0)
+                    rr = s
+                    if use_gumbel:
+                        gn = O.gumbel_noise(seed, g, b, np.array([i]), np.array([j]))[0]
+                        rr = np.float32(s + np.float32(np.float32(tau) * gn)) + np.float32(0)
+                    cands.append((float(rr), j, s))
+                cands = sorted(cands, key=lambda c: (-c[0], c[1]))[:K]
+                for kk, (_, j, s) in enumerate(cands):
+                    idx[g, b, r, kk] = j
+                    sc[g, b, r, kk] = s
+    return idx, sc
+
+
+@pytest.mark.parametrize("use_gumbel", [False, True])
+@pytest.mark.parametrize("base,n_kv", [(0, 12), (3, 7)])
+def test_topk_matches_brute_force(use_gumbel, base, n_kv):
+    rng = np.random.default_rng(17)
+    G, B, n_q, K = 2, 2, 12, 3
+    lq = I.as_f64(torch.from_numpy(rng.standard_normal((G, B, n_q, 64), dtype=np.float32)).to(torch.bfloat16))
+    lk = I.as_f64(torch.from_numpy(rng.standard_normal((G, B, n_kv, 64), dtype=np.float32)).to(torch.bfloat16))
+    idx, sc = O.retrieve(lq, lk, K, use_gumbel=use_gumbel, seed=4, tau=1.0,
+                         q_chunk_base=base, n_kv=n_kv)
+    bidx, bsc = _brute_topk(lq, lk, K, use_gumbel, 4, 1.0, base, n_kv)
+    np.testing.assert_array_equal(idx, bidx)
+    np.testing.assert_array_equal(sc, bsc)
+    # strict causality of the candidate set and padding
+    for g in range(G):
+        for b in range(B):
+            for r in range(n_q):
+                i = base + r
+                valid = idx[g, b, r] >= 0
+                assert valid.sum() == min(K, min(i, n_kv))
+                assert np.all(idx[g, b, r][valid] < min(i, n_kv))
+                assert np.all(np.isneginf(sc[g, b, r][~valid]))
+
+
+def test_topk_ties_go_to_lower_chunk():
+    rng = np.random.default_rng(2)
+    n = 20
+    lk = np.zeros((1, 1, n, 64))
+    base_vec = rng.standard_normal(64).astype(np.float32)
+    for j in range(n):  # duplicates in pairs: (0,1), (2,3), ...
+        lk[0, 0, j] = base_vec * (1 + (j // 2) % 3)
+    lq = np.tile(base_vec.astype(np.float64), (1, 1, n, 1))
+    idx, sc = O.retrieve(lq, lk, 4)
+    for r in range(n):
+        row = [int(x) for x in idx[0, 0, r] if x >= 0]
+        srow = sc[0, 0, r][: len(row)]
+        for a in range(len(row) - 1):
+            assert srow[a] > srow[a + 1] or (srow[a] == srow[a + 1] and row[a] < row[a + 1])
+    # all landmarks equal: the first K chunks, in order
+    lk_eq = np.ones((1, 1, n, 64))
+    lq_eq = np.ones((1, 1, n, 64))
+    idx, sc = O.retrieve(lq_eq, lk_eq, 4)
+    assert list(idx[0, 0, 10]) == [0, 1, 2, 3]
+    assert np.all(sc[0, 0, 10] == np.float32(8.0))
+
+
+def test_planted_passkey_is_top1():
+    rng = np.random.default_rng(8)
+    n = 64
+    lq = rng.standard_normal((1, 1, n, 64)) / 8
+    lk = rng.standard_normal((1, 1, n, 64)) / 8
+    i_star, j_star = 50, 13
+    lk[0, 0, j_star] = 10 * lq[0, 0, i_star]
+    idx, _ = O.retrieve(lq, lk, 8)
+    assert idx[0, 0, i_star, 0] == j_star
+
+
+# ----------------------------------------------------------------------------- forward
+def _small_case(seed=0, G=2, B=2, H=3, n=8, K=3, dtype="f32"):
+    shp = I.Shape(B=B, G=G, H=H, n_q=n, n_kv=n, topk=K)
+    t = I.make_inputs(shp, dtype, seed=seed)
+    x = {k: I.as_f64(v) for k, v in t.items()}
+    idx, sc = O.retrieve(x["lq"], x["lk"], K)
+    return shp, x, idx, sc
+
+
+def test_k1_reduces_to_sdpa():
+    shp, x, idx, sc = _small_case(K=1)
+    o, lse = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=1, attn_scale=0.125)
+    q, k, v = (torch.from_numpy(x[n]) for n in ("q", "k", "v"))
+    for g in range(shp.G):
+        for b in range(shp.B):
+            for t in range(shp.n_q):
+                rows = slice(64 * t, 64 * t + 64)
+                if t < 2:
+                    assert np.all(o[g, b, :, rows] == 0)
+                    continue
+                j = int(idx[g, b, t - 1, 0])
+                keys = slice(64 * j, 64 * j + 64)
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    q[g, b, :, rows], k[b, :, keys], v[b, :, keys], scale=0.125)
+                np.testing.assert_allclose(o[g, b, :, rows], ref.numpy(), rtol=1e-12, atol=1e-12)
+                z = 0.125 * (q[g, b, :, rows] @ k[b, :, keys].transpose(-1, -2))
+                np.testing.assert_allclose(lse[g, b, :, rows, 0], torch.logsumexp(z, -1).numpy(),
+                                           rtol=1e-12, atol=1e-12)
+
+
+def test_fusion_closed_forms():
+    shp, x, idx, sc = _small_case(K=3)
+    # V constant per chunk: O_t = sum_k softmax(score)_k c_{j_k}
+    c = np.arange(shp.n_kv, dtype=np.float64) * 0.37 - 1.1
+    v = np.repeat(c, 64)[None, None, :, None] * np.ones_like(x["v"])
+    o, _ = O.forward(x["q"], x["k"], v, idx, sc, shift=1)
+    for g in range(shp.G):
+        for b in range(shp.B):
+            for t in range(shp.n_q):
+                row = t - 1
+                rows = slice(64 * t, 64 * t + 64)
+                valid = idx[g, b, row] >= 0 if row >= 0 else np.zeros(shp.topk, bool)
+                if not valid.any():
+                    assert np.all(o[g, b, :, rows] == 0)
+                    continue
+                s = sc[g, b, row][valid].astype(np.float64)
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                assert abs(w.sum() - 1) < 1e-12
+                expect = float((w * c[idx[g, b, row][valid]]).sum())
+                np.testing.assert_allclose(o[g, b, :, rows], expect, rtol=1e-12, atol=1e-12)
+    # Q = 0: each slot output is the mean of V over its chunk
+    o0, _ = O.forward(np.zeros_like(x["q"]), x["k"], x["v"], idx, sc, shift=1)
+    g, b, t = 1, 0, 5
+    valid = idx[g, b, t - 1] >= 0
+    s = sc[g, b, t - 1][valid].astype(np.float64)
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    expect = sum(w[n] * x["v"][b, :, 64 * j:64 * j + 64].mean(axis=1)
+                 for n, j in enumerate(idx[g, b, t - 1][valid]))
+    np.testing.assert_allclose(o0[g, b, :, 64 * t], expect, rtol=1e-12, atol=1e-12)
+
+
+def test_causality_future_chunks_do_not_matter():
+    shp, x, idx, sc = _small_case(seed=4, n=10, K=3)
+    c = 6  # query chunk under test; it uses row c-1, whose candidates are chunks < c-1
+    o, lse = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=1)
+    y = {k: v.copy() for k, v in x.items()}
+    rng = np.random.default_rng(1)
+    y["q"][:, :, :, 64 * (c + 1):] += rng.standard_normal(y["q"][:, :, :, 64 * (c + 1):].shape)
+    y["k"][:, :, 64 * (c - 1):] += rng.standard_normal(y["k"][:, :, 64 * (c - 1):].shape)
+    y["v"][:, :, 64 * (c - 1):] += rng.standard_normal(y["v"][:, :, 64 * (c - 1):].shape)
+    y["lq"][:, :, c:] += rng.standard_normal(y["lq"][:, :, c:].shape)
+    y["lk"][:, :, c - 1:] += rng.standard_normal(y["lk"][:, :, c - 1:].shape)
+    idx2, sc2 = O.retrieve(y["lq"], y["lk"], shp.topk)
+    np.testing.assert_array_equal(idx2[:, :, :c], idx[:, :, :c])
+    np.testing.assert_array_equal(sc2[:, :, :c], sc[:, :, :c])
+    o2, lse2 = O.forward(y["q"], y["k"], y["v"], idx2, sc2, shift=1)
+    rows = slice(0, 64 * (c + 1))
+    assert np.array_equal(o2[:, :, :, rows], o[:, :, :, rows])
+    assert np.array_equal(lse2[:, :, :, rows], lse[:, :, :, rows])
+
+
+# ----------------------------------------------------------------------------- backward
+def _torch_gca(q, k, v, idx, score, shift, scale):
+    """Independent torch float64 re-expression of the forward, for autograd."""
+    G, B, H, Lq, d = q.shape
+    n_q = Lq // 64
+    outs = []
+    for g in range(G):
+        per_b = []
+        for b in range(B):
+            chunks = []
+            for t in range(n_q):
+                row = t - shift
+                sel = [] if row < 0 else [kk for kk in range(idx.shape[-1]) if idx[g, b, row, kk] >= 0]
+                if not sel:
+                    chunks.append(torch.zeros(H, 64, d, dtype=q.dtype))
+                    continue
+                w = torch.softmax(score[g, b, row, sel], dim=0)
+                acc = 0
+                for n, kk in enumerate(sel):
+                    j = int(idx[g, b, row, kk])
+                    kj = k[b, :, 64 * j:64 * j + 64]
+                    vj = v[b, :, 64 * j:64 * j + 64]
+                    a = torch.softmax(scale * q[g, b, :, 64 * t:64 * t + 64] @ kj.transpose(-1, -2), -1)
+                    acc = acc + w[n] * (a @ vj)
+                chunks.append(acc)
+            per_b.append(torch.cat(chunks, dim=1))
+        outs.append(torch.stack(per_b))
+    return torch.stack(outs)
+
+
+def test_backward_matches_autograd_of_independent_forward():
+    shp, x, idx, sc = _small_case(seed=3, G=2, B=1, H=2, n=7, K=3)
+    rng = np.random.default_rng(0)
+    dout = rng.standard_normal(x["q"].shape)
+    q, k, v = (torch.tensor(x[n], requires_grad=True) for n in ("q", "k", "v"))
+    s_t = torch.tensor(sc.astype(np.float64), requires_grad=True)
+    out = _torch_gca(q, k, v, idx, s_t, 1, 0.125)
+    o_or, _ = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=1)
+    np.testing.assert_allclose(out.detach().numpy(), o_or, rtol=1e-12, atol=1e-12)
+    out.backward(torch.from_numpy(dout))
+    dq, dk, dv, ds = O.backward(x["q"], x["k"], x["v"], idx, sc, dout, shift=1)
+    np.testing.assert_allclose(dq, q.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk, k.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv, v.grad.numpy(), rtol=1e-10, atol=1e-11)
+    g_s = s_t.grad.numpy()
+    g_s = np.where(idx >= 0, g_s, 0.0)
+    np.testing.assert_allclose(ds, g_s, rtol=1e-10, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    shp, x, idx, sc = _small_case(seed=6, G=1, B=1, H=1, n=6, K=2)
+    rng = np.random.default_rng(1)
+    dout = rng.standard_normal(x["q"].shape)
+    dq, dk, dv, ds = O.backward(x["q"], x["k"], x["v"], idx, sc, dout, shift=1)
+
+    def loss(q, k, v, s):
+        o, _ = O.forward(q, k, v, idx, s, shift=1)
+        return float((o * dout).sum())
+
+    h = 1e-6
+    picks = [("q", (0, 0, 0, 64 * 3 + 5, 7)), ("q", (0, 0, 0, 64 * 5 + 63, 0)),
+             ("k", (0, 0, 64 * int(idx[0, 0, 3, 0]) + 2, 9)), ("v", (0, 0, 64 * int(idx[0, 0, 4, 1]) + 60, 33))]
+    grads = {"q": dq, "k": dk, "v": dv}
+    for name, pos in picks:
+        plus = {n: x[n].copy() for n in ("q", "k", "v")}
+        minus = {n: x[n].copy() for n in ("q", "k", "v")}
+        plus[name][pos] += h
+        minus[name][pos] -= h
+        fd = (loss(plus["q"], plus["k"], plus["v"], sc) - loss(minus["q"], minus["k"], minus["v"], sc)) / (2 * h)
+        assert abs(fd - grads[name][pos]) < 1e-6 * max(1.0, abs(fd))
+    for r, kk in [(3, 0), (3, 1), (4, 1)]:
+        sp = sc.astype(np.float64).copy()
+        sm = sp.copy()
+        sp[0, 0, r, kk] += h
+        sm[0, 0, r, kk] -= h
+        fd = (loss(x["q"], x["k"], x["v"], sp) - loss(x["q"], x["k"], x["v"], sm)) / (2 * h)
+        assert abs(fd - ds[0, 0, r, kk]) < 1e-6 * max(1.0, abs(fd))
+
+
+def test_backward_invariants():
+    shp, x, idx, sc = _small_case(seed=11, G=2, B=2, H=2, n=9, K=3)
+    rng = np.random.default_rng(2)
+    dout = rng.standard_normal(x["q"].shape)
+    dq, dk, dv, ds = O.backward(x["q"], x["k"], x["v"], idx, sc, dout, shift=1)
+    # each row's score gradients sum to zero (softmax), invalid slots and unused rows are zero
+    np.testing.assert_allclose(ds.sum(-1), 0, atol=1e-12)
+    assert np.all(ds[idx < 0] == 0)
+    assert np.all(ds[:, :, -1] == 0)
+    # dK summed over any chunk's 64 keys is zero (each per-slot softmax sums to one)
+    per_chunk = dk.reshape(shp.B, shp.H, shp.n_kv, 64, 64).sum(axis=3)
+    np.testing.assert_allclose(per_chunk, 0, atol=1e-10)
+    # sum of dV = sum over groups of dO over tokens with at least one valid slot
+    has = np.zeros((shp.G, shp.B, shp.n_q), dtype=bool)
+    for t in range(1, shp.n_q):
+        has[:, :, t] = (idx[:, :, t - 1] >= 0).any(-1)
+    mask = np.repeat(has, 64, axis=-1)[:, :, None, :, None]
+    np.testing.assert_allclose(dv.sum(axis=2), (dout * mask).sum(axis=(0, 3)), rtol=1e-10, atol=1e-10)
+    # chunks nobody retrieved get zero dK, dV
+    used = set(int(j) for j in idx[:, :, :-1].ravel() if j >= 0)
+    for j in range(shp.n_kv):
+        if j not in used:
+            assert np.all(dk[:, :, 64 * j:64 * j + 64] == 0)
+            assert np.all(dv[:, :, 64 * j:64 * j + 64] == 0)
