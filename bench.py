@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the GCA hot path on one MI355X.
+
+One step = causal retrieval (Gumbel top-k) + grouped cross-attention forward + backward over one
+batch of the 16K-token training workload (B=8, L=16384 = 256 chunks of 64, H=12, d=64, K=8, G=2,
+bf16, synthetic N(0,1)/8 inputs).  Prints one JSON line: tokens/s with inputs resident in HBM,
+the roofline position of the dominant kernel (HIP events around each kernel launch inside the
+timed region), the CPU oracle timed on a bounded sample of the same workload, and the per-chunk
+retrieve+attend latency over 1M- and 16M-token histories held in HBM.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-inference] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GCA fwd+bwd tokens/s at 16K ctx; per-chunk retrieve+attend latency at 16M"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+UNIT_FLOPS = 2 * 64 * 64 * 64  # one 64x64x64 matrix product (one slot, one head)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def training_step_setup(seed=0):
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    shape = I.TRAIN_16K_G2
+    cfg = gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                     dtype="bf16", use_gumbel=True, seed=1)
+    log("generating inputs", shape)
+    host = I.make_inputs(shape, "bf16", seed=seed, scale=0.125)
+    dev = {k: v.cuda() for k, v in host.items()}
+    G, B, H, nq, K = shape.G, shape.B, shape.H, shape.n_q, shape.topk
+    bufs = {
+        "idx": torch.empty((G, B, nq, K), dtype=torch.int32, device="cuda"),
+        "score": torch.empty((G, B, nq, K), dtype=torch.float32, device="cuda"),
+        "o": torch.empty_like(dev["q"]),
+        "lse": torch.empty((G, B, H, nq * 64, K), dtype=torch.float32, device="cuda"),
+        "dq": torch.empty_like(dev["q"]),
+        "dk": torch.empty_like(dev["k"]),
+        "dv": torch.empty_like(dev["v"]),
+        "dscore": torch.empty((G, B, nq, K), dtype=torch.float32, device="cuda"),
+    }
+    ws_b = torch.empty(gca.workspace_size(gca.OP_BACKWARD, cfg), dtype=torch.uint8, device="cuda")
+    assert gca.workspace_size(gca.OP_RETRIEVE, cfg) == 0
+
+    def step():
+        gca.retrieve(cfg, dev["lq"], dev["lk"], bufs["idx"], bufs["score"])
+        gca.forward(cfg, dev["q"], dev["k"], dev["v"], bufs["idx"], bufs["score"], o=bufs["o"], lse=bufs["lse"])
+        gca.backward(cfg, dev["q"], dev["k"], dev["v"], bufs["idx"], bufs["score"], bufs["lse"], dev["dout"],
+                     ws=ws_b, out=(bufs["dq"], bufs["dk"], bufs["dv"], bufs["dscore"]))
+
+    return shape, cfg, host, dev, bufs, step
+
+
+def kernel_figures(shape, idx_cpu):
+    """Algorithmic flops and HBM bytes per launch of each kernel (compulsory traffic)."""
+    import numpy as np
+
+    G, B, H, nq, nkv, K = shape.G, shape.B, shape.H, shape.n_q, shape.n_kv, shape.topk
+    idx = np.asarray(idx_cpu)
+    used = idx[:, :, : nq - 1] >= 0            # row r feeds query chunk r + 1
+    tiles = int(used.sum()) * H                # (slot, head) pairs of 64x64 tiles
+    tok = B * nq * 64
+    T = tok * H * 64 * 2                       # one [B, H, L, 64] bf16 tensor
+    lse = G * tok * H * K * 4
+    lmk = G * B * (nq + nkv) * 64 * 2
+    sel = G * B * nq * K * 8
+    pairs = G * B * nq * (nq - 1) // 2
+    return {
+        "score_topk": {"flops": 2 * 64 * pairs, "bytes": lmk + sel, "tiles": 0},
+        # forward: S and PV per tile; reads Q, K, V, writes O and LSE
+        "attend_fwd": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + 1 + 1 + G) * T + lse + sel, "tiles": tiles},
+        # query-major backward: dP' and dQ per tile; reads Q, dO, K, V, LSE, writes dQ
+        "bwd_query": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + G) * T + lse + sel, "tiles": tiles},
+        # key-major backward: dK and dV per tile; reads Q, dO, K, V, LSE, writes dK, dV
+        "bwd_key": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + 1 + 1) * T + lse, "tiles": tiles},
+        "csr_build": {"flops": 0, "bytes": sel // 2, "tiles": 0},
+        "score_grad": {"flops": 0, "bytes": sel, "tiles": 0},
+    }
+
+
+def roofline_for(name, fig, ms):
+    t = ms * 1e-3
+    t_mfma = fig["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = fig["bytes"] / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = fig["flops"] / t / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flops": fig["flops"], "algorithmic_bytes": fig["bytes"], "avg_launch_ms": ms}
+    ach = fig["bytes"] / t / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS, "traffic": None,
+            "algorithmic_flops": fig["flops"], "algorithmic_bytes": fig["bytes"], "avg_launch_ms": ms}
+
+
+def cpu_baseline(shape, host):
+    """The oracle on a bounded sample: batch row 0 of the workload (both groups, all heads)."""
+    from long_context_lm_amd import inputs as I
+    from oracle import gca_oracle as O
+
+    x = {k: I.as_f64(v[:, 0:1] if k in ("lq", "lk", "q", "dout") else v[0:1]) for k, v in host.items()}
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    idx, sc = O.retrieve(x["lq"], x["lk"], shape.topk, use_gumbel=True, seed=1)
+    _o, _lse = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=1)
+    O.backward(x["q"], x["k"], x["v"], idx, sc, x["dout"], shift=1)
+    dt = time.perf_counter() - t0
+    tokens = shape.n_q * 64
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch row 0 of the workload ({tokens} tokens, G=2, H=12): retrieve+fwd+bwd, "
+                      f"{dt:.1f} s on {os.cpu_count()} host CPUs (BLAS threads {threads})"}
+
+
+def inference_latency(shape, iters=50):
+    """Per-chunk retrieve + attend latency over a long history held in HBM (warm and cold)."""
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    cfg = gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                     dtype="bf16", q_chunk_base=shape.q_chunk_base, shift=shape.shift)
+    host = I.make_inputs(shape, "bf16", seed=0, names=("lq", "lk", "q"))
+    lq, lk, q = (host[n].cuda() for n in ("lq", "lk", "q"))
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    k = torch.randn(shape.tensor_shape("k"), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(shape.tensor_shape("v"), generator=gen, device="cuda", dtype=torch.bfloat16)
+    idx = torch.empty((shape.G, shape.B, shape.n_q, shape.topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty_like(idx, dtype=torch.float32)
+    o = torch.empty_like(q)
+    nws = gca.workspace_size(gca.OP_RETRIEVE, cfg)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # 1 GiB > 256 MB MALL
+
+    def one():
+        gca.retrieve(cfg, lq, lk, idx, sc, ws=ws if nws else None)
+        gca.forward(cfg, q, k, v, idx, sc, need_lse=False, o=o)
+
+    for _ in range(5):
+        one()
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("warm", "cold"):
+        times = []
+        for _ in range(iters):
+            if mode == "cold":
+                flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            one()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        times.sort()
+        res[mode] = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
+                     "p90_us": times[(9 * len(times)) // 10]}
+    lmk_bytes = shape.G * shape.B * shape.n_kv * 64 * 2
+    gather = shape.G * shape.B * shape.topk * shape.H * 2 * 64 * 64 * 2
+    res["hbm_bytes"] = lmk_bytes + gather
+    res["hbm_bound_us"] = res["hbm_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
+    del k, v, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-inference", action="store_true", help="skip the 1M/16M-history latency runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the GCA path here runs on a single MI355X with no "
+              "sharding or collectives; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gca.load()
+    shape, cfg, host, dev, bufs, step = training_step_setup()
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gca.profile_collect()
+    gca.profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    gca.profile_enable(False)
+    kern = gca.profile_collect()
+    ms = start.elapsed_time(end) / args.steps
+    tokens = shape.B * shape.n_q * 64
+    log(f"step {ms:.3f} ms -> {tokens / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+
+    figs = kernel_figures(shape, bufs["idx"].cpu().numpy())
+    kernels = {}
+    for name, (tot, n) in kern.items():
+        avg = tot / max(n, 1)
+        kernels[name] = {"avg_ms": avg, "launches": n}
+        if name in figs and figs[name]["flops"] + figs[name]["bytes"] > 0:
+            r = roofline_for(name, figs[name], avg)
+            kernels[name].update({"bound": r["bound"], "frac": r["frac"], "achieved": r["achieved"], "unit": r["unit"]})
+    dominant = max(kern.items(), key=lambda kv: kv[1][0])[0]
+    roof = roofline_for(dominant, figs[dominant], kern[dominant][0] / kern[dominant][1])
+    # whole-step position against the algorithmic roofline (max of the two ceilings per kernel)
+    step_floor_ms = sum(max(f["flops"] / (PEAK_BF16_TFLOPS * 1e12), f["bytes"] / (PEAK_HBM_GBS * 1e9))
+                        for f in figs.values()) * 1e3
+    roof["step_floor_ms"] = step_floor_ms
+    roof["step_frac"] = step_floor_ms / ms
+    for k, v in kernels.items():
+        log(f"  {k:12s} {v['avg_ms'] * 1e3:9.1f} us  x{v['launches']}"
+            + (f"  {v['bound']} {v['frac'] * 100:5.1f}%" if "frac" in v else ""))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(shape, host)
+        log(f"  oracle {cpu['value']:.0f} tokens/s")
+
+    infer = None
+    del dev, bufs
+    torch.cuda.empty_cache()
+    if not args.no_inference:
+        infer = {}
+        for label, shp in (("1M", I.INFER_1M), ("16M", I.INFER_16M)):
+            log("inference latency", label)
+            infer[label] = inference_latency(shp)
+            log(f"  {label}: warm {infer[label]['warm']['median_us']:.1f} us, "
+                f"cold {infer[label]['cold']['median_us']:.1f} us")
+
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GCA retrieve+fwd+bwd, Gumbel top-k, B=8 L=16384 (256 chunks of 64) "
+                               "H=12 d=64 K=8 G=2, inputs N(0,1)/8", "global_batch": shape.B,
+                   "seq_len": shape.n_q * 64, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "inference_latency": infer,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

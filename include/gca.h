@@ -1,0 +1,171 @@
+/*
+ * gca.h -- C ABI of the Grouped Cross-Attention (GCA) library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows the pages on "Efficient Length-Generalizable Attention via Causal
+ * Retrieval for Long-Context Language Modeling" (ICML 2025):
+ *   [Notes]  zhaoyang97.github.io Paper-Notes page on the paper;
+ *   [Forum]  openreview.net forum page (abstract).
+ * A sequence is cut into chunks of S = 64 tokens [Notes, Overall framework].  The landmark of
+ * chunk i is scored against the landmark of every strictly earlier chunk and the top-k are
+ * kept, optionally after adding Gumbel noise [Notes, Key designs: causal retrieval; Gumbel
+ * top-k].  Every token of the next chunk attends to each retrieved chunk with its own softmax,
+ * and the k outputs are fused with a softmax of the retrieval scores, so the scores receive
+ * gradients [Notes, Key designs: GCA; Background].  K/V are shared by all retrieval groups
+ * [Notes, Key designs: GCA].
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major (last index fastest), in device memory, owned by the
+ *     caller.  The library never allocates, frees or synchronises, keeps no state between
+ *     calls, and enqueues all work on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Floating tensors q, k, v, o, dout, dq, dk, dv, lq, lk use `problem->dtype`
+ *     (bf16 or fp32).  idx is int32; score, lse and dscore are fp32.
+ *   - Shapes (n_q = n_q_chunks, n_kv = n_kv_chunks, S = 64, d = d_head, dl = d_lmk):
+ *       lq     [G, B, n_q,   dl]      query landmarks (one per retrieval row)
+ *       lk     [G, B, n_kv,  dl]      key landmarks (one per history chunk)
+ *       q, o, dout, dq  [G, B, H, n_q*S, d]
+ *       k, v, dk, dv    [B, H, n_kv*S, d]      shared by all G groups
+ *       idx, score, dscore [G, B, n_q, topk]
+ *       lse    [G, B, H, n_q*S, topk]
+ *   - Row r of a retrieval is global chunk i = q_chunk_base + r; its candidates are the
+ *     chunks j < min(i, n_kv).  Query chunk t uses row t - shift (shift = 1 in training, where
+ *     the landmark of chunk t-1 retrieves for chunk t; shift = 0 when the caller passes the
+ *     landmark of the chunk being generated).  Query chunks whose row is missing or has no
+ *     valid slot get o = 0, lse = -inf, dq = 0.
+ *   - Pointers to the floating tensors and to lq, lk must be 16-byte aligned; idx, score,
+ *     lse, dscore 4-byte aligned.  Otherwise GCA_ERR_MISALIGNED.
+ *   - Every call validates all arguments on the host before touching the GPU and enqueues
+ *     nothing when it returns an error.  A launch failure returns GCA_ERR_HIP; the HIP code
+ *     is then available from gca_last_hip_error() (per calling thread).  Faults inside
+ *     kernels surface at the caller's next synchronisation.
+ *   - Outputs are fully overwritten; inputs are read only.  Results are bit-identical from
+ *     run to run (no floating-point atomics anywhere).
+ *   - gca_retrieve and gca_forward with n_q_chunks = 0 validate and return GCA_OK without
+ *     launching anything; gca_backward with n_q_chunks = 0 still writes zero dk and dv.
+ */
+#ifndef GCA_H
+#define GCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GCA_OK = 0,
+  GCA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, bad enum, non-finite scale */
+  GCA_ERR_UNSUPPORTED = 2,         /* S, d_head, d_lmk other than 64, topk > 16, size limits  */
+  GCA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below gca_workspace_size()                     */
+  GCA_ERR_MISALIGNED = 4,          /* a tensor pointer breaks the alignment rule above        */
+  GCA_ERR_HIP = 5                  /* a HIP launch failed; see gca_last_hip_error()           */
+} gca_status;
+
+typedef enum { GCA_BF16 = 0, GCA_F32 = 1 } gca_dtype;
+
+typedef enum { GCA_OP_RETRIEVE = 0, GCA_OP_FORWARD = 1, GCA_OP_BACKWARD = 2 } gca_op;
+
+/* Sizes and options of one problem.  Fields are read, never written. */
+typedef struct {
+  int32_t B;              /* batch                                            >= 1 */
+  int32_t G;              /* retrieval groups (independent landmark sets)     >= 1 */
+  int32_t H;              /* attention heads                                  >= 1 */
+  int32_t S;              /* chunk length: must be 64                              */
+  int64_t n_q_chunks;     /* retrieval rows / query chunks in this call       >= 0 */
+  int64_t q_chunk_base;   /* global chunk index of row 0                      >= 0 */
+  int64_t n_kv_chunks;    /* chunks of K, V and key landmarks present         >= 0 */
+  int32_t d_head;         /* must be 64                                            */
+  int32_t d_lmk;          /* landmark dimension: must be 64                        */
+  int32_t topk;           /* K, 1..16                                              */
+  int32_t dtype;          /* gca_dtype of the floating tensors                     */
+  float attn_scale;       /* z = attn_scale * <q, k>; usually 1/sqrt(d_head)       */
+  float score_scale;      /* s = score_scale * <lq, lk>; usually 1/sqrt(d_lmk)     */
+  int32_t use_gumbel;     /* 0 or 1: perturb the scores before the top-k           */
+  int32_t shift;          /* 0 or 1: query chunk t uses retrieval row t - shift    */
+  uint64_t seed;          /* Philox key word 0 for the Gumbel noise                */
+  float gumbel_tau;       /* noise scale tau >= 0 (1 = standard Gumbel top-k)      */
+  int32_t reserved;       /* must be 0                                             */
+} gca_problem;
+
+/*
+ * Device workspace (bytes) that `op` needs for `problem`; 0 means ws may be NULL.
+ * Pure host function.  Errors: GCA_ERR_INVALID_ARGUMENT (bad op, NULL pointers, invalid
+ * problem), GCA_ERR_UNSUPPORTED.
+ */
+gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes);
+
+/*
+ * Causal retrieval [Notes, Key designs: causal retrieval; Gumbel top-k].
+ * For every (g, b, row r) with i = q_chunk_base + r:
+ *   s_ij = fl32(fl32(sum_{d=0}^{dl-1} lq[i,d] * lk[j,d]) * score_scale), the sum taken exactly
+ *          as a float64 sequential sum over d (products of bf16/fp32 values are exact), -0
+ *          canonicalised to +0;
+ *   r_ij = s_ij, or with use_gumbel r_ij = fl32(s_ij + fl32(tau * g_ij)) where
+ *          g_ij = fl32(-ln_s(-ln_s(u))), u = ((x >> 12) + 1/2) 2^-52, x = word 0 of
+ *          Philox4x64-10(key = (seed, 0), counter = (j, i, (g << 32) | b, 0)) and ln_s the
+ *          fixed atanh-series logarithm (float64, no fused multiply-add);
+ *   the K candidates j < min(i, n_kv) with the largest r (ties toward lower j) are written to
+ *   idx[g,b,r,:] in order (r descending, j ascending) with their clean s_ij in score[g,b,r,:];
+ *   unused slots get idx = -1 and score = -inf.
+ * lq, lk: inputs (see shapes).  idx, score: outputs.  ws: >= gca_workspace_size(RETRIEVE).
+ */
+gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* lk,
+                        int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * GCA forward [Notes, Key designs: GCA].  For query chunk t with row = t - shift, valid slots
+ * k (0 <= idx[k] < n_kv; gca_retrieve only produces j < min(i, n_kv)), w = softmax over the
+ * valid slots of score[g,b,row,:]:
+ *   O_{t,k} = softmax_u(attn_scale * q_t . K_u) V_u over the 64 keys u of chunk idx[k],
+ *   o_t     = sum_k w_k O_{t,k},   lse[t,k] = logsumexp_u(attn_scale * q_t . K_u) (-inf if
+ *   slot k is invalid).
+ * q, k, v, idx, score: inputs; o: output; lse: output, or NULL when no backward will follow.
+ * Arithmetic: bf16 inputs use bf16 matrix cores with fp32 accumulation and fp32 softmax; fp32
+ * inputs use fp32 matrix cores.  ws: >= gca_workspace_size(FORWARD) (currently 0).
+ */
+gca_status gca_forward(const gca_problem* problem, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const float* score, void* o, float* lse, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * GCA backward: gradients of sum(dout * o) with the retrieved idx held fixed [Notes,
+ * Background: the retrieval scores act as weights, so the loss gradient reaches them].
+ *   e_{t,k}  = <dout_t, O_{t,k}>,  dw_k = sum over the chunk's 64 tokens and all heads of e,
+ *   dscore_k = w_k (dw_k - sum_k' w_k' dw_k')  (0 on invalid slots and unused rows),
+ *   dz_u     = w_k a_u (<dout_t, V_u> - e_{t,k}),
+ *   dq_t     = attn_scale sum_{k,u} dz_u K_u,
+ *   dk_u     = attn_scale sum dz_u q_t,   dv_u = sum w_k a_u dout_t, both summed over all
+ *              groups and every (token, slot) that retrieved the chunk of u (zero if none).
+ * q, k, v, idx, score, lse (from gca_forward), dout: inputs; dq, dk, dv, dscore: outputs.
+ * dk and dv are accumulated in fp32 in a fixed order and rounded once to dtype.
+ * ws: >= gca_workspace_size(BACKWARD).  GCA_ERR_UNSUPPORTED if one batch row holds more than
+ * 8192 (group, row, slot) retrievals (G * n_q * topk > 8192).
+ */
+gca_status gca_backward(const gca_problem* problem, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const float* score, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* dscore, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Static English text for a status code ("unknown status" for values outside the enum). */
+const char* gca_status_string(gca_status status);
+
+/* hipError_t value of the last failed HIP call made by this thread inside the library
+ * (0 if none). */
+int gca_last_hip_error(void);
+
+/*
+ * Kernel timing, for measurement tools.  While enabled (on != 0), every kernel the library
+ * launches from the calling thread is bracketed by HIP events recorded on its stream.
+ * gca_profile_collect() waits for the recorded events, writes up to `cap` entries (static
+ * kernel names, summed milliseconds and launch counts) and clears the record; *n receives the
+ * number of distinct kernels.  Disabled by default; costs nothing when disabled.
+ */
+gca_status gca_profile_enable(int on);
+gca_status gca_profile_collect(int cap, const char** names, double* total_ms, int64_t* counts,
+                               int* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCA_H */

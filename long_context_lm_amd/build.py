@@ -1,0 +1,74 @@
+"""Build the GCA HIP library (libgca.so) in-tree for gfx950.
+
+    python -m long_context_lm_amd.build        # compiles every source, always
+
+Objects go to ``_build/`` at the repository root; the shared library lands next to this file
+so that it travels with the source tree.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = ["csrc/retrieve.hip", "csrc/attend.hip", "csrc/gca_api.hip"]
+LIB = os.path.join(HERE, "libgca.so")
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-I", os.path.join(ROOT, "include"),
+    # no packed fp32 instructions (v_pk_*_f32) anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the GCA library)")
+
+
+def _compile(src: str, obj: str) -> tuple[str, int, str]:
+    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; that is harmless
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    return src, r.returncode, err
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libgca.so; returns the library path."""
+    bdir = os.path.join(ROOT, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, os.path.basename(s).replace(".hip", ".o")) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
+        results = list(ex.map(_compile, SOURCES, objs))
+    failed = False
+    for src, rc, err in results:
+        if err.strip() and (verbose or rc != 0):
+            print(f"[build] {src}:\n{err}", file=sys.stderr)
+        failed |= rc != 0
+    if failed:
+        raise RuntimeError("GCA library compilation failed")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,371 @@
+// C ABI of the GCA library: argument validation, workspace carving and kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no state between calls (the optional
+// kernel timer aside).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/gca.h"
+#include "gca_internal.hpp"
+
+namespace gca {
+
+const char* kernel_name(int id) {
+  static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd", "csr_build",
+                                           "bwd_query",  "bwd_key",    "score_grad"};
+  return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
+}
+
+namespace {
+
+thread_local int t_last_hip_error = 0;
+
+struct ProfRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+struct ProfState {
+  bool on = false;
+  std::vector<ProfRecord> records;
+};
+thread_local ProfState t_prof;
+
+constexpr int kRetrieveThreads = 256;
+constexpr int kRetrieveMinBlock = 1024;  // candidates per block before splitting a row
+constexpr int kRetrieveMaxBlocks = 256;  // partial lists per row merged by the second kernel
+constexpr int64_t kCsrCap = 8192;        // retrievals per batch row the inverse index sorts
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Launch `fn` and, when the timer is on, bracket it with events on `stream`.
+template <typename F>
+gca_status launch(int kernel, hipStream_t stream, F fn) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (t_prof.on) {
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess ||
+        hipEventRecord(a, stream) != hipSuccess) {
+      t_last_hip_error = static_cast<int>(hipGetLastError());
+      return GCA_ERR_HIP;
+    }
+  }
+  const hipError_t err = fn();
+  if (err != hipSuccess) {
+    t_last_hip_error = static_cast<int>(err);
+    return GCA_ERR_HIP;
+  }
+  if (t_prof.on) {
+    if (hipEventRecord(b, stream) != hipSuccess) {
+      t_last_hip_error = static_cast<int>(hipGetLastError());
+      return GCA_ERR_HIP;
+    }
+    t_prof.records.push_back({kernel, a, b});
+  }
+  return GCA_OK;
+}
+
+gca_status validate_problem(const gca_problem* p) {
+  if (p == nullptr) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->B < 1 || p->G < 1 || p->H < 1) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->n_q_chunks < 0 || p->q_chunk_base < 0 || p->n_kv_chunks < 0) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->topk < 1) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != GCA_BF16 && p->dtype != GCA_F32) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->use_gumbel != 0 && p->use_gumbel != 1) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->shift != 0 && p->shift != 1) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->reserved != 0) return GCA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->attn_scale) || !std::isfinite(p->score_scale)) return GCA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->gumbel_tau) || p->gumbel_tau < 0.f) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->S != 64 || p->d_head != 64 || p->d_lmk != 64) return GCA_ERR_UNSUPPORTED;
+  if (p->topk > 16) return GCA_ERR_UNSUPPORTED;
+  // index ranges: chunk ids travel as int32, grids as 32-bit block counts
+  const int64_t big = (int64_t{1} << 31) - 1;
+  if (p->n_kv_chunks > big || p->q_chunk_base + p->n_q_chunks > big) return GCA_ERR_UNSUPPORTED;
+  const int64_t gbh = static_cast<int64_t>(p->G) * p->B * p->H;
+  if (p->n_q_chunks > 0 && gbh > big / p->n_q_chunks) return GCA_ERR_UNSUPPORTED;
+  if (p->n_kv_chunks > 0 && static_cast<int64_t>(p->B) * p->H > big / p->n_kv_chunks) return GCA_ERR_UNSUPPORTED;
+  return GCA_OK;
+}
+
+struct RetrievePlan {
+  int32_t nblk, cpt;
+  size_t ws;
+};
+
+RetrievePlan plan_retrieve(const gca_problem* p) {
+  RetrievePlan r{1, 1, 0};
+  if (p->n_q_chunks == 0) return r;
+  const int64_t last_row = p->q_chunk_base + p->n_q_chunks - 1;
+  const int64_t max_cand = last_row < p->n_kv_chunks ? last_row : p->n_kv_chunks;
+  int64_t nblk = (max_cand + kRetrieveMinBlock - 1) / kRetrieveMinBlock;
+  if (nblk < 1) nblk = 1;
+  if (nblk > kRetrieveMaxBlocks) nblk = kRetrieveMaxBlocks;
+  int64_t cpt = (max_cand + kRetrieveThreads * nblk - 1) / (kRetrieveThreads * nblk);
+  if (cpt < 1) cpt = 1;
+  r.nblk = static_cast<int32_t>(nblk);
+  r.cpt = static_cast<int32_t>(cpt);
+  if (nblk > 1) {
+    const size_t n = static_cast<size_t>(p->G) * p->B * p->n_q_chunks * nblk * p->topk;
+    r.ws = align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(float));
+  }
+  return r;
+}
+
+struct BackwardLayout {
+  size_t delta, dw_part, wts, pairs, seg, total;
+};
+
+BackwardLayout plan_backward(const gca_problem* p) {
+  BackwardLayout l{};
+  if (p->n_q_chunks == 0 && p->n_kv_chunks == 0) return l;  // nothing to compute or write
+  const size_t G = p->G, B = p->B, H = p->H, K = p->topk;
+  const size_t nq = static_cast<size_t>(p->n_q_chunks), nkv = static_cast<size_t>(p->n_kv_chunks);
+  size_t off = 0;
+  l.delta = off;
+  off += align_up(G * B * H * nq * 64 * K * sizeof(float));
+  l.dw_part = off;
+  off += align_up(G * B * nq * H * K * sizeof(float));
+  l.wts = off;
+  off += align_up(G * B * nq * K * sizeof(float));
+  l.pairs = off;
+  off += align_up(B * G * nq * K * sizeof(int32_t));
+  l.seg = off;
+  off += align_up(B * (nkv + 1) * sizeof(int32_t));
+  l.total = off;
+  return l;
+}
+
+gca_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (ws_bytes < need) return GCA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && ws == nullptr) return GCA_ERR_INVALID_ARGUMENT;
+  if (need > 0 && !aligned(ws, kAlign)) return GCA_ERR_MISALIGNED;
+  return GCA_OK;
+}
+
+gca_status check_tensor(const void* ptr, bool nonempty, uintptr_t align) {
+  if (!nonempty) return GCA_OK;
+  if (ptr == nullptr) return GCA_ERR_INVALID_ARGUMENT;
+  if (!aligned(ptr, align)) return GCA_ERR_MISALIGNED;
+  return GCA_OK;
+}
+
+#define GCA_TRY(expr)                   \
+  do {                                  \
+    const gca_status _s = (expr);       \
+    if (_s != GCA_OK) return _s;        \
+  } while (0)
+
+AttendParams attend_params(const gca_problem* p) {
+  AttendParams a{};
+  a.n_q = p->n_q_chunks;
+  a.n_kv = p->n_kv_chunks;
+  a.G = p->G;
+  a.B = p->B;
+  a.H = p->H;
+  a.K = p->topk;
+  a.shift = p->shift;
+  a.pair_cap = static_cast<int32_t>(static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk);
+  a.attn_scale = p->attn_scale;
+  return a;
+}
+
+}  // namespace
+}  // namespace gca
+
+using namespace gca;
+
+extern "C" {
+
+gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes) {
+  if (bytes == nullptr) return GCA_ERR_INVALID_ARGUMENT;
+  GCA_TRY(validate_problem(problem));
+  switch (op) {
+    case GCA_OP_RETRIEVE: *bytes = plan_retrieve(problem).ws; return GCA_OK;
+    case GCA_OP_FORWARD: *bytes = 0; return GCA_OK;
+    case GCA_OP_BACKWARD:
+      if (static_cast<int64_t>(problem->G) * problem->n_q_chunks * problem->topk > kCsrCap)
+        return GCA_ERR_UNSUPPORTED;
+      *bytes = plan_backward(problem).total;
+      return GCA_OK;
+    default: return GCA_ERR_INVALID_ARGUMENT;
+  }
+}
+
+gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* lk, int32_t* idx,
+                        float* score, void* ws, size_t ws_bytes, void* stream) {
+  GCA_TRY(validate_problem(problem));
+  const gca_problem* p = problem;
+  const bool any = p->n_q_chunks > 0;
+  GCA_TRY(check_tensor(lq, any, 16));
+  GCA_TRY(check_tensor(lk, any && p->n_kv_chunks > 0, 16));
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(score, any, 4));
+  const RetrievePlan plan = plan_retrieve(p);
+  GCA_TRY(check_ws(plan.ws, ws, ws_bytes));
+  if (!any) return GCA_OK;
+
+  RetrieveParams rp{};
+  rp.lq = lq;
+  rp.lk = lk;
+  rp.idx = idx;
+  rp.score = score;
+  rp.n_q = p->n_q_chunks;
+  rp.base = p->q_chunk_base;
+  rp.n_kv = p->n_kv_chunks;
+  rp.G = p->G;
+  rp.B = p->B;
+  rp.K = p->topk;
+  rp.nblk = plan.nblk;
+  rp.cpt = plan.cpt;
+  rp.score_scale = p->score_scale;
+  rp.use_gumbel = p->use_gumbel;
+  rp.seed = p->seed;
+  rp.tau = p->gumbel_tau;
+  if (plan.nblk > 1) {
+    const size_t n = static_cast<size_t>(p->G) * p->B * p->n_q_chunks * plan.nblk * p->topk;
+    rp.part_key = static_cast<uint64_t*>(ws);
+    rp.part_s = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(n * sizeof(uint64_t)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = p->dtype == GCA_F32;
+  GCA_TRY(launch(kScoreTopk, s, [&] { return launch_score_topk(rp, f32, s); }));
+  if (plan.nblk > 1) GCA_TRY(launch(kTopkMerge, s, [&] { return launch_topk_merge(rp, s); }));
+  return GCA_OK;
+}
+
+gca_status gca_forward(const gca_problem* problem, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const float* score, void* o, float* lse, void* ws,
+                       size_t ws_bytes, void* stream) {
+  GCA_TRY(validate_problem(problem));
+  const gca_problem* p = problem;
+  const bool any = p->n_q_chunks > 0;
+  const bool kv = any && p->n_kv_chunks > 0;
+  GCA_TRY(check_tensor(q, any, 16));
+  GCA_TRY(check_tensor(k, kv, 16));
+  GCA_TRY(check_tensor(v, kv, 16));
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(score, any, 4));
+  GCA_TRY(check_tensor(o, any, 16));
+  if (lse != nullptr) GCA_TRY(check_tensor(lse, any, 4));
+  GCA_TRY(check_ws(0, ws, ws_bytes));
+  if (!any) return GCA_OK;
+
+  AttendParams a = attend_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.score = score;
+  a.o = o;
+  a.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = p->dtype == GCA_F32;
+  return launch(kAttendFwd, s, [&] { return launch_attend_fwd(a, f32, s); });
+}
+
+gca_status gca_backward(const gca_problem* problem, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const float* score, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv, float* dscore, void* ws, size_t ws_bytes,
+                        void* stream) {
+  GCA_TRY(validate_problem(problem));
+  const gca_problem* p = problem;
+  if (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk > kCsrCap) return GCA_ERR_UNSUPPORTED;
+  const bool any = p->n_q_chunks > 0;
+  const bool kv = p->n_kv_chunks > 0;
+  GCA_TRY(check_tensor(q, any, 16));
+  GCA_TRY(check_tensor(k, kv, 16));
+  GCA_TRY(check_tensor(v, kv, 16));
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(score, any, 4));
+  GCA_TRY(check_tensor(lse, any, 4));
+  GCA_TRY(check_tensor(dout, any, 16));
+  GCA_TRY(check_tensor(dq, any, 16));
+  GCA_TRY(check_tensor(dk, kv, 16));
+  GCA_TRY(check_tensor(dv, kv, 16));
+  GCA_TRY(check_tensor(dscore, any, 4));
+  const BackwardLayout L = plan_backward(p);
+  GCA_TRY(check_ws(L.total, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!any && !kv) return GCA_OK;
+
+  AttendParams a = attend_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.score = score;
+  a.lse_in = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dscore = dscore;
+  char* w = static_cast<char*>(ws);
+  a.delta = reinterpret_cast<float*>(w + L.delta);
+  a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
+  a.wts = reinterpret_cast<float*>(w + L.wts);
+  a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
+  a.seg = reinterpret_cast<int32_t*>(w + L.seg);
+  const bool f32 = p->dtype == GCA_F32;
+  // With no query chunk, only the inverse index (empty) and the key-major pass (which writes
+  // zero dk, dv for chunks nobody retrieved) run.
+  GCA_TRY(launch(kCsrBuild, s, [&] { return launch_csr_build(a, s); }));
+  if (any) GCA_TRY(launch(kBwdQuery, s, [&] { return launch_bwd_query(a, f32, s); }));
+  if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
+  if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
+  return GCA_OK;
+}
+
+const char* gca_status_string(gca_status status) {
+  switch (status) {
+    case GCA_OK: return "ok";
+    case GCA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GCA_ERR_UNSUPPORTED: return "unsupported problem size or option";
+    case GCA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GCA_ERR_MISALIGNED: return "misaligned tensor pointer";
+    case GCA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gca_last_hip_error(void) { return t_last_hip_error; }
+
+gca_status gca_profile_enable(int on) {
+  t_prof.on = on != 0;
+  return GCA_OK;
+}
+
+gca_status gca_profile_collect(int cap, const char** names, double* total_ms, int64_t* counts, int* n) {
+  if (n == nullptr || cap < 0 || (cap > 0 && (names == nullptr || total_ms == nullptr || counts == nullptr)))
+    return GCA_ERR_INVALID_ARGUMENT;
+  double ms[kNumKernels] = {0};
+  int64_t cnt[kNumKernels] = {0};
+  gca_status st = GCA_OK;
+  for (const ProfRecord& r : t_prof.records) {
+    float e = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&e, r.start, r.stop) != hipSuccess) {
+      t_last_hip_error = static_cast<int>(hipGetLastError());
+      st = GCA_ERR_HIP;
+    }
+    ms[r.kernel] += e;
+    cnt[r.kernel] += 1;
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  t_prof.records.clear();
+  int m = 0;
+  for (int k = 0; k < kNumKernels; ++k) {
+    if (cnt[k] == 0) continue;
+    if (m < cap) {
+      names[m] = kernel_name(k);
+      total_ms[m] = ms[k];
+      counts[m] = cnt[k];
+    }
+    ++m;
+  }
+  *n = m;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Host-side launch descriptors shared by the GCA kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gca {
+
+// Which kernel a launch belongs to (names reported by the kernel timer).
+enum KernelId {
+  kScoreTopk = 0,
+  kTopkMerge,
+  kAttendFwd,
+  kCsrBuild,
+  kBwdQuery,
+  kBwdKey,
+  kScoreGrad,
+  kNumKernels
+};
+const char* kernel_name(int id);
+
+struct RetrieveParams {
+  const void* lq;
+  const void* lk;
+  int32_t* idx;
+  float* score;
+  uint64_t* part_key;   // [rows, nblk, K] partial keys (two-stage only)
+  float* part_s;        // [rows, nblk, K] partial clean scores
+  int64_t n_q, base, n_kv;
+  int32_t G, B, K;
+  int32_t nblk;         // candidate blocks per row (1 = single stage)
+  int32_t cpt;          // candidates per thread per block
+  float score_scale;
+  int32_t use_gumbel;
+  uint64_t seed;
+  float tau;
+};
+
+struct AttendParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  const float* score;
+  const float* lse_in;  // backward: forward log-sum-exp
+  const void* dout;
+  void* o;              // forward output
+  float* lse;           // forward output (may be null)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dscore;
+  float* delta;         // [G, B, H, Lq, K]  e_{t,k} = <dout_t, O_{t,k}>
+  float* dw_part;       // [G, B, n_q, H, K] per-head sums of e over a chunk's tokens
+  float* wts;           // [G, B, n_q, K] fusion weights (0 on invalid slots)
+  int32_t* pairs;       // [B, cap] retrievals sorted by key chunk
+  int32_t* seg;         // [B, n_kv + 1] segment offsets into pairs
+  int64_t n_q, n_kv;
+  int32_t G, B, H, K, shift;
+  int32_t pair_cap;     // G * n_q * K
+  float attn_scale;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s);
+hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s);
+hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s);
+hipError_t launch_csr_build(const AttendParams& p, hipStream_t s);
+hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s);
+hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s);
+hipError_t launch_score_grad(const AttendParams& p, hipStream_t s);
+
+}  // namespace gca

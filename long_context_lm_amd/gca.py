@@ -1,0 +1,234 @@
+"""Thin ctypes binding of the GCA C ABI (include/gca.h).
+
+Argument marshalling only: every step of retrieval, attention, fusion and backward runs in the
+HIP kernels of libgca.so.  PyTorch provides device memory and the current stream.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgca.so")
+
+GCA_OK = 0
+OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
+DTYPES = {"bf16": 0, "f32": 1}
+
+
+class Problem(ctypes.Structure):
+    """Mirror of gca_problem (natural C alignment, 88 bytes)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("G", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("S", ctypes.c_int32),
+        ("n_q_chunks", ctypes.c_int64),
+        ("q_chunk_base", ctypes.c_int64),
+        ("n_kv_chunks", ctypes.c_int64),
+        ("d_head", ctypes.c_int32),
+        ("d_lmk", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("attn_scale", ctypes.c_float),
+        ("score_scale", ctypes.c_float),
+        ("use_gumbel", ctypes.c_int32),
+        ("shift", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+        ("gumbel_tau", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+EXPORTS = (
+    "gca_workspace_size",
+    "gca_retrieve",
+    "gca_forward",
+    "gca_backward",
+    "gca_status_string",
+    "gca_last_hip_error",
+    "gca_profile_enable",
+    "gca_profile_collect",
+)
+
+_lib = None
+
+
+class GcaError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        lib = load()
+        text = lib.gca_status_string(status).decode()
+        hip = lib.gca_last_hip_error() if status == 5 else 0
+        super().__init__(f"{call} failed: {text} (status {status}{', hip error %d' % hip if hip else ''})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libgca.so (built by long_context_lm_amd.build); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: run `python -m long_context_lm_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER(Problem)
+    lib.gca_workspace_size.argtypes = [ctypes.c_int, P, ctypes.POINTER(sz)]
+    lib.gca_retrieve.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.gca_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gca_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward",
+              "gca_profile_enable", "gca_profile_collect"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.gca_status_string.argtypes = [ctypes.c_int]
+    lib.gca_status_string.restype = ctypes.c_char_p
+    lib.gca_last_hip_error.argtypes = []
+    lib.gca_last_hip_error.restype = ctypes.c_int
+    lib.gca_profile_enable.argtypes = [ctypes.c_int]
+    lib.gca_profile_collect.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int)]
+    _lib = lib
+    return lib
+
+
+@dataclass
+class Config:
+    """Problem options of one GCA layer call (see gca_problem in include/gca.h)."""
+
+    B: int
+    G: int
+    H: int
+    n_q: int
+    n_kv: int
+    topk: int = 8
+    dtype: str = "bf16"
+    q_chunk_base: int = 0
+    shift: int = 1
+    use_gumbel: bool = False
+    seed: int = 0
+    tau: float = 1.0
+    attn_scale: float = 1.0 / math.sqrt(64)
+    score_scale: float = 1.0 / math.sqrt(64)
+
+    def problem(self) -> Problem:
+        return Problem(B=self.B, G=self.G, H=self.H, S=64, n_q_chunks=self.n_q,
+                       q_chunk_base=self.q_chunk_base, n_kv_chunks=self.n_kv, d_head=64,
+                       d_lmk=64, topk=self.topk, dtype=DTYPES[self.dtype],
+                       attn_scale=self.attn_scale, score_scale=self.score_scale,
+                       use_gumbel=int(self.use_gumbel), shift=self.shift,
+                       seed=self.seed & ((1 << 64) - 1), gumbel_tau=self.tau, reserved=0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(call: str, status: int):
+    if status != GCA_OK:
+        raise GcaError(call, status)
+
+
+def workspace_size(op: int, cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    prob = cfg.problem()
+    _check("gca_workspace_size", load().gca_workspace_size(op, ctypes.byref(prob), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(op: int, cfg: Config, device):
+    import torch
+
+    n = workspace_size(op, cfg)
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def _torch_dtype(cfg: Config):
+    import torch
+
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def retrieve(cfg: Config, lq, lk, idx=None, score=None, ws=None):
+    """gca_retrieve: returns (idx int32 [G,B,n_q,K], score fp32 [G,B,n_q,K])."""
+    import torch
+
+    dev = lq.device
+    shp = (cfg.G, cfg.B, cfg.n_q, cfg.topk)
+    idx = torch.empty(shp, dtype=torch.int32, device=dev) if idx is None else idx
+    score = torch.empty(shp, dtype=torch.float32, device=dev) if score is None else score
+    if ws is None:
+        ws, n = _workspace(OP_RETRIEVE, cfg, dev)
+    else:
+        n = ws.numel()
+    prob = cfg.problem()
+    _check("gca_retrieve", load().gca_retrieve(ctypes.byref(prob), _ptr(lq), _ptr(lk), _ptr(idx),
+                                               _ptr(score), _ptr(ws), n, _stream()))
+    return idx, score
+
+
+def forward(cfg: Config, q, k, v, idx, score, need_lse: bool = True, o=None, lse=None):
+    """gca_forward: returns (o [G,B,H,n_q*64,64], lse fp32 [G,B,H,n_q*64,K] or None)."""
+    import torch
+
+    dev = q.device
+    o = torch.empty_like(q) if o is None else o
+    if need_lse and lse is None:
+        lse = torch.empty((cfg.G, cfg.B, cfg.H, cfg.n_q * 64, cfg.topk), dtype=torch.float32, device=dev)
+    prob = cfg.problem()
+    _check("gca_forward", load().gca_forward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                             _ptr(score), _ptr(o), _ptr(lse) if need_lse else None,
+                                             None, 0, _stream()))
+    return o, (lse if need_lse else None)
+
+
+def backward(cfg: Config, q, k, v, idx, score, lse, dout, ws=None, out=None):
+    """gca_backward: returns (dq, dk, dv, dscore)."""
+    import torch
+
+    dev = q.device
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dscore = torch.empty(idx.shape, dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv, dscore = out
+    if ws is None:
+        ws, n = _workspace(OP_BACKWARD, cfg, dev)
+    else:
+        n = ws.numel()
+    prob = cfg.problem()
+    _check("gca_backward", load().gca_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                               _ptr(score), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                               _ptr(dv), _ptr(dscore), _ptr(ws), n, _stream()))
+    return dq, dk, dv, dscore
+
+
+def profile_enable(on: bool = True):
+    _check("gca_profile_enable", load().gca_profile_enable(1 if on else 0))
+
+
+def profile_collect() -> dict:
+    """{kernel name: (total ms, launches)} for launches since the last collect."""
+    lib = load()
+    cap = 16
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int64 * cap)()
+    n = ctypes.c_int(0)
+    _check("gca_profile_collect", lib.gca_profile_collect(cap, names, ms, cnt, ctypes.byref(n)))
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(n.value, cap))}

@@ -1,0 +1,56 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path, compare."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from long_context_lm_amd import gca
+from long_context_lm_amd import inputs as I
+
+
+def say(*args):
+    print("[gpu-test]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def config_for(shape: I.Shape, dtype: str, **kw) -> gca.Config:
+    return gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                      dtype=dtype, q_chunk_base=shape.q_chunk_base, shift=shape.shift, **kw)
+
+
+def upload(tensors: dict, device="cuda") -> dict:
+    return {k: v.to(device) for k, v in tensors.items()}
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((got - ref).ravel())
+    return float(num / den) if den > 0 else float(num)
+
+
+def assert_close(name: str, got, ref, dtype: str):
+    """fp32: max-abs <= 1e-4; bf16: relative L2 <= 1e-2 (the stated parity bars)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if dtype == "f32":
+        err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+        assert err <= 1e-4, f"{name}: max-abs {err:.3e} > 1e-4"
+    else:
+        err = rel_l2(got, ref)
+        assert err <= 1e-2, f"{name}: rel-L2 {err:.3e} > 1e-2"
+    return err
+
+
+def lse_compare(name: str, got, ref, dtype: str):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    inf_g, inf_r = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(inf_g, inf_r), f"{name}: -inf pattern differs"
+    return assert_close(name, got[~inf_r], ref[~inf_r], dtype)

@@ -1,0 +1,154 @@
+"""The C ABI on the host: the library loads, exports what include/gca.h declares, and rejects
+invalid arguments with the documented status codes before touching the GPU."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from long_context_lm_amd import gca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gca.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, MISALIGNED, HIP = range(6)
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gca_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gca.load()
+    names = declared_functions()
+    assert set(gca.EXPORTS) <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libgca.so does not export {n}"
+
+
+def test_problem_struct_layout_matches_c():
+    fields = [f for f, _ in gca.Problem._fields_]
+    prog = "#include <stdio.h>\n#include <stddef.h>\n#include \"gca.h\"\nint main(void){\n"
+    prog += 'printf("%zu\\n", sizeof(gca_problem));\n'
+    for f in fields:
+        prog += f'printf("%zu\\n", offsetof(gca_problem, {f}));\n'
+    prog += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(gca.Problem)
+    assert out[1:] == [getattr(gca.Problem, f).offset for f in fields]
+
+
+def good(**kw):
+    c = gca.Config(B=2, G=2, H=3, n_q=8, n_kv=8, topk=4, dtype="bf16")
+    p = c.problem()
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def ws_size(p, op):
+    n = ctypes.c_size_t(0)
+    st = gca.load().gca_workspace_size(op, ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, INVALID), ("G", -1, INVALID), ("H", 0, INVALID), ("n_q_chunks", -1, INVALID),
+    ("q_chunk_base", -3, INVALID), ("n_kv_chunks", -1, INVALID), ("topk", 0, INVALID),
+    ("topk", 17, UNSUPPORTED), ("S", 32, UNSUPPORTED), ("d_head", 128, UNSUPPORTED),
+    ("d_lmk", 32, UNSUPPORTED), ("dtype", 7, INVALID), ("use_gumbel", 2, INVALID),
+    ("shift", 2, INVALID), ("reserved", 1, INVALID), ("attn_scale", float("inf"), INVALID),
+    ("score_scale", float("nan"), INVALID), ("gumbel_tau", -1.0, INVALID),
+    ("n_kv_chunks", 1 << 31, UNSUPPORTED), ("n_q_chunks", 1 << 40, UNSUPPORTED),
+])
+def test_problem_validation(field, value, status):
+    p = good(**{field: value})
+    lib = gca.load()
+    for op in (0, 1, 2):
+        assert ws_size(p, op)[0] == status
+    z = ctypes.c_void_p(FAKE)
+    assert lib.gca_retrieve(ctypes.byref(p), z, z, z, z, None, 0, None) == status
+    assert lib.gca_forward(ctypes.byref(p), z, z, z, z, z, z, z, None, 0, None) == status
+    assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, None, 0, None) == status
+
+
+def test_null_problem_and_bad_op():
+    lib = gca.load()
+    n = ctypes.c_size_t(0)
+    assert lib.gca_workspace_size(0, None, ctypes.byref(n)) == INVALID
+    p = good()
+    assert lib.gca_workspace_size(3, ctypes.byref(p), ctypes.byref(n)) == INVALID
+    assert lib.gca_workspace_size(0, ctypes.byref(p), None) == INVALID
+    assert lib.gca_retrieve(None, None, None, None, None, None, 0, None) == INVALID
+
+
+def test_workspace_sizes():
+    # 16K training shape: retrieval fits one block per row; backward needs its index buffers
+    c = gca.Config(B=8, G=2, H=12, n_q=256, n_kv=256, topk=8)
+    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 0
+    assert gca.workspace_size(gca.OP_FORWARD, c) == 0
+    bw = gca.workspace_size(gca.OP_BACKWARD, c)
+    assert bw >= 2 * 8 * 12 * 256 * 64 * 8 * 4  # per-(token, slot) e values
+    # 16M-token history: 256 partial lists of 8 keys per row and group
+    c = gca.Config(B=1, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
+    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 2 * 256 * 8 * 8 + 2 * 256 * 8 * 4
+    # too many retrievals per batch row for the inverse index
+    c = gca.Config(B=1, G=2, H=1, n_q=1024, n_kv=1024, topk=8)
+    with pytest.raises(gca.GcaError):
+        gca.workspace_size(gca.OP_BACKWARD, c)
+
+
+def test_pointer_checks():
+    lib = gca.load()
+    p = good()
+    z = ctypes.c_void_p(FAKE)
+    mis = ctypes.c_void_p(FAKE + 8)
+    # retrieval: null and misaligned inputs/outputs
+    assert lib.gca_retrieve(ctypes.byref(p), None, z, z, z, None, 0, None) == INVALID
+    assert lib.gca_retrieve(ctypes.byref(p), z, z, None, z, None, 0, None) == INVALID
+    assert lib.gca_retrieve(ctypes.byref(p), mis, z, z, z, None, 0, None) == MISALIGNED
+    assert lib.gca_retrieve(ctypes.byref(p), z, z, ctypes.c_void_p(FAKE + 2), z, None, 0, None) == MISALIGNED
+    # forward
+    assert lib.gca_forward(ctypes.byref(p), z, z, z, z, z, None, None, None, 0, None) == INVALID
+    assert lib.gca_forward(ctypes.byref(p), z, mis, z, z, z, z, z, None, 0, None) == MISALIGNED
+    # backward: workspace checks come after the tensors
+    st, need = ws_size(p, 2)
+    assert st == OK and need > 0
+    assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, z, need - 1, None) == WS_SMALL
+    assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, None, need, None) == INVALID
+    assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z,
+                            ctypes.c_void_p(FAKE + 16), need, None) == MISALIGNED
+    assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, mis, z, z, z, need, None) == MISALIGNED
+    # backward beyond the inverse-index capacity
+    big = good(n_q_chunks=1025, n_kv_chunks=1025)  # G * n_q * K = 8200 > 8192
+    assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED
+
+
+def test_empty_problem_is_a_noop_without_gpu():
+    lib = gca.load()
+    p = good(n_q_chunks=0)
+    assert lib.gca_retrieve(ctypes.byref(p), None, None, None, None, None, 0, None) == OK
+    assert lib.gca_forward(ctypes.byref(p), None, None, None, None, None, None, None, None, 0, None) == OK
+    p = good(n_q_chunks=0, n_kv_chunks=0)
+    assert lib.gca_backward(ctypes.byref(p), *([None] * 11), None, 0, None) == OK
+
+
+def test_status_strings_and_error_state():
+    lib = gca.load()
+    texts = [lib.gca_status_string(s).decode() for s in range(6)]
+    assert len(set(texts)) == 6
+    assert lib.gca_status_string(99).decode() == "unknown status"
+    assert lib.gca_last_hip_error() == 0
+    gca.profile_enable(False)
+    assert gca.profile_collect() == {}

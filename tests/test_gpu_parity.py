@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: retrieved idx and score bit-exact; fp32 outputs and gradients within max-abs 1e-4; bf16
+within relative L2 1e-2.  Shapes follow the pages' workloads (S = 64, K = 8, 16K contexts,
+histories up to 16M tokens) plus small cases that span many chunk tiles, short rows (fewer
+candidates than K), offsets and degenerate sizes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_lm_amd import gca
+from long_context_lm_amd import inputs as I
+from oracle import gca_oracle as O
+from tests.gpu_util import assert_close, config_for, lse_compare, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gca.load()  # fails loudly if the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def _oracle_all(shape, x, cfg, need_bwd):
+    idx, sc = O.retrieve(x["lq"], x["lk"], shape.topk, score_scale=cfg.score_scale,
+                         use_gumbel=cfg.use_gumbel, seed=cfg.seed, tau=cfg.tau,
+                         q_chunk_base=shape.q_chunk_base, n_kv=shape.n_kv)
+    o, lse = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=shape.shift, attn_scale=cfg.attn_scale)
+    grads = None
+    if need_bwd:
+        grads = O.backward(x["q"], x["k"], x["v"], idx, sc, x["dout"], shift=shape.shift,
+                           attn_scale=cfg.attn_scale)
+    return idx, sc, o, lse, grads
+
+
+def _run_case(shape, dtype, scale=1.0, seed=0, need_bwd=True, **cfgkw):
+    say("case", shape, dtype, cfgkw)
+    cfg = config_for(shape, dtype, **cfgkw)
+    host = I.make_inputs(shape, dtype, seed=seed, scale=scale)
+    x = {k: I.as_f64(v) for k, v in host.items()}
+    dev = upload(host)
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    grads = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"]) if need_bwd else None
+    torch.cuda.synchronize()
+    say("  gpu done; running oracle")
+    r_idx, r_sc, r_o, r_lse, r_grads = _oracle_all(shape, x, cfg, need_bwd)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    errs = {"o": assert_close("o", I.as_f64(o), r_o, dtype),
+            "lse": lse_compare("lse", lse.cpu().numpy(), r_lse, dtype)}
+    if need_bwd:
+        for name, got, ref in zip(("dq", "dk", "dv", "dscore"), grads, r_grads):
+            errs[name] = assert_close(name, I.as_f64(got), ref, dtype)
+    say("  errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    return cfg, dev, (idx, sc, o, lse, grads)
+
+
+# ------------------------------------------------------------------ small shapes, full check
+def test_tiny_fp32_forward_backward():
+    """B=1, L=1024 (16 chunks), H=2, K=4, fp32, N(0,1) inputs, no Gumbel."""
+    _run_case(I.TINY_FP32, "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_gumbel_two_groups(dtype):
+    shape = I.Shape(B=2, G=2, H=3, n_q=21, n_kv=21, topk=8)
+    _run_case(shape, dtype, scale=0.125, use_gumbel=True, seed=5, tau=1.0)
+
+
+@pytest.mark.parametrize("topk", [1, 3, 16])
+def test_small_topk_variants_bf16(topk):
+    shape = I.Shape(B=1, G=1, H=2, n_q=24, n_kv=24, topk=topk)
+    _run_case(shape, "bf16", scale=0.125, seed=topk)
+
+
+def test_history_shorter_than_queries_and_offset_rows():
+    # rows are global chunks 5..16; only 9 history chunks exist
+    shape = I.Shape(B=2, G=1, H=2, n_q=12, n_kv=9, topk=4, q_chunk_base=5, shift=0)
+    _run_case(shape, "f32", seed=2)
+
+
+def test_inference_shape_shift0_fp32():
+    shape = I.Shape(B=1, G=2, H=2, n_q=1, n_kv=40, topk=8, q_chunk_base=40, shift=0)
+    _run_case(shape, "f32", seed=3, use_gumbel=False)
+
+
+# ------------------------------------------------------------------ degenerate sizes
+def test_no_query_chunks_is_noop_and_zeroes_kv_grads():
+    shape = I.Shape(B=1, G=1, H=2, n_q=0, n_kv=4, topk=4)
+    cfg = config_for(shape, "bf16")
+    dev = upload(I.make_inputs(shape, "bf16"))
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    dk0 = torch.full_like(dev["k"], 7.0)
+    dv0 = torch.full_like(dev["v"], 7.0)
+    dq, dk, dv, ds = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"],
+                                  out=(torch.empty_like(dev["q"]), dk0, dv0,
+                                       torch.empty(idx.shape, dtype=torch.float32, device="cuda")))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_no_history():
+    shape = I.Shape(B=1, G=1, H=2, n_q=3, n_kv=0, topk=4)
+    cfg = config_for(shape, "f32")
+    dev = upload(I.make_inputs(shape, "f32"))
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    dq, dk, dv, ds = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
+    torch.cuda.synchronize()
+    assert torch.all(idx == -1) and torch.all(torch.isneginf(sc))
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(dq == 0) and torch.all(ds == 0)
+
+
+# ------------------------------------------------------------------ retrieval stress
+def test_ties_hub_and_passkey_retrieval():
+    """Duplicate landmarks (ties toward lower j), a hub chunk every row prefers, a planted key."""
+    n = 48
+    shape = I.Shape(B=2, G=2, H=1, n_q=n, n_kv=n, topk=8)
+    rng = np.random.default_rng(0)
+    lq = (rng.standard_normal((2, 2, n, 64)) / 8).astype(np.float32)
+    lk = (rng.standard_normal((2, 2, n, 64)) / 8).astype(np.float32)
+    lk[0, 0, 1::2] = lk[0, 0, 0::2]             # pairs of identical key landmarks
+    lk[0, 1, :] = lk[0, 1, 0]                   # every key landmark equal: all ties
+    lk[1, 0, 3] = 4 * lq[1, 0].mean(axis=0)     # hub chunk 3
+    lk[1, 1, 17] = 10 * lq[1, 1, 40]            # passkey for row 40
+    lq_t = torch.from_numpy(lq).to(torch.bfloat16)
+    lk_t = torch.from_numpy(lk).to(torch.bfloat16)
+    cfg = config_for(shape, "bf16")
+    idx, sc = gca.retrieve(cfg, lq_t.cuda(), lk_t.cuda())
+    torch.cuda.synchronize()
+    r_idx, r_sc = O.retrieve(I.as_f64(lq_t), I.as_f64(lk_t), 8)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    assert list(r_idx[0, 1, 20]) == list(range(8))
+    assert r_idx[1, 1, 40, 0] == 17
+
+
+def test_retrieval_gumbel_long_rows_two_stage():
+    """Rows with more candidates than one block (forces the split + merge kernels)."""
+    n_kv = 5000
+    shape = I.Shape(B=1, G=2, H=1, n_q=3, n_kv=n_kv, topk=8, q_chunk_base=n_kv - 1, shift=0)
+    host = I.make_inputs(shape, "bf16", seed=9, scale=0.125, names=("lq", "lk"))
+    for gumbel in (False, True):
+        cfg = config_for(shape, "bf16", use_gumbel=gumbel, seed=77)
+        idx, sc = gca.retrieve(cfg, host["lq"].cuda(), host["lk"].cuda())
+        torch.cuda.synchronize()
+        r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8, use_gumbel=gumbel,
+                                 seed=77, q_chunk_base=n_kv - 1, n_kv=n_kv)
+        np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+        np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+
+
+# ------------------------------------------------------------------ invariants on device
+def test_determinism_and_causality_on_device():
+    shape = I.Shape(B=2, G=2, H=2, n_q=12, n_kv=12, topk=4)
+    cfg = config_for(shape, "bf16", use_gumbel=True, seed=3)
+    host = I.make_inputs(shape, "bf16", seed=1, scale=0.125)
+    dev = upload(host)
+
+    def run(d):
+        idx, sc = gca.retrieve(cfg, d["lq"], d["lk"])
+        o, lse = gca.forward(cfg, d["q"], d["k"], d["v"], idx, sc)
+        g = gca.backward(cfg, d["q"], d["k"], d["v"], idx, sc, lse, d["dout"])
+        torch.cuda.synchronize()
+        return [t.cpu() for t in (idx, sc, o, lse, *g)]
+
+    a = run(dev)
+    b = run(dev)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), "run-to-run outputs differ"
+    # perturb everything at or after chunk c (and K/V, lk of chunk c-1): chunk c's outputs hold
+    c = 7
+    d2 = {k: v.clone() for k, v in dev.items()}
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    d2["q"][:, :, :, 64 * (c + 1):] += torch.randn(d2["q"][:, :, :, 64 * (c + 1):].shape, generator=gen,
+                                                  device="cuda").to(d2["q"].dtype)
+    d2["k"][:, :, 64 * (c - 1):] += 1
+    d2["v"][:, :, 64 * (c - 1):] += 1
+    d2["lq"][:, :, c:] += 1
+    d2["lk"][:, :, c - 1:] -= 1
+    e = run(d2)
+    assert torch.equal(e[0][:, :, :c], a[0][:, :, :c])
+    assert torch.equal(e[1][:, :, :c], a[1][:, :, :c])
+    assert torch.equal(e[2][:, :, :, : 64 * (c + 1)], a[2][:, :, :, : 64 * (c + 1)])
+    assert torch.equal(e[3][:, :, :, : 64 * (c + 1)], a[3][:, :, :, : 64 * (c + 1)])
+
+
+# ------------------------------------------------------------------ full training shape
+@pytest.mark.timeout(900)
+def test_full_16k_training_step_sampled():
+    """B=8, L=16384, H=12, K=8, G=2, Gumbel, bf16 inputs N(0,1)/8: the benchmark's step.
+
+    idx/score are compared in full; o, dq for every head of batch rows 0 and 5; dk, dv for
+    heads 0 and 11 of those rows (every retrieval that selected their chunks is included);
+    dscore for those rows (sums over all heads).
+    """
+    shape = I.TRAIN_16K_G2
+    cfg = config_for(shape, "bf16", use_gumbel=True, seed=1)
+    say("generating full-size inputs")
+    host = I.make_inputs(shape, "bf16", seed=0, scale=0.125)
+    dev = upload(host)
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    dq, dk, dv, ds = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
+    torch.cuda.synchronize()
+    say("gpu step done")
+    lq, lk = I.as_f64(host["lq"]), I.as_f64(host["lk"])
+    r_idx, r_sc = O.retrieve(lq, lk, 8, use_gumbel=True, seed=1)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    say("retrieval bit-exact")
+    for b in (0, 5):
+        x = {n: I.as_f64(host[n][:, b:b + 1]) if n in ("q", "dout") else None for n in ("q", "dout")}
+        kb = I.as_f64(host["k"][b:b + 1])
+        vb = I.as_f64(host["v"][b:b + 1])
+        ib, sb = r_idx[:, b:b + 1], r_sc[:, b:b + 1]
+        r_o, r_lse = O.forward(x["q"], kb, vb, ib, sb, shift=1)
+        assert_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o, "bf16")
+        lse_compare(f"lse[b={b}]", lse[:, b:b + 1].cpu().numpy(), r_lse, "bf16")
+        r_dq, r_dk, r_dv, r_ds = O.backward(x["q"], kb, vb, ib, sb, x["dout"], shift=1)
+        assert_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq, "bf16")
+        for h in (0, 11):
+            assert_close(f"dk[b={b},h={h}]", I.as_f64(dk[b:b + 1, h]), r_dk[:, h], "bf16")
+            assert_close(f"dv[b={b},h={h}]", I.as_f64(dv[b:b + 1, h]), r_dv[:, h], "bf16")
+        assert_close(f"dscore[b={b}]", ds[:, b:b + 1].cpu().numpy(), r_ds, "bf16")
+        say(f"batch row {b} matches")
+
+
+# ------------------------------------------------------------------ long-history inference
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("shape", [I.INFER_1M, I.INFER_16M], ids=["1M", "16M"])
+def test_long_history_inference_step(shape):
+    """One new chunk retrieves over a 1M / 16M-token history resident in HBM (bf16)."""
+    cfg = config_for(shape, "bf16")
+    say("allocating history", shape.n_kv, "chunks")
+    host = I.make_inputs(shape, "bf16", seed=0, names=("lq", "lk", "q"))
+    lq, lk, q = host["lq"].cuda(), host["lk"].cuda(), host["q"].cuda()
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    kv_shape = shape.tensor_shape("k")
+    k = torch.randn(kv_shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(kv_shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    idx, sc = gca.retrieve(cfg, lq, lk)
+    o, _ = gca.forward(cfg, q, k, v, idx, sc, need_lse=False)
+    torch.cuda.synchronize()
+    r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), shape.topk,
+                             q_chunk_base=shape.q_chunk_base, n_kv=shape.n_kv)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    # oracle forward on the retrieved tiles only: gather them (copies of torch's data) and remap
+    used = sorted(set(int(j) for j in r_idx.ravel() if j >= 0))
+    remap = {j: n for n, j in enumerate(used)}
+    kk = torch.cat([k[:, :, 64 * j:64 * j + 64] for j in used], dim=2)
+    vv = torch.cat([v[:, :, 64 * j:64 * j + 64] for j in used], dim=2)
+    idx2 = np.vectorize(lambda j: remap.get(int(j), -1))(r_idx).astype(np.int32)
+    r_o, _ = O.forward(I.as_f64(host["q"]), I.as_f64(kk), I.as_f64(vv), idx2, r_sc, shift=0)
+    assert_close("o", I.as_f64(o), r_o, "bf16")
+    del k, v
+    torch.cuda.empty_cache()
