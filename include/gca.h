@@ -25,14 +25,14 @@
  *       q, o, dout, dq  [G, B, H, n_q*S, d]
  *       k, v, dk, dv    [B, H, n_kv*S, d]      shared by all G groups
  *       idx, score, dscore [G, B, n_q, topk]
- *       lse    [G, B, H, n_q*S, topk]
+ *       lse    [G, B, H, n_q, topk, S]   (per query chunk and slot, the chunk's S tokens)
  *   - Row r of a retrieval is global chunk i = q_chunk_base + r; its candidates are the
  *     chunks j < min(i, n_kv).  Query chunk t uses row t - shift (shift = 1 in training, where
  *     the landmark of chunk t-1 retrieves for chunk t; shift = 0 when the caller passes the
  *     landmark of the chunk being generated).  Query chunks whose row is missing or has no
  *     valid slot get o = 0, lse = -inf, dq = 0.
- *   - Pointers to the floating tensors and to lq, lk must be 16-byte aligned; idx, score,
- *     lse, dscore 4-byte aligned.  Otherwise GCA_ERR_MISALIGNED.
+ *   - Pointers to the floating tensors, lq, lk and lse must be 16-byte aligned; idx, score,
+ *     dscore 4-byte aligned.  Otherwise GCA_ERR_MISALIGNED.
  *   - Every call validates all arguments on the host before touching the GPU and enqueues
  *     nothing when it returns an error.  A launch failure returns GCA_ERR_HIP; the HIP code
  *     is then available from gca_last_hip_error() (per calling thread).  Faults inside
@@ -138,8 +138,8 @@ gca_status gca_forward(const gca_problem* problem, const void* q, const void* k,
  *              groups and every (token, slot) that retrieved the chunk of u (zero if none).
  * q, k, v, idx, score, lse (from gca_forward), dout: inputs; dq, dk, dv, dscore: outputs.
  * dk and dv are accumulated in fp32 in a fixed order and rounded once to dtype.
- * ws: >= gca_workspace_size(BACKWARD).  GCA_ERR_UNSUPPORTED if one batch row holds more than
- * 8192 (group, row, slot) retrievals (G * n_q * topk > 8192).
+ * ws: >= gca_workspace_size(BACKWARD); it holds, among others, an inverse retrieval index of
+ * B * n_kv * G * n_q int32 entries.
  */
 gca_status gca_backward(const gca_problem* problem, const void* q, const void* k, const void* v,
                         const int32_t* idx, const float* score, const float* lse,

@@ -6,23 +6,29 @@
 // [Notes, Background: entry point].  K/V are shared by all retrieval groups [Notes, Key
 // designs: GCA].
 //
-// Tiles.  A chunk is 64 tokens, the head dim is 64, so one retrieved chunk of one head is a
+// Tiles.  A chunk is 64 tokens and the head dim is 64, so one retrieved chunk of one head is a
 // 64x64 K tile and a 64x64 V tile, and one (query chunk, head) is a 64x64 Q tile.  A workgroup
 // of two waves owns one 64-query tile (forward and query-major backward) or one 64-key tile
 // (key-major backward); each wave owns 32 rows and all 64 columns.  Each per-chunk softmax
-// covers exactly one 64-key tile, so it is computed whole, without an online rescaling.
+// covers exactly one 64-key tile, so it is computed whole, without online rescaling.
 //
-// Layout trick (see gca_device.hpp): S^T = K Q^T is computed with the K rows loaded through
-// the permutation pi, which leaves each lane holding 16 consecutive keys of one query per
-// 32-key tile; that register block is directly the B operand (P^T) of O^T = V^T P^T, so the
-// probabilities never leave registers.  Operands that must be read down a column of a row-major
-// tile (V in the forward, K in dQ, Q and dO in dK/dV) are staged transposed in LDS.
+// Data movement.  The tiles a workgroup walks through (K/V of each retrieved chunk, or Q/dO of
+// each retrieving chunk) are copied global -> LDS with direct 16-byte-per-lane copies into a
+// row-major, XOR-swizzled layout, double-buffered: the copy of item n+1 is in flight while item
+// n is computed, and one barrier per item both publishes the new buffer and retires the old.
+// Operands read along a tile row come from ds_read_b128; operands read down a tile column (V in
+// the forward, K in dQ, Q and dO in dK/dV) come from transposing LDS reads, so no tile is ever
+// stored transposed.
+//
+// Layout trick (see gca_device.hpp): S^T = K Q^T is computed with the K rows loaded through the
+// permutation pi, which leaves each lane holding 16 consecutive keys of one query per 32-key
+// tile; that register block is directly the B operand (P^T) of O^T = V^T P^T.
 //
 // Backward without floating-point atomics.  dQ and the per-slot sums of e = <dO, O_k> are
 // produced query-major (one workgroup per query tile).  dK and dV are produced key-major: an
 // inverse index lists, per (batch row, key chunk), the (group, row, slot) retrievals that
-// selected it, in a fixed order, and one workgroup per (batch row, head, key chunk) walks that
-// list and accumulates in registers.  d(score) sums the per-head partials in head order.
+// selected it in a fixed order; one workgroup per (batch row, head, key chunk) walks that list
+// and accumulates in registers.  d(score) sums the per-head partials in a fixed order.
 #include "gca_device.hpp"
 #include "gca_internal.hpp"
 
@@ -30,52 +36,10 @@ namespace gca {
 namespace {
 
 constexpr int kThreads = 128;  // two waves
+constexpr int kWaves = 2;
+constexpr int kEntRound = 512;  // inverse-index entries staged in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2f = 0.6931471805599453f;
-
-template <typename T>
-struct TileCfg {
-  static constexpr int kVec = 16 / static_cast<int>(sizeof(T));      // elements per 16 bytes
-  static constexpr int kLd = kDim + kVec;                             // LDS row stride
-  static constexpr int kChunksPerRow = kDim / kVec;
-  static constexpr int kChunks = kChunk * kChunksPerRow;              // 16-byte pieces per tile
-  static constexpr int kPerThread = kChunks / kThreads;
-};
-
-__device__ __forceinline__ uint16_t elem16(const u32x4_t& x, int e) {
-  return static_cast<uint16_t>(x[e >> 1] >> ((e & 1) * 16));
-}
-
-// Copy a 64x64 tile (row stride 64 in global memory) to LDS, row-major and/or transposed.
-template <typename T, bool kRow, bool kTrans>
-__device__ __forceinline__ void stage_tile(const T* __restrict__ src, T* rowm, T* trans) {
-  using C = TileCfg<T>;
-  const int tid = threadIdx.x;
-  u32x4_t x[C::kPerThread];
-#pragma unroll
-  for (int n = 0; n < C::kPerThread; ++n) {
-    const int c = tid + n * kThreads;
-    const int u = c / C::kChunksPerRow, col = (c % C::kChunksPerRow) * C::kVec;
-    x[n] = *reinterpret_cast<const u32x4_t*>(src + u * kDim + col);
-  }
-#pragma unroll
-  for (int n = 0; n < C::kPerThread; ++n) {
-    const int c = tid + n * kThreads;
-    const int u = c / C::kChunksPerRow, col = (c % C::kChunksPerRow) * C::kVec;
-    if (kRow) *reinterpret_cast<u32x4_t*>(rowm + u * C::kLd + col) = x[n];
-    if (kTrans) {
-      if constexpr (sizeof(T) == 2) {
-        uint16_t* t16 = reinterpret_cast<uint16_t*>(trans);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t16[(col + e) * C::kLd + u] = elem16(x[n], e);
-      } else {
-        float* t32 = reinterpret_cast<float*>(trans);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t32[(col + e) * C::kLd + u] = __uint_as_float(x[n][e]);
-      }
-    }
-  }
-}
 
 // Slot table of one retrieval row: valid slots (0 <= j < n_kv) in slot order, with the fusion
 // weights w = softmax over the valid slots of the clean scores.
@@ -83,39 +47,40 @@ struct SlotTable {
   int32_t j[kMaxTopk];
   int32_t slot[kMaxTopk];
   float w[kMaxTopk];
+  float w_all[kMaxTopk];  // by slot, 0 on invalid slots
+  uint32_t valid_mask;
   int n;
 };
 
-__device__ void fusion_weights(const int32_t* idx_row, const float* score_row, int K, int64_t n_kv,
-                               float* w_out, bool* valid_out) {
-  float mx = -__builtin_inff();
-  for (int k = 0; k < K; ++k) {
-    const int32_t j = idx_row[k];
-    const bool ok = j >= 0 && j < n_kv;
-    valid_out[k] = ok;
-    if (ok) mx = fmaxf(mx, score_row[k]);
-  }
-  float sum = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const float e = valid_out[k] ? expf(score_row[k] - mx) : 0.f;
-    w_out[k] = e;
-    sum += e;
-  }
-  for (int k = 0; k < K; ++k) w_out[k] = valid_out[k] ? w_out[k] / sum : 0.f;
-}
-
 __device__ void build_slot_table(SlotTable& st, const AttendParams& p, int g, int b, int64_t row) {
   st.n = 0;
+  st.valid_mask = 0;
+  for (int k = 0; k < kMaxTopk; ++k) st.w_all[k] = 0.f;
   if (row < 0) return;
   const int64_t base = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K;
-  float w[kMaxTopk];
-  bool valid[kMaxTopk];
-  fusion_weights(p.idx + base, p.score + base, p.K, p.n_kv, w, valid);
+  const int32_t* ir = p.idx + base;
+  const float* sr = p.score + base;
+  float mx = -__builtin_inff();
   for (int k = 0; k < p.K; ++k) {
-    if (!valid[k]) continue;
-    st.j[st.n] = p.idx[base + k];
+    const int32_t j = ir[k];
+    if (j >= 0 && j < p.n_kv) {
+      st.valid_mask |= 1u << k;
+      mx = fmaxf(mx, sr[k]);
+    }
+  }
+  float sum = 0.f;
+  for (int k = 0; k < p.K; ++k) {
+    if (!((st.valid_mask >> k) & 1u)) continue;
+    const float e = expf(sr[k] - mx);
+    st.w_all[k] = e;
+    sum += e;
+  }
+  for (int k = 0; k < p.K; ++k) {
+    if (!((st.valid_mask >> k) & 1u)) continue;
+    st.w_all[k] = st.w_all[k] / sum;
+    st.j[st.n] = ir[k];
     st.slot[st.n] = k;
-    st.w[st.n] = w[k];
+    st.w[st.n] = st.w_all[k];
     ++st.n;
   }
 }
@@ -123,6 +88,7 @@ __device__ void build_slot_table(SlotTable& st, const AttendParams& p, int g, in
 struct QTileCoord {
   int b, h, g;
   int64_t t;
+  int64_t gbh;  // (g * B + b) * H + h
 };
 
 __device__ __forceinline__ QTileCoord query_tile_coord(const AttendParams& p) {
@@ -134,61 +100,83 @@ __device__ __forceinline__ QTileCoord query_tile_coord(const AttendParams& p) {
   rest /= p.G;
   c.h = static_cast<int>(rest % p.H);
   c.b = static_cast<int>(rest / p.H);
+  c.gbh = (static_cast<int64_t>(c.g) * p.B + c.b) * p.H + c.h;
   return c;
+}
+
+// Per-(chunk, slot) vectors of 64 floats (lse, e) live at [gbh][t][slot][64].
+__device__ __forceinline__ int64_t slot_vec_offset(const AttendParams& p, int64_t gbh, int64_t t, int slot) {
+  return ((gbh * p.n_q + t) * p.K + slot) * kChunk;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* kv_tile(const void* base, const AttendParams& p, int b, int h, int64_t j) {
+  return static_cast<const T*>(base) + ((static_cast<int64_t>(b) * p.H + h) * p.n_kv + j) * kChunk * kDim;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> row_frag(const char* tile, int row, int col0) {
+  return frag_row(tile, row, col0, static_cast<T*>(nullptr));
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> col_frag(const char* tile, int r0, int c_base) {
+  return frag_col(tile, r0, c_base, static_cast<T*>(nullptr));
 }
 
 // ------------------------------------------------------------------------------ forward
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
-  using C = TileCfg<T>;
-  __shared__ __align__(16) T Ks[kChunk * C::kLd];
-  __shared__ __align__(16) T Vt[kDim * C::kLd];
-  __shared__ float lse_s[kChunk * kMaxTopk];
+  using TL = Tile<T>;
+  // Two buffers, each [K tile, V tile], as separate objects so that the compiler can tell the
+  // buffer being read from the one being filled and does not wait for the fill.
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes];
+  __shared__ __align__(1024) char buf1[2 * TL::kBytes];
   __shared__ SlotTable st;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hl = lane >> 5;
   const QTileCoord c = query_tile_coord(p);
   const int64_t Lq = p.n_q * kChunk;
-  const int64_t qrow0 = ((static_cast<int64_t>(c.g) * p.B + c.b) * p.H + c.h) * Lq + c.t * kChunk;
+  const int64_t qrow0 = c.gbh * Lq + c.t * kChunk;
   const int my_q = 32 * wave + li;
 
   if (tid == 0) build_slot_table(st, p, c.g, c.b, c.t - p.shift);
-  for (int e = tid; e < kChunk * kMaxTopk; e += kThreads) lse_s[e] = -__builtin_inff();
-
   Frag<T> qf[4];
   const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s].load(q + 16 * s + 8 * hl);
+  __syncthreads();
+
+  const int nslots = st.n;
+  auto fill = [&](int n, char* buf) {
+    tile_load_async<T, kWaves>(kv_tile<T>(p.k, p, c.b, c.h, st.j[n]), buf);
+    tile_load_async<T, kWaves>(kv_tile<T>(p.v, p, c.b, c.h, st.j[n]), buf + TL::kBytes);
+  };
+  if (nslots > 0) fill(0, buf0);
+  if (p.lse) {  // invalid slots: -inf
+    for (int e = tid; e < p.K * kChunk; e += kThreads)
+      if (!((st.valid_mask >> (e / kChunk)) & 1u)) p.lse[slot_vec_offset(p, c.gbh, c.t, 0) + e] = -__builtin_inff();
+  }
+  wait_async_copies();
+  __syncthreads();
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
-  const T* kbase = static_cast<const T*>(p.k) + (static_cast<int64_t>(c.b) * p.H + c.h) * p.n_kv * kChunk * kDim;
-  const T* vbase = static_cast<const T*>(p.v) + (static_cast<int64_t>(c.b) * p.H + c.h) * p.n_kv * kChunk * kDim;
-  __syncthreads();
-
-  for (int n = 0; n < st.n; ++n) {
-    const int64_t j = st.j[n];
-    stage_tile<T, true, false>(kbase + j * kChunk * kDim, Ks, nullptr);
-    stage_tile<T, false, true>(vbase + j * kChunk * kDim, nullptr, Vt);
-    __syncthreads();
-
+  auto body = [&](int n, const char* cur, char* nxt) {
+    if (n + 1 < nslots) fill(n + 1, nxt);
+    const char* Ks = cur;
+    const char* Vs = cur + TL::kBytes;
     f32x16_t sacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       sacc[tt] = zero16();
-      const T* arow = Ks + (32 * tt + pi_row(li)) * C::kLd + 8 * hl;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        Frag<T> a;
-        a.load(arow + 16 * s);
-        sacc[tt] = mma(a, qf[s], sacc[tt]);
-      }
+      for (int s = 0; s < 4; ++s) sacc[tt] = mma(row_frag<T>(Ks, 32 * tt + pi_row(li), 16 * s + 8 * hl), qf[s], sacc[tt]);
     }
-    // softmax over the 64 keys of this chunk (32 here, 32 in lane ^ 32)
-    float mx = sacc[0][0];
+    // softmax over the 64 keys of this chunk (32 in this lane, 32 in lane ^ 32)
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
     mx = xor32_max(mx);
     const float bias = -mx * c2;
     float l = 0.f;
@@ -201,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
         l += e;
       }
     l = xor32_sum(l);
-    if (hl == 0) lse_s[my_q * kMaxTopk + st.slot[n]] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
+    if (p.lse && hl == 0)
+      p.lse[slot_vec_offset(p, c.gbh, c.t, st.slot[n]) + my_q] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
     const float f = st.w[n] / l;
     Frag<T> pf[4];
 #pragma unroll
@@ -212,16 +201,16 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
       pf[s].set(x);
     }
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const T* arow = Vt + (32 * dt + li) * C::kLd + 16 * hl;
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        Frag<T> a;
-        a.load(arow + 32 * (s >> 1) + 8 * (s & 1));
-        oacc[dt] = mma(a, pf[s], oacc[dt]);
-      }
-    }
+      for (int s = 0; s < 4; ++s)
+        oacc[dt] = mma(col_frag<T>(Vs, 32 * (s >> 1) + 16 * hl + 8 * (s & 1), 32 * dt), pf[s], oacc[dt]);
+    wait_async_copies();
     __syncthreads();
+  };
+  for (int n = 0; n < nslots; n += 2) {
+    body(n, buf0, buf1);
+    if (n + 1 < nslots) body(n + 1, buf1, buf0);
   }
 
   T* o = static_cast<T*>(p.o) + (qrow0 + my_q) * kDim;
@@ -231,20 +220,14 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
     for (int a = 0; a < 4; ++a)
       store4(o + 32 * dt + 8 * a + 4 * hl, oacc[dt][4 * a], oacc[dt][4 * a + 1], oacc[dt][4 * a + 2],
              oacc[dt][4 * a + 3]);
-  if (p.lse) {
-    __syncthreads();
-    float* lse = p.lse + qrow0 * p.K;
-    for (int e = tid; e < kChunk * p.K; e += kThreads) lse[e] = lse_s[(e / p.K) * kMaxTopk + e % p.K];
-  }
 }
 
 // ------------------------------------------------------------- backward, query-major (dQ)
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
-  using C = TileCfg<T>;
-  __shared__ __align__(16) T Ks[kChunk * C::kLd];
-  __shared__ __align__(16) T Kt[kDim * C::kLd];
-  __shared__ __align__(16) T Vs[kChunk * C::kLd];
+  using TL = Tile<T>;
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes];  // [K tile, V tile]
+  __shared__ __align__(1024) char buf1[2 * TL::kBytes];
   __shared__ float dw_s[2][kMaxTopk];
   __shared__ SlotTable st;
 
@@ -252,13 +235,12 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
   const int li = lane & 31, hl = lane >> 5;
   const QTileCoord c = query_tile_coord(p);
   const int64_t Lq = p.n_q * kChunk;
-  const int64_t qrow0 = ((static_cast<int64_t>(c.g) * p.B + c.b) * p.H + c.h) * Lq + c.t * kChunk;
+  const int64_t qrow0 = c.gbh * Lq + c.t * kChunk;
   const int my_q = 32 * wave + li;
   const int64_t row = c.t - p.shift;
 
   if (tid == 0) build_slot_table(st, p, c.g, c.b, row);
   if (tid < 2 * kMaxTopk) dw_s[tid / kMaxTopk][tid % kMaxTopk] = 0.f;
-
   Frag<T> qf[4], df[4];
   const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
   const T* dout = static_cast<const T*>(p.dout) + (qrow0 + my_q) * kDim;
@@ -267,54 +249,59 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     qf[s].load(q + 16 * s + 8 * hl);
     df[s].load(dout + 16 * s + 8 * hl);
   }
-  f32x16_t dqacc[2] = {zero16(), zero16()};
-  const float c2 = p.attn_scale * kLog2e;
-  const T* kbase = static_cast<const T*>(p.k) + (static_cast<int64_t>(c.b) * p.H + c.h) * p.n_kv * kChunk * kDim;
-  const T* vbase = static_cast<const T*>(p.v) + (static_cast<int64_t>(c.b) * p.H + c.h) * p.n_kv * kChunk * kDim;
   __syncthreads();
 
-  for (int n = 0; n < st.n; ++n) {
-    const int64_t j = st.j[n];
-    const int slot = st.slot[n];
-    stage_tile<T, true, true>(kbase + j * kChunk * kDim, Ks, Kt);
-    stage_tile<T, true, false>(vbase + j * kChunk * kDim, Vs, nullptr);
-    const float lse_b = p.lse_in[(qrow0 + my_q) * p.K + slot] * kLog2e;
-    __syncthreads();
+  const int nslots = st.n;
+  float lse_next = 0.f;
+  auto fill = [&](int n, char* buf) {
+    tile_load_async<T, kWaves>(kv_tile<T>(p.k, p, c.b, c.h, st.j[n]), buf);
+    tile_load_async<T, kWaves>(kv_tile<T>(p.v, p, c.b, c.h, st.j[n]), buf + TL::kBytes);
+    lse_next = p.lse_in[slot_vec_offset(p, c.gbh, c.t, st.slot[n]) + my_q];
+  };
+  if (nslots > 0) fill(0, buf0);
+  if (c.h == 0 && row >= 0 && tid < p.K)
+    p.wts[((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.K + tid] = st.w_all[tid];
+  wait_async_copies();
+  __syncthreads();
 
+  f32x16_t dqacc[2] = {zero16(), zero16()};
+  const float c2 = p.attn_scale * kLog2e;
+  auto body = [&](int n, const char* cur, char* nxt) {
+    const int slot = st.slot[n];
+    const float lse_b = lse_next * kLog2e;
+    if (n + 1 < nslots) fill(n + 1, nxt);
+    const char* Ks = cur;
+    const char* Vs = cur + TL::kBytes;
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       sacc[tt] = zero16();
       pacc[tt] = zero16();
-      const T* krow = Ks + (32 * tt + pi_row(li)) * C::kLd + 8 * hl;
-      const T* vrow = Vs + (32 * tt + pi_row(li)) * C::kLd + 8 * hl;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        Frag<T> a, bv;
-        a.load(krow + 16 * s);
-        bv.load(vrow + 16 * s);
-        sacc[tt] = mma(a, qf[s], sacc[tt]);
-        pacc[tt] = mma(bv, df[s], pacc[tt]);
+        sacc[tt] = mma(row_frag<T>(Ks, 32 * tt + pi_row(li), 16 * s + 8 * hl), qf[s], sacc[tt]);
+        pacc[tt] = mma(row_frag<T>(Vs, 32 * tt + pi_row(li), 16 * s + 8 * hl), df[s], pacc[tt]);
       }
     }
-    // P = exp(z - lse); e = sum_u P dP'
-    float e = 0.f;
+    // P_w = w exp(z - lse) (log2 w folded into the bias); e = sum_u P dP' = (sum_u P_w dP') / w
+    const float w = st.w[n];
+    const float bias = __builtin_amdgcn_logf(w) - lse_b;
+    float ew = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, -lse_b));
+        const float pr = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
         sacc[tt][r] = pr;
-        e = __builtin_fmaf(pr, pacc[tt][r], e);
+        ew = __builtin_fmaf(pr, pacc[tt][r], ew);
       }
-    e = xor32_sum(e);
-    if (hl == 0) p.delta[(qrow0 + my_q) * p.K + slot] = e;
-    // per-wave sum of e over its 32 queries, fixed butterfly order
-    float es = e;
+    ew = xor32_sum(ew);
+    const float e = w > 0.f ? ew / w : 0.f;  // w underflows to 0 only if P_w (and dz) is 0 anyway
+    if (hl == 0) p.delta[slot_vec_offset(p, c.gbh, c.t, slot) + my_q] = e;
+    float es = e;  // per-wave sum of e over its 32 queries, fixed butterfly order
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) es += __shfl_xor(es, off, 64);
     if (lane == 0) dw_s[wave][slot] = es;
-    const float w = st.w[n];
     Frag<T> zf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -322,21 +309,21 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 #pragma unroll
       for (int ee = 0; ee < 8; ++ee) {
         const int tt = s >> 1, r = 8 * (s & 1) + ee;
-        x[ee] = w * sacc[tt][r] * (pacc[tt][r] - e);
+        x[ee] = sacc[tt][r] * (pacc[tt][r] - e);
       }
       zf[s].set(x);
     }
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const T* arow = Kt + (32 * dt + li) * C::kLd + 16 * hl;
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        Frag<T> a;
-        a.load(arow + 32 * (s >> 1) + 8 * (s & 1));
-        dqacc[dt] = mma(a, zf[s], dqacc[dt]);
-      }
-    }
+      for (int s = 0; s < 4; ++s)
+        dqacc[dt] = mma(col_frag<T>(Ks, 32 * (s >> 1) + 16 * hl + 8 * (s & 1), 32 * dt), zf[s], dqacc[dt]);
+    wait_async_copies();
     __syncthreads();
+  };
+  for (int n = 0; n < nslots; n += 2) {
+    body(n, buf0, buf1);
+    if (n + 1 < nslots) body(n + 1, buf1, buf0);
   }
 
   T* dq = static_cast<T*>(p.dq) + (qrow0 + my_q) * kDim;
@@ -354,15 +341,31 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 }
 
 // ------------------------------------------------------------- backward, key-major (dK, dV)
+struct PairRef {
+  int g, slot;
+  int64_t row, t;
+};
+
+// Entry codes are (g * n_q + row) * K + slot < 2^31; decoded in wave-uniform 32-bit arithmetic.
+__device__ __forceinline__ PairRef decode_pair(const AttendParams& p, int32_t code) {
+  const int32_t c = __builtin_amdgcn_readfirstlane(code);
+  const int32_t nq = static_cast<int32_t>(p.n_q);
+  PairRef r;
+  r.slot = c % p.K;
+  const int32_t gr = c / p.K;
+  r.row = gr % nq;
+  r.g = gr / nq;
+  r.t = r.row + p.shift;
+  return r;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
-  using C = TileCfg<T>;
-  __shared__ __align__(16) T Qs[kChunk * C::kLd];
-  __shared__ __align__(16) T Qt[kDim * C::kLd];
-  __shared__ __align__(16) T Ds[kChunk * C::kLd];
-  __shared__ __align__(16) T Dt[kDim * C::kLd];
-  __shared__ __align__(16) float lse_s[kChunk];
-  __shared__ __align__(16) float del_s[kChunk];
+  using TL = Tile<T>;
+  constexpr int kVecBytes = 2 * kChunk * 4;                      // lse and e of one pair
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];  // [Q tile, dO tile, lse, e]
+  __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
+  __shared__ i32x2_t ents[kEntRound];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hl = lane >> 5;
@@ -386,73 +389,92 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   f32x16_t dvacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
   const int64_t Lq = p.n_q * kChunk;
-  const int32_t* seg = p.seg + static_cast<int64_t>(b) * (p.n_kv + 1);
-  const int32_t beg = seg[j], end = seg[j + 1];
-  const int32_t* pairs = p.pairs + static_cast<int64_t>(b) * p.pair_cap;
+  const int64_t segment = static_cast<int64_t>(b) * p.n_kv + j;
+  const int32_t count = p.counts[segment];
+  const i32x2_t* list = reinterpret_cast<const i32x2_t*>(p.pairs) + segment * p.pair_cap;
 
-  for (int32_t pr = beg; pr < end; ++pr) {
-    const int32_t code = pairs[pr];
-    const int slot = code % p.K;
-    const int64_t gr = code / p.K;  // g * n_q + row
-    const int64_t row = gr % p.n_q;
-    const int g = static_cast<int>(gr / p.n_q);
-    const int64_t t = row + p.shift;
-    const float w = p.wts[((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K + slot];
-    const int64_t qrow0 = ((static_cast<int64_t>(g) * p.B + b) * p.H + h) * Lq + t * kChunk;
-    stage_tile<T, true, true>(static_cast<const T*>(p.q) + qrow0 * kDim, Qs, Qt);
-    stage_tile<T, true, true>(static_cast<const T*>(p.dout) + qrow0 * kDim, Ds, Dt);
-    if (tid < kChunk) lse_s[tid] = p.lse_in[(qrow0 + tid) * p.K + slot] * kLog2e;
-    else del_s[tid - kChunk] = p.delta[(qrow0 + tid - kChunk) * p.K + slot];
-    __syncthreads();
+  // The list is walked in rounds of up to kEntRound entries {code, weight}, staged in LDS so
+  // that the pipelined loop never waits on a global load.
+  float w_next = 0.f;
+  auto fill = [&](const i32x2_t ent, char* buf) {
+    const PairRef r = decode_pair(p, ent[0]);
+    w_next = __int_as_float(__builtin_amdgcn_readfirstlane(ent[1]));
+    const int64_t gbh = (static_cast<int64_t>(r.g) * p.B + b) * p.H + h;
+    const int64_t qrow0 = gbh * Lq + r.t * kChunk;
+    tile_load_async<T, kWaves>(static_cast<const T*>(p.q) + qrow0 * kDim, buf);
+    tile_load_async<T, kWaves>(static_cast<const T*>(p.dout) + qrow0 * kDim, buf + TL::kBytes);
+    if (lane < 16) {  // wave 0 copies the 64 lse values, wave 1 the 64 e values
+      const float* src = (wave == 0 ? p.lse_in : p.delta) + slot_vec_offset(p, gbh, r.t, r.slot) + 4 * lane;
+      copy16_async(src, buf + 2 * TL::kBytes + wave * kChunk * 4);
+    }
+  };
 
-    // S[q][u] and dP'[q][u] for the 64 queries (two tiles) and this wave's 32 keys.
+  int32_t n = 0;  // entries in the current round
+  auto body = [&](int32_t pr, const char* cur, char* nxt) {
+    const float w = w_next;
+    if (pr + 1 < n) fill(ents[pr + 1], nxt);
+    const char* Qs = cur;
+    const char* Ds = cur + TL::kBytes;
+    const float* lse_v = reinterpret_cast<const float*>(cur + 2 * TL::kBytes);
+    const float* del_v = lse_v + kChunk;
+    // S[q][u] and dP'[q][u] for the 64 queries (two tiles) and this wave's 32 keys
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       sacc[qt] = zero16();
       pacc[qt] = zero16();
-      const T* qr = Qs + (32 * qt + pi_row(li)) * C::kLd + 8 * hl;
-      const T* dr = Ds + (32 * qt + pi_row(li)) * C::kLd + 8 * hl;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        Frag<T> a, bq;
-        a.load(qr + 16 * s);
-        bq.load(dr + 16 * s);
-        sacc[qt] = mma(a, kf[s], sacc[qt]);
-        pacc[qt] = mma(bq, vf[s], pacc[qt]);
+        sacc[qt] = mma(row_frag<T>(Qs, 32 * qt + pi_row(li), 16 * s + 8 * hl), kf[s], sacc[qt]);
+        pacc[qt] = mma(row_frag<T>(Ds, 32 * qt + pi_row(li), 16 * s + 8 * hl), vf[s], pacc[qt]);
       }
     }
-    // lane holds queries 32 qt + 16 hl + r
+    // lane holds queries 32 qt + 16 hl + r; P_w = w exp(z - lse) with log2(w) folded in the bias
+    const float lw = __builtin_amdgcn_logf(w);
     Frag<T> pf[4], zf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int qt = s >> 1;
       const int q0 = 32 * qt + 16 * hl + 8 * (s & 1);
+      const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(lse_v + q0);
+      const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(lse_v + q0 + 4);
+      const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(del_v + q0);
+      const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(del_v + q0 + 4);
       float xp[8], xz[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * (s & 1) + e;
-        const float pw = w * fast_exp2(__builtin_fmaf(sacc[qt][r], c2, -lse_s[q0 + e]));
+        const float lse_q = e < 4 ? l0[e] : l1[e - 4];
+        const float del_q = e < 4 ? d0[e] : d1[e - 4];
+        const float pw = fast_exp2(__builtin_fmaf(sacc[qt][r], c2, __builtin_fmaf(-lse_q, kLog2e, lw)));
         xp[e] = pw;
-        xz[e] = pw * (pacc[qt][r] - del_s[q0 + e]);
+        xz[e] = pw * (pacc[qt][r] - del_q);
       }
       pf[s].set(xp);
       zf[s].set(xz);
     }
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const T* dtr = Dt + (32 * dt + li) * C::kLd + 16 * hl;
-      const T* qtr = Qt + (32 * dt + li) * C::kLd + 16 * hl;
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        Frag<T> a, bq;
-        a.load(dtr + 32 * (s >> 1) + 8 * (s & 1));
-        bq.load(qtr + 32 * (s >> 1) + 8 * (s & 1));
-        dvacc[dt] = mma(a, pf[s], dvacc[dt]);
-        dkacc[dt] = mma(bq, zf[s], dkacc[dt]);
+        const int r0 = 32 * (s >> 1) + 16 * hl + 8 * (s & 1);
+        dvacc[dt] = mma(col_frag<T>(Ds, r0, 32 * dt), pf[s], dvacc[dt]);
+        dkacc[dt] = mma(col_frag<T>(Qs, r0, 32 * dt), zf[s], dkacc[dt]);
       }
-    }
+    wait_async_copies();
     __syncthreads();
+  };
+  for (int32_t round0 = 0; round0 < count; round0 += kEntRound) {
+    n = count - round0 < kEntRound ? count - round0 : kEntRound;
+    for (int e = tid; e < n; e += kThreads) ents[e] = list[round0 + e];
+    __syncthreads();
+    fill(ents[0], buf0);
+    wait_async_copies();
+    __syncthreads();
+    for (int32_t pr = 0; pr < n; pr += 2) {
+      body(pr, buf0, buf1);
+      if (pr + 1 < n) body(pr + 1, buf1, buf0);
+    }
   }
 
   T* dk = static_cast<T*>(p.dk) + krow * kDim;
@@ -470,102 +492,122 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
 }
 
 // ------------------------------------------------------------- inverse retrieval index
-// One workgroup per batch row b.  Entry e = (g * n_q + row) * K + slot; key = (j << 32) | e for
-// retrievals that feed an existing query chunk (row + shift < n_q) and name a chunk j < n_kv,
-// all ones otherwise.  A bitonic sort in LDS orders them by (j, e); segment offsets come from
-// binary search.  The same pass writes the fusion weights of every row.
-constexpr int kCsrThreads = 256;
-constexpr int kCsrCap = 8192;
+// For one batch row and 64 consecutive key chunks (lane = chunk j), list the retrievals that
+// selected each chunk as entries {(group, row, slot) code, fusion weight}, in (group, row) order.
+// Retrieval rows, flattened as gr = g * n_q + row, are handled in rounds of kIdxWords 32-row
+// words.  Each round copies the rows' idx values to LDS (coalesced), then: phase 1, wave w
+// builds for words w, w + 4, ... the per-lane bit mask of the rows naming its chunk (all lanes
+// read the same LDS word, a broadcast); phase 2, a running prefix of the masks' popcounts gives
+// every word its first output position; phase 3, each (chunk, word) writes its rows' entries
+// there.  Only rows that feed a query chunk (row + shift < n_q) and can hold a chunk of this
+// block (global chunk index q_base + row above the block's first chunk) are marked.  Runs after
+// the query-major pass, which writes the fusion weights.
+constexpr int kIdxThreads = 256;
+constexpr int kIdxWords = 32;
 
-__global__ __launch_bounds__(kCsrThreads) void csr_build_kernel(AttendParams p) {
-  __shared__ uint64_t keys[kCsrCap];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int n_ent = p.pair_cap;
-  int n2 = 1;
-  while (n2 < n_ent) n2 <<= 1;
-  for (int e = tid; e < n2; e += kCsrThreads) {
-    uint64_t key = ~0ull;
-    if (e < n_ent) {
-      const int slot = e % p.K;
-      const int64_t gr = e / p.K;
+__global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams p) {
+  __shared__ int32_t idx_s[kIdxWords * 32 * kMaxTopk];
+  __shared__ uint32_t mask[kIdxWords][64];
+  __shared__ int32_t first[kIdxWords][64];
+  __shared__ int32_t total[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nblk = (p.n_kv + 63) / 64;
+  const int b = static_cast<int>(blockIdx.x / nblk);
+  const int64_t j0 = (blockIdx.x % nblk) * 64;
+  const int64_t j = j0 + lane;
+  int64_t row_lo = j0 - p.q_base + 1;
+  if (row_lo < 0) row_lo = 0;
+  const int64_t row_hi = p.n_q - p.shift;
+  const int64_t n_rows = static_cast<int64_t>(p.G) * p.n_q;
+  const int64_t n_words = (n_rows + 31) / 32;
+  const int K = p.K;
+  if (tid < 64) total[tid] = 0;
+  i32x2_t* out = reinterpret_cast<i32x2_t*>(p.pairs) + (static_cast<int64_t>(b) * p.n_kv + j) * p.pair_cap;
+
+  for (int64_t w0 = 0; w0 < n_words; w0 += kIdxWords) {
+    const int nw = static_cast<int>(n_words - w0 < kIdxWords ? n_words - w0 : kIdxWords);
+    const int64_t gr0 = w0 * 32;
+    const int64_t nr = (gr0 + nw * 32 <= n_rows) ? nw * 32 : n_rows - gr0;
+    for (int64_t e = tid; e < nr * K; e += kIdxThreads) {
+      const int64_t gr = gr0 + e / K;
       const int64_t row = gr % p.n_q;
       const int g = static_cast<int>(gr / p.n_q);
-      const int32_t jj = p.idx[((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K + slot];
-      if (row + p.shift < p.n_q && jj >= 0 && jj < p.n_kv)
-        key = (static_cast<uint64_t>(jj) << 32) | static_cast<uint32_t>(e);
+      idx_s[e] = p.idx[((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * K + e % K];
     }
-    keys[e] = key;
-  }
-  // fusion weights of every (g, row) of this batch row
-  for (int64_t gr = tid; gr < static_cast<int64_t>(p.G) * p.n_q; gr += kCsrThreads) {
-    const int64_t row = gr % p.n_q;
-    const int g = static_cast<int>(gr / p.n_q);
-    const int64_t base = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K;
-    float w[kMaxTopk];
-    bool valid[kMaxTopk];
-    fusion_weights(p.idx + base, p.score + base, p.K, p.n_kv, w, valid);
-    for (int k = 0; k < p.K; ++k) p.wts[base + k] = w[k];
-  }
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int e = tid; e < n2 / 2; e += kCsrThreads) {
-        const int lo = 2 * e - (e & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t a = keys[lo], c = keys[hi];
-        if ((a > c) == up) {
-          keys[lo] = c;
-          keys[hi] = a;
+    __syncthreads();
+    // phase 1: masks
+    for (int wl = wave; wl < nw; wl += kIdxThreads / 64) {
+      uint32_t m = 0;
+      for (int bit = 0; bit < 32; ++bit) {
+        const int64_t lr = static_cast<int64_t>(wl) * 32 + bit;
+        if (lr >= nr) break;
+        const int64_t row = (gr0 + lr) % p.n_q;
+        if (row < row_lo || row >= row_hi) continue;
+        const int32_t* ir = idx_s + lr * K;
+        bool hit = false;
+        for (int k = 0; k < K; ++k) hit |= ir[k] == j;
+        m |= hit ? (1u << bit) : 0u;
+      }
+      mask[wl][lane] = m;
+    }
+    __syncthreads();
+    // phase 2: first output position of every word
+    if (tid < 64) {
+      int32_t run = total[tid];
+      for (int wl = 0; wl < nw; ++wl) {
+        first[wl][tid] = run;
+        run += __popc(mask[wl][tid]);
+      }
+      total[tid] = run;
+    }
+    __syncthreads();
+    // phase 3: entries
+    if (j < p.n_kv) {
+      for (int wl = wave; wl < nw; wl += kIdxThreads / 64) {
+        uint32_t m = mask[wl][lane];
+        int32_t pos = first[wl][lane];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          const int64_t lr = static_cast<int64_t>(wl) * 32 + bit;
+          const int64_t gr = gr0 + lr;
+          int k = 0;
+          while (idx_s[lr * K + k] != j) ++k;  // the first slot naming j; one exists (mask bit)
+          const int64_t row = gr % p.n_q;
+          const int g = static_cast<int>(gr / p.n_q);
+          const int64_t rbase = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * K;
+          out[pos++] = i32x2_t{static_cast<int32_t>(gr * K + k), __float_as_int(p.wts[rbase + k])};
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
   }
-  int32_t* pairs = p.pairs + static_cast<int64_t>(b) * p.pair_cap;
-  for (int e = tid; e < n_ent; e += kCsrThreads)
-    pairs[e] = keys[e] == ~0ull ? -1 : static_cast<int32_t>(keys[e] & 0xffffffffu);
-  int32_t* seg = p.seg + static_cast<int64_t>(b) * (p.n_kv + 1);
-  for (int64_t jj = tid; jj <= p.n_kv; jj += kCsrThreads) {
-    const uint64_t target = static_cast<uint64_t>(jj) << 32;
-    int lo = 0, hi = n_ent;  // first position with key >= target
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (keys[mid] < target) lo = mid + 1;
-      else hi = mid;
-    }
-    seg[jj] = lo;
-  }
+  if (tid < 64 && j < p.n_kv) p.counts[static_cast<int64_t>(b) * p.n_kv + j] = total[tid];
 }
 
 // ------------------------------------------------------------- d(score)
 // dscore_k = w_k (dw_k - sum_k' w_k' dw_k'), dw_k = sum over heads (in order) of the per-head
-// sums of e over the chunk's tokens.  One thread per (g, b, row).
+// sums of e over the chunk's tokens.  Sixteen lanes per (g, b, row), one lane per slot.
 __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int k = threadIdx.x & 15;
   const int64_t rows = static_cast<int64_t>(p.G) * p.B * p.n_q;
-  if (gid >= rows) return;
+  const bool in_range = gid < rows && k < p.K;
   const int64_t row = gid % p.n_q;
-  float* ds = p.dscore + gid * p.K;
-  const bool used = row + p.shift < p.n_q;
-  float dw[kMaxTopk];
-  float wdw = 0.f;
-  for (int k = 0; k < p.K; ++k) {
-    float acc = 0.f;
-    const float w = p.wts[gid * p.K + k];
+  bool valid = false;
+  float w = 0.f, dw = 0.f;
+  if (in_range) {
     const int32_t jj = p.idx[gid * p.K + k];
-    if (used && jj >= 0 && jj < p.n_kv) {
-      for (int h = 0; h < p.H; ++h) acc += p.dw_part[(gid * p.H + h) * p.K + k];
+    valid = row + p.shift < p.n_q && jj >= 0 && jj < p.n_kv;
+    if (valid) {
+      w = p.wts[gid * p.K + k];
+      for (int h = 0; h < p.H; ++h) dw += p.dw_part[(gid * p.H + h) * p.K + k];
     }
-    dw[k] = acc;
-    wdw = __builtin_fmaf(w, acc, wdw);
   }
-  for (int k = 0; k < p.K; ++k) {
-    const int32_t jj = p.idx[gid * p.K + k];
-    const bool valid = used && jj >= 0 && jj < p.n_kv;
-    ds[k] = valid ? p.wts[gid * p.K + k] * (dw[k] - wdw) : 0.f;
-  }
+  float wdw = w * dw;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) wdw += __shfl_xor(wdw, off, 16);
+  if (in_range) p.dscore[gid * p.K + k] = valid ? w * (dw - wdw) : 0.f;
 }
 
 }  // namespace
@@ -580,7 +622,8 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
 }
 
 hipError_t launch_csr_build(const AttendParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(csr_build_kernel, dim3(static_cast<uint32_t>(p.B)), dim3(kCsrThreads), 0, s, p);
+  const int64_t blocks = static_cast<int64_t>(p.B) * ((p.n_kv + 63) / 64);
+  hipLaunchKernelGGL(inverse_index_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kIdxThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -604,7 +647,7 @@ hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s) {
 
 hipError_t launch_score_grad(const AttendParams& p, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(p.G) * p.B * p.n_q;
-  const int64_t blocks = (rows + 255) / 256;
+  const int64_t blocks = (rows + 15) / 16;
   hipLaunchKernelGGL(score_grad_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -34,7 +34,6 @@ thread_local ProfState t_prof;
 constexpr int kRetrieveThreads = 256;
 constexpr int kRetrieveMinBlock = 1024;  // candidates per block before splitting a row
 constexpr int kRetrieveMaxBlocks = 256;  // partial lists per row merged by the second kernel
-constexpr int64_t kCsrCap = 8192;        // retrievals per batch row the inverse index sorts
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -85,6 +84,8 @@ gca_status validate_problem(const gca_problem* p) {
   const int64_t gbh = static_cast<int64_t>(p->G) * p->B * p->H;
   if (p->n_q_chunks > 0 && gbh > big / p->n_q_chunks) return GCA_ERR_UNSUPPORTED;
   if (p->n_kv_chunks > 0 && static_cast<int64_t>(p->B) * p->H > big / p->n_kv_chunks) return GCA_ERR_UNSUPPORTED;
+  // (group, row, slot) codes of the inverse index travel as int32
+  if (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk > big) return GCA_ERR_UNSUPPORTED;
   return GCA_OK;
 }
 
@@ -113,7 +114,7 @@ RetrievePlan plan_retrieve(const gca_problem* p) {
 }
 
 struct BackwardLayout {
-  size_t delta, dw_part, wts, pairs, seg, total;
+  size_t delta, dw_part, wts, pairs, counts, total;
 };
 
 BackwardLayout plan_backward(const gca_problem* p) {
@@ -129,9 +130,9 @@ BackwardLayout plan_backward(const gca_problem* p) {
   l.wts = off;
   off += align_up(G * B * nq * K * sizeof(float));
   l.pairs = off;
-  off += align_up(B * G * nq * K * sizeof(int32_t));
-  l.seg = off;
-  off += align_up(B * (nkv + 1) * sizeof(int32_t));
+  off += align_up(B * nkv * G * nq * 2 * sizeof(int32_t));
+  l.counts = off;
+  off += align_up(B * nkv * sizeof(int32_t));
   l.total = off;
   return l;
 }
@@ -165,7 +166,8 @@ AttendParams attend_params(const gca_problem* p) {
   a.H = p->H;
   a.K = p->topk;
   a.shift = p->shift;
-  a.pair_cap = static_cast<int32_t>(static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk);
+  a.q_base = p->q_chunk_base;
+  a.pair_cap = static_cast<int32_t>(static_cast<int64_t>(p->G) * p->n_q_chunks);
   a.attn_scale = p->attn_scale;
   return a;
 }
@@ -184,8 +186,6 @@ gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes)
     case GCA_OP_RETRIEVE: *bytes = plan_retrieve(problem).ws; return GCA_OK;
     case GCA_OP_FORWARD: *bytes = 0; return GCA_OK;
     case GCA_OP_BACKWARD:
-      if (static_cast<int64_t>(problem->G) * problem->n_q_chunks * problem->topk > kCsrCap)
-        return GCA_ERR_UNSUPPORTED;
       *bytes = plan_backward(problem).total;
       return GCA_OK;
     default: return GCA_ERR_INVALID_ARGUMENT;
@@ -247,7 +247,7 @@ gca_status gca_forward(const gca_problem* problem, const void* q, const void* k,
   GCA_TRY(check_tensor(idx, any, 4));
   GCA_TRY(check_tensor(score, any, 4));
   GCA_TRY(check_tensor(o, any, 16));
-  if (lse != nullptr) GCA_TRY(check_tensor(lse, any, 4));
+  if (lse != nullptr) GCA_TRY(check_tensor(lse, any, 16));
   GCA_TRY(check_ws(0, ws, ws_bytes));
   if (!any) return GCA_OK;
 
@@ -270,7 +270,6 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
                         void* stream) {
   GCA_TRY(validate_problem(problem));
   const gca_problem* p = problem;
-  if (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk > kCsrCap) return GCA_ERR_UNSUPPORTED;
   const bool any = p->n_q_chunks > 0;
   const bool kv = p->n_kv_chunks > 0;
   GCA_TRY(check_tensor(q, any, 16));
@@ -278,7 +277,7 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   GCA_TRY(check_tensor(v, kv, 16));
   GCA_TRY(check_tensor(idx, any, 4));
   GCA_TRY(check_tensor(score, any, 4));
-  GCA_TRY(check_tensor(lse, any, 4));
+  GCA_TRY(check_tensor(lse, any, 16));
   GCA_TRY(check_tensor(dout, any, 16));
   GCA_TRY(check_tensor(dq, any, 16));
   GCA_TRY(check_tensor(dk, kv, 16));
@@ -306,12 +305,12 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
   a.wts = reinterpret_cast<float*>(w + L.wts);
   a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
-  a.seg = reinterpret_cast<int32_t*>(w + L.seg);
+  a.counts = reinterpret_cast<int32_t*>(w + L.counts);
   const bool f32 = p->dtype == GCA_F32;
-  // With no query chunk, only the inverse index (empty) and the key-major pass (which writes
-  // zero dk, dv for chunks nobody retrieved) run.
-  GCA_TRY(launch(kCsrBuild, s, [&] { return launch_csr_build(a, s); }));
+  // With no query chunk, only the inverse index (empty lists) and the key-major pass (which
+  // writes zero dk, dv for chunks nobody retrieved) run.
   if (any) GCA_TRY(launch(kBwdQuery, s, [&] { return launch_bwd_query(a, f32, s); }));
+  if (kv) GCA_TRY(launch(kCsrBuild, s, [&] { return launch_csr_build(a, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
   if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
   return GCA_OK;

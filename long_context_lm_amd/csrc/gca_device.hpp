@@ -27,6 +27,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
 
 struct bf16_t {  // storage type of one bf16 value
   uint16_t bits;
@@ -48,8 +49,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair with round-to-nearest-even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2_t));
 }
 
 // ------------------------------------------------------------------ fragments
@@ -136,6 +141,108 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t bid, int64_t nblock
   const int64_t x = bid % nx, n = bid / nx;
   const int64_t q = nblocks / nx, rem = nblocks % nx;
   return x * q + (x < rem ? x : rem) + n;
+}
+
+}  // namespace gca
+
+namespace gca {
+
+// ------------------------------------------------------------------ 64x64 tiles in LDS
+// Row-major, 64 elements per row, no padding; the 16-byte chunks of row R sit at chunk position
+// c ^ swz(R).  swz spreads (a) the eight rows pi(rho), rho = 8a..8a+7, that one read of eight
+// consecutive lanes touches, and (b) four consecutive rows read together by a transposing read,
+// over distinct bank groups.
+template <typename T>
+struct Tile {
+  static constexpr int kElemsPerChunk = 16 / static_cast<int>(sizeof(T));  // 8 bf16 or 4 fp32
+  static constexpr int kChunksPerRow = kDim / kElemsPerChunk;
+  static constexpr int kRowBytes = kDim * static_cast<int>(sizeof(T));
+  static constexpr int kBytes = kChunk * kRowBytes;
+  static constexpr int kChunks = kBytes / 16;
+  __device__ static __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 4) & 1); }
+  __device__ static __forceinline__ int chunk_offset(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+  }
+  __device__ static __forceinline__ int elem_offset(int row, int col) {
+    return chunk_offset(row, col / kElemsPerChunk) + (col % kElemsPerChunk) * static_cast<int>(sizeof(T));
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// Asynchronous copy global -> LDS of 16 bytes per lane: lane l of the wave writes bytes
+// [16 l, 16 l + 16) after `lds_wave_base` (which must be the same in every lane).
+__device__ __forceinline__ void copy16_async(const void* gsrc, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)(gsrc), (lds_void_t*)(lds_wave_base), 16, 0, 0);
+}
+
+// Start copying one 64x64 tile (global row stride 64 elements) into swizzled LDS.  All threads of
+// a workgroup of kWaves waves call it; each wave issues its share of the 1 KiB wave copies.  The
+// data is usable after wait_async_copies() and a workgroup barrier.
+template <typename T, int kWaves>
+__device__ __forceinline__ void tile_load_async(const T* __restrict__ g, char* lds) {
+  using TL = Tile<T>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const char* gb = reinterpret_cast<const char*>(g);
+#pragma unroll
+  for (int n = 0; n < TL::kChunks / 64 / kWaves; ++n) {
+    const int blk = n * kWaves + wave;
+    const int pos = blk * 64 + lane;
+    const int row = pos / TL::kChunksPerRow;
+    const int chunk = (pos % TL::kChunksPerRow) ^ TL::swz(row);
+    // uniform tile base + 32-bit lane offset, so the copy can use the scalar-base address form
+    const uint32_t off = static_cast<uint32_t>(row * TL::kRowBytes + chunk * 16);
+    copy16_async(gb + off, lds + blk * 1024);
+  }
+}
+
+__device__ __forceinline__ void wait_async_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// MFMA operand holding 8 consecutive columns of one tile row: lane gets X[row][col0 .. col0+7].
+__device__ __forceinline__ Frag<bf16_t> frag_row(const char* lds, int row, int col0, bf16_t*) {
+  Frag<bf16_t> f;
+  f.v = *reinterpret_cast<const u32x4_t*>(lds + Tile<bf16_t>::chunk_offset(row, col0 >> 3));
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_row(const char* lds, int row, int col0, float*) {
+  Frag<float> f;
+  f.v0 = *reinterpret_cast<const f32x4_t*>(lds + Tile<float>::chunk_offset(row, col0 >> 2));
+  f.v1 = *reinterpret_cast<const f32x4_t*>(lds + Tile<float>::chunk_offset(row, (col0 >> 2) + 1));
+  return f;
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// MFMA operand holding 8 consecutive rows of one tile column: lane l (rho = l % 32) gets
+// X[r0 + e][c_base + rho], e = 0..7 (r0 the same within each half-wave).  For bf16 the 16 lanes of
+// a block read a 4-row x 16-column block in row-major 8-byte pieces with ds_read_b64_tr_b16, which
+// hands lane i of the block the four rows of column i.
+__device__ __forceinline__ Frag<bf16_t> frag_col(const char* lds, int r0, int c_base, bf16_t*) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, bb = (lane >> 4) & 1;
+  const int col = c_base + 16 * bb + 4 * (j & 3);
+  const int row = r0 + (j >> 2);
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(lds + Tile<bf16_t>::elem_offset(row, col)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(lds + Tile<bf16_t>::elem_offset(row + 4, col)));
+  Frag<bf16_t> f;
+  const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+  const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+  f.v = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_col(const char* lds, int r0, int c_base, float*) {
+  const int rho = threadIdx.x & 31;
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const float*>(lds + Tile<float>::elem_offset(r0 + e, c_base + rho));
+  Frag<float> f;
+  f.set(x);
+  return f;
 }
 
 }  // namespace gca

@@ -50,14 +50,15 @@ struct AttendParams {
   void* dk;
   void* dv;
   float* dscore;
-  float* delta;         // [G, B, H, Lq, K]  e_{t,k} = <dout_t, O_{t,k}>
+  float* delta;         // [G, B, H, n_q, K, 64]  e_{t,k} = <dout_t, O_{t,k}>
   float* dw_part;       // [G, B, n_q, H, K] per-head sums of e over a chunk's tokens
   float* wts;           // [G, B, n_q, K] fusion weights (0 on invalid slots)
-  int32_t* pairs;       // [B, cap] retrievals sorted by key chunk
-  int32_t* seg;         // [B, n_kv + 1] segment offsets into pairs
-  int64_t n_q, n_kv;
+  int32_t* pairs;       // [B, n_kv, pair_cap, 2] {(g, row, slot) code, fusion weight} per retrieval of
+                        // each key chunk, in (g, row, slot) order
+  int32_t* counts;      // [B, n_kv] list lengths
+  int64_t n_q, n_kv, q_base;
   int32_t G, B, H, K, shift;
-  int32_t pair_cap;     // G * n_q * K
+  int32_t pair_cap;     // G * n_q: most retrievals one key chunk can receive
   float attn_scale;
 };
 

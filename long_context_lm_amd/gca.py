@@ -181,13 +181,13 @@ def retrieve(cfg: Config, lq, lk, idx=None, score=None, ws=None):
 
 
 def forward(cfg: Config, q, k, v, idx, score, need_lse: bool = True, o=None, lse=None):
-    """gca_forward: returns (o [G,B,H,n_q*64,64], lse fp32 [G,B,H,n_q*64,K] or None)."""
+    """gca_forward: returns (o [G,B,H,n_q*64,64], lse fp32 [G,B,H,n_q,K,64] or None)."""
     import torch
 
     dev = q.device
     o = torch.empty_like(q) if o is None else o
     if need_lse and lse is None:
-        lse = torch.empty((cfg.G, cfg.B, cfg.H, cfg.n_q * 64, cfg.topk), dtype=torch.float32, device=dev)
+        lse = torch.empty((cfg.G, cfg.B, cfg.H, cfg.n_q, cfg.topk, 64), dtype=torch.float32, device=dev)
     prob = cfg.problem()
     _check("gca_forward", load().gca_forward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                              _ptr(score), _ptr(o), _ptr(lse) if need_lse else None,

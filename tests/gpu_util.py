@@ -48,8 +48,15 @@ def assert_close(name: str, got, ref, dtype: str):
     return err
 
 
+def lse_tokens(lse) -> np.ndarray:
+    """Library lse [G, B, H, n_q, K, 64] -> the oracle's token-major [G, B, H, n_q * 64, K]."""
+    a = lse.detach().cpu().numpy() if hasattr(lse, "detach") else np.asarray(lse)
+    G, B, H, nq, K, S = a.shape
+    return a.transpose(0, 1, 2, 3, 5, 4).reshape(G, B, H, nq * S, K)
+
+
 def lse_compare(name: str, got, ref, dtype: str):
-    got = np.asarray(got, dtype=np.float64)
+    got = lse_tokens(got).astype(np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     inf_g, inf_r = np.isneginf(got), np.isneginf(ref)
     assert np.array_equal(inf_g, inf_r), f"{name}: -inf pattern differs"

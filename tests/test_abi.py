@@ -18,6 +18,14 @@ OK, INVALID, UNSUPPORTED, WS_SMALL, MISALIGNED, HIP = range(6)
 FAKE = 0x100000  # never dereferenced: every call below fails validation first
 
 
+@pytest.fixture(autouse=True)
+def _no_launch_attempted():
+    """Every call here must fail validation (or be an empty problem) before any HIP call; on a
+    machine without a GPU an attempted launch would leave a HIP error behind."""
+    yield
+    assert gca.load().gca_last_hip_error() == 0, "a test call got past validation to a launch"
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -103,8 +111,8 @@ def test_workspace_sizes():
     # 16M-token history: 256 partial lists of 8 keys per row and group
     c = gca.Config(B=1, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
     assert gca.workspace_size(gca.OP_RETRIEVE, c) == 2 * 256 * 8 * 8 + 2 * 256 * 8 * 4
-    # too many retrievals per batch row for the inverse index
-    c = gca.Config(B=1, G=2, H=1, n_q=1024, n_kv=1024, topk=8)
+    # (group, row, slot) codes of the inverse index must fit in int32
+    c = gca.Config(B=1, G=4, H=1, n_q=1 << 26, n_kv=1024, topk=16)
     with pytest.raises(gca.GcaError):
         gca.workspace_size(gca.OP_BACKWARD, c)
 
@@ -130,8 +138,8 @@ def test_pointer_checks():
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z,
                             ctypes.c_void_p(FAKE + 16), need, None) == MISALIGNED
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, mis, z, z, z, need, None) == MISALIGNED
-    # backward beyond the inverse-index capacity
-    big = good(n_q_chunks=1025, n_kv_chunks=1025)  # G * n_q * K = 8200 > 8192
+    # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
+    big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED
 
 

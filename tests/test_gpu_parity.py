@@ -53,7 +53,7 @@ def _run_case(shape, dtype, scale=1.0, seed=0, need_bwd=True, **cfgkw):
     np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
     np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
     errs = {"o": assert_close("o", I.as_f64(o), r_o, dtype),
-            "lse": lse_compare("lse", lse.cpu().numpy(), r_lse, dtype)}
+            "lse": lse_compare("lse", lse, r_lse, dtype)}
     if need_bwd:
         for name, got, ref in zip(("dq", "dk", "dv", "dscore"), grads, r_grads):
             errs[name] = assert_close(name, I.as_f64(got), ref, dtype)
@@ -190,7 +190,7 @@ def test_determinism_and_causality_on_device():
     assert torch.equal(e[0][:, :, :c], a[0][:, :, :c])
     assert torch.equal(e[1][:, :, :c], a[1][:, :, :c])
     assert torch.equal(e[2][:, :, :, : 64 * (c + 1)], a[2][:, :, :, : 64 * (c + 1)])
-    assert torch.equal(e[3][:, :, :, : 64 * (c + 1)], a[3][:, :, :, : 64 * (c + 1)])
+    assert torch.equal(e[3][:, :, :, : c + 1], a[3][:, :, :, : c + 1])
 
 
 # ------------------------------------------------------------------ full training shape
@@ -224,7 +224,7 @@ def test_full_16k_training_step_sampled():
         ib, sb = r_idx[:, b:b + 1], r_sc[:, b:b + 1]
         r_o, r_lse = O.forward(x["q"], kb, vb, ib, sb, shift=1)
         assert_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o, "bf16")
-        lse_compare(f"lse[b={b}]", lse[:, b:b + 1].cpu().numpy(), r_lse, "bf16")
+        lse_compare(f"lse[b={b}]", lse[:, b:b + 1], r_lse, "bf16")
         r_dq, r_dk, r_dv, r_ds = O.backward(x["q"], kb, vb, ib, sb, x["dout"], shift=1)
         assert_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq, "bf16")
         for h in (0, 11):
