@@ -417,50 +417,46 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     const char* Ds = cur + TL::kBytes;
     const float* lse_v = reinterpret_cast<const float*>(cur + 2 * TL::kBytes);
     const float* del_v = lse_v + kChunk;
-    // S[q][u] and dP'[q][u] for the 64 queries (two tiles) and this wave's 32 keys
-    f32x16_t sacc[2], pacc[2];
+    // The two 32-query tiles are processed one after the other (dK, dV need no reduction over
+    // queries), which halves the live score registers.
+    const float lw = __builtin_amdgcn_logf(w);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      sacc[qt] = zero16();
-      pacc[qt] = zero16();
+      // S[q][u] and dP'[q][u] for the 32 queries of this tile and this wave's 32 keys
+      f32x16_t sacc = zero16(), pacc = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sacc[qt] = mma(row_frag<T>(Qs, 32 * qt + pi_row(li), 16 * s + 8 * hl), kf[s], sacc[qt]);
-        pacc[qt] = mma(row_frag<T>(Ds, 32 * qt + pi_row(li), 16 * s + 8 * hl), vf[s], pacc[qt]);
+        sacc = mma(row_frag<T>(Qs, 32 * qt + pi_row(li), 16 * s + 8 * hl), kf[s], sacc);
+        pacc = mma(row_frag<T>(Ds, 32 * qt + pi_row(li), 16 * s + 8 * hl), vf[s], pacc);
+      }
+      // lane holds queries 32 qt + 16 hl + r; P_w = w exp(z - lse), log2(w) folded in the bias
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int q0 = 32 * qt + 16 * hl + 8 * half;
+        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(lse_v + q0);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(lse_v + q0 + 4);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(del_v + q0);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(del_v + q0 + 4);
+        float xp[8], xz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          const float lse_q = e < 4 ? l0[e] : l1[e - 4];
+          const float del_q = e < 4 ? d0[e] : d1[e - 4];
+          const float pw = fast_exp2(__builtin_fmaf(sacc[r], c2, __builtin_fmaf(-lse_q, kLog2e, lw)));
+          xp[e] = pw;
+          xz[e] = pw * (pacc[r] - del_q);
+        }
+        Frag<T> pf, zf;
+        pf.set(xp);
+        zf.set(xz);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          dvacc[dt] = mma(col_frag<T>(Ds, q0, 32 * dt), pf, dvacc[dt]);
+          dkacc[dt] = mma(col_frag<T>(Qs, q0, 32 * dt), zf, dkacc[dt]);
+        }
       }
     }
-    // lane holds queries 32 qt + 16 hl + r; P_w = w exp(z - lse) with log2(w) folded in the bias
-    const float lw = __builtin_amdgcn_logf(w);
-    Frag<T> pf[4], zf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int qt = s >> 1;
-      const int q0 = 32 * qt + 16 * hl + 8 * (s & 1);
-      const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(lse_v + q0);
-      const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(lse_v + q0 + 4);
-      const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(del_v + q0);
-      const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(del_v + q0 + 4);
-      float xp[8], xz[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * (s & 1) + e;
-        const float lse_q = e < 4 ? l0[e] : l1[e - 4];
-        const float del_q = e < 4 ? d0[e] : d1[e - 4];
-        const float pw = fast_exp2(__builtin_fmaf(sacc[qt][r], c2, __builtin_fmaf(-lse_q, kLog2e, lw)));
-        xp[e] = pw;
-        xz[e] = pw * (pacc[qt][r] - del_q);
-      }
-      pf[s].set(xp);
-      zf[s].set(xz);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int r0 = 32 * (s >> 1) + 16 * hl + 8 * (s & 1);
-        dvacc[dt] = mma(col_frag<T>(Ds, r0, 32 * dt), pf[s], dvacc[dt]);
-        dkacc[dt] = mma(col_frag<T>(Qs, r0, 32 * dt), zf[s], dkacc[dt]);
-      }
     wait_async_copies();
     __syncthreads();
   };
@@ -494,61 +490,56 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
 // ------------------------------------------------------------- inverse retrieval index
 // For one batch row and 64 consecutive key chunks (lane = chunk j), list the retrievals that
 // selected each chunk as entries {(group, row, slot) code, fusion weight}, in (group, row) order.
-// Retrieval rows, flattened as gr = g * n_q + row, are handled in rounds of kIdxWords 32-row
-// words.  Each round copies the rows' idx values to LDS (coalesced), then: phase 1, wave w
-// builds for words w, w + 4, ... the per-lane bit mask of the rows naming its chunk (all lanes
-// read the same LDS word, a broadcast); phase 2, a running prefix of the masks' popcounts gives
-// every word its first output position; phase 3, each (chunk, word) writes its rows' entries
-// there.  Only rows that feed a query chunk (row + shift < n_q) and can hold a chunk of this
-// block (global chunk index q_base + row above the block's first chunk) are marked.  Runs after
-// the query-major pass, which writes the fusion weights.
+// Retrieval rows, flattened as gr = g * n_q + row, are handled kIdxRows at a time as 32-row
+// words.  Phase 1: one thread per row ORs the row's bit into the mask of every chunk of this
+// block the row names (integer OR: the result does not depend on the order).  Phase 2: a running
+// prefix of the masks' popcounts gives every (word, chunk) its first output position.  Phase 3:
+// each (chunk, word) writes its rows' entries there, in row order.  Only rows that feed a query
+// chunk (row + shift < n_q) and can hold a chunk of this block (global chunk index q_base + row
+// above the block's first chunk) are marked.  Runs after the query-major pass, which writes the
+// fusion weights.
 constexpr int kIdxThreads = 256;
-constexpr int kIdxWords = 32;
+constexpr int kIdxWords = 16;
+constexpr int kIdxRows = kIdxWords * 32;
 
 __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams p) {
-  __shared__ int32_t idx_s[kIdxWords * 32 * kMaxTopk];
+  __shared__ int32_t idx_s[kIdxRows][kMaxTopk];
+  __shared__ float wts_s[kIdxRows][kMaxTopk];
   __shared__ uint32_t mask[kIdxWords][64];
   __shared__ int32_t first[kIdxWords][64];
   __shared__ int32_t total[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nblk = (p.n_kv + 63) / 64;
+  const int32_t nblk = static_cast<int32_t>((p.n_kv + 63) / 64);
   const int b = static_cast<int>(blockIdx.x / nblk);
-  const int64_t j0 = (blockIdx.x % nblk) * 64;
-  const int64_t j = j0 + lane;
-  int64_t row_lo = j0 - p.q_base + 1;
-  if (row_lo < 0) row_lo = 0;
-  const int64_t row_hi = p.n_q - p.shift;
-  const int64_t n_rows = static_cast<int64_t>(p.G) * p.n_q;
-  const int64_t n_words = (n_rows + 31) / 32;
+  const int32_t j0 = static_cast<int32_t>(blockIdx.x % nblk) * 64;
+  const int32_t j = j0 + lane;
+  // chunk ids, row counts and (g, row) indices fit in int32 (checked on the host)
+  const int32_t nq = static_cast<int32_t>(p.n_q);
+  const int32_t row_lo = static_cast<int32_t>(j0 - p.q_base + 1 > 0 ? j0 - p.q_base + 1 : 0);
+  const int32_t row_hi = nq - p.shift;
+  const int32_t n_rows = p.G * nq;
   const int K = p.K;
   if (tid < 64) total[tid] = 0;
   i32x2_t* out = reinterpret_cast<i32x2_t*>(p.pairs) + (static_cast<int64_t>(b) * p.n_kv + j) * p.pair_cap;
 
-  for (int64_t w0 = 0; w0 < n_words; w0 += kIdxWords) {
-    const int nw = static_cast<int>(n_words - w0 < kIdxWords ? n_words - w0 : kIdxWords);
-    const int64_t gr0 = w0 * 32;
-    const int64_t nr = (gr0 + nw * 32 <= n_rows) ? nw * 32 : n_rows - gr0;
-    for (int64_t e = tid; e < nr * K; e += kIdxThreads) {
-      const int64_t gr = gr0 + e / K;
-      const int64_t row = gr % p.n_q;
-      const int g = static_cast<int>(gr / p.n_q);
-      idx_s[e] = p.idx[((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * K + e % K];
-    }
+  for (int32_t gr0 = 0; gr0 < n_rows; gr0 += kIdxRows) {
+    const int32_t nr = n_rows - gr0 < kIdxRows ? n_rows - gr0 : kIdxRows;
+    const int nw = (nr + 31) / 32;
+    for (int e = tid; e < kIdxWords * 64; e += kIdxThreads) mask[e / 64][e % 64] = 0u;
     __syncthreads();
-    // phase 1: masks
-    for (int wl = wave; wl < nw; wl += kIdxThreads / 64) {
-      uint32_t m = 0;
-      for (int bit = 0; bit < 32; ++bit) {
-        const int64_t lr = static_cast<int64_t>(wl) * 32 + bit;
-        if (lr >= nr) break;
-        const int64_t row = (gr0 + lr) % p.n_q;
-        if (row < row_lo || row >= row_hi) continue;
-        const int32_t* ir = idx_s + lr * K;
-        bool hit = false;
-        for (int k = 0; k < K; ++k) hit |= ir[k] == j;
-        m |= hit ? (1u << bit) : 0u;
+    // phase 1: one thread per row
+    for (int lr = tid; lr < nr; lr += kIdxThreads) {
+      const int32_t gr = gr0 + lr;
+      const int32_t g = gr / nq, row = gr - g * nq;
+      const int64_t rbase = ((static_cast<int64_t>(g) * p.B + b) * nq + row) * K;
+      const bool live = row >= row_lo && row < row_hi;
+      for (int k = 0; k < K; ++k) {
+        const int32_t jj = p.idx[rbase + k];
+        idx_s[lr][k] = jj;
+        wts_s[lr][k] = p.wts[rbase + k];
+        if (live && jj >= j0 && jj < j0 + 64 && jj < p.n_kv)
+          atomicOr(&mask[lr >> 5][jj - j0], 1u << (lr & 31));
       }
-      mask[wl][lane] = m;
     }
     __syncthreads();
     // phase 2: first output position of every word
@@ -569,14 +560,10 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
         while (m) {
           const int bit = __ffs(m) - 1;
           m &= m - 1;
-          const int64_t lr = static_cast<int64_t>(wl) * 32 + bit;
-          const int64_t gr = gr0 + lr;
+          const int lr = wl * 32 + bit;
           int k = 0;
-          while (idx_s[lr * K + k] != j) ++k;  // the first slot naming j; one exists (mask bit)
-          const int64_t row = gr % p.n_q;
-          const int g = static_cast<int>(gr / p.n_q);
-          const int64_t rbase = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * K;
-          out[pos++] = i32x2_t{static_cast<int32_t>(gr * K + k), __float_as_int(p.wts[rbase + k])};
+          while (idx_s[lr][k] != j) ++k;  // the first slot naming j; one exists (mask bit)
+          out[pos++] = i32x2_t{(gr0 + lr) * K + k, __float_as_int(wts_s[lr][k])};
         }
       }
     }

@@ -31,9 +31,12 @@ struct ProfState {
 };
 thread_local ProfState t_prof;
 
-constexpr int kRetrieveThreads = 256;
-constexpr int kRetrieveMinBlock = 1024;  // candidates per block before splitting a row
-constexpr int kRetrieveMaxBlocks = 256;  // partial lists per row merged by the second kernel
+// Retrieval: one wave scores a block of 64 * cpt candidates of one row.  Rows of at most 256
+// candidates take one block (cpt 4); longer rows are split into at most kRetrieveMaxBlocks
+// blocks of at least 1024 candidates, whose partial lists a second kernel merges.
+constexpr int64_t kRetrieveShortRow = 256;
+constexpr int64_t kRetrieveLongBlock = 1024;
+constexpr int64_t kRetrieveMaxBlocks = 256;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -95,15 +98,14 @@ struct RetrievePlan {
 };
 
 RetrievePlan plan_retrieve(const gca_problem* p) {
-  RetrievePlan r{1, 1, 0};
+  RetrievePlan r{1, 4, 0};
   if (p->n_q_chunks == 0) return r;
   const int64_t last_row = p->q_chunk_base + p->n_q_chunks - 1;
   const int64_t max_cand = last_row < p->n_kv_chunks ? last_row : p->n_kv_chunks;
-  int64_t nblk = (max_cand + kRetrieveMinBlock - 1) / kRetrieveMinBlock;
-  if (nblk < 1) nblk = 1;
+  if (max_cand <= kRetrieveShortRow) return r;
+  int64_t nblk = (max_cand + kRetrieveLongBlock - 1) / kRetrieveLongBlock;
   if (nblk > kRetrieveMaxBlocks) nblk = kRetrieveMaxBlocks;
-  int64_t cpt = (max_cand + kRetrieveThreads * nblk - 1) / (kRetrieveThreads * nblk);
-  if (cpt < 1) cpt = 1;
+  const int64_t cpt = (max_cand + 64 * nblk - 1) / (64 * nblk);
   r.nblk = static_cast<int32_t>(nblk);
   r.cpt = static_cast<int32_t>(cpt);
   if (nblk > 1) {

@@ -12,19 +12,16 @@
 // above the complement of j, so the largest key is the best score with the lowest j.  Key 0
 // never occurs for a finite score and marks an empty slot.
 //
-// One 256-thread workgroup scores one block of candidates of one row; each thread keeps its
-// own sorted top-K list, the block merges them with wave-wide max reductions.  Rows with more
-// candidates than one block covers are split over several blocks whose partial top-K lists a
-// second kernel merges (the 16M-token history: 262,144 candidates per row).
+// One wave scores one block of candidates of one row (cpt candidates per lane); each lane keeps
+// a sorted list of its best keys and the wave extracts the top K with K rounds of a wave-wide
+// maximum.  Rows with more candidates than one block are split over several waves whose partial
+// top-K lists a second kernel merges (the 16M-token history: 262,144 candidates per row).
 #include "gca_device.hpp"
 #include "gca_internal.hpp"
 
 namespace gca {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kList = kMaxTopk;  // per-thread list length (>= K)
 
 // --------------------------------------------------------------- Philox4x64-10 (SC'11)
 __device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
@@ -100,22 +97,23 @@ __device__ __forceinline__ int32_t key_index(uint64_t key) {
   return key == 0 ? -1 : static_cast<int32_t>(~static_cast<uint32_t>(key));
 }
 
-// --------------------------------------------------------------- per-thread sorted list
+// --------------------------------------------------------------- per-lane sorted list
+template <int KL>
 struct TopList {
-  uint64_t key[kList];
-  float s[kList];
+  uint64_t key[KL];
+  float s[KL];
   __device__ __forceinline__ void clear() {
 #pragma unroll
-    for (int e = 0; e < kList; ++e) {
+    for (int e = 0; e < KL; ++e) {
       key[e] = 0;
       s[e] = 0.f;
     }
   }
   // Insert keeping key[] descending; the smallest entry falls off the end.
   __device__ __forceinline__ void insert(uint64_t k, float sv) {
-    if (k <= key[kList - 1]) return;
+    if (k <= key[KL - 1]) return;
 #pragma unroll
-    for (int e = 0; e < kList; ++e) {
+    for (int e = 0; e < KL; ++e) {
       const bool take = k > key[e];
       const uint64_t tk = key[e];
       const float ts = s[e];
@@ -127,65 +125,66 @@ struct TopList {
   }
   __device__ __forceinline__ void pop() {
 #pragma unroll
-    for (int e = 0; e + 1 < kList; ++e) {
+    for (int e = 0; e + 1 < KL; ++e) {
       key[e] = key[e + 1];
       s[e] = s[e + 1];
     }
-    key[kList - 1] = 0;
+    key[KL - 1] = 0;
   }
 };
 
+// Wave-wide maximum of a 64-bit key, in every lane.  Within each 16-lane row the partners come
+// from DPP lane permutations (xor 1, xor 2, then the half-row and row mirrors, which act as xor 4
+// and xor 8 once the quads agree); across rows from v_permlane16_swap / v_permlane32_swap.  No
+// LDS traffic, so the K selection rounds are not bound by LDS latency.
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(v), kCtrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(v >> 32), kCtrl, 0xf, 0xf, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ uint64_t swap_max_u64(uint64_t v, bool rows16) {
+  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  auto l = rows16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto h = rows16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const uint64_t a = (static_cast<uint64_t>(h[0]) << 32) | l[0];
+  const uint64_t b = (static_cast<uint64_t>(h[1]) << 32) | l[1];
+  return max_u64(a, b);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+  v = swap_max_u64(v, true);          // rows 0<->1, 2<->3
+  v = swap_max_u64(v, false);         // halves
   return v;
 }
 
-// Block-wide top-K of the threads' lists.  Results land in out_key/out_s (LDS, K entries).
-__device__ void block_topk(TopList& L, int K, uint64_t* wave_key, float* wave_s, uint64_t* out_key,
-                           float* out_s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Top K of the wave's lists; lane k (< K) returns the k-th best key and its clean score.
+template <int KL>
+__device__ __forceinline__ void wave_topk(TopList<KL>& L, int K, uint64_t& my_key, float& my_s) {
+  const int lane = threadIdx.x & 63;
+  my_key = 0;
+  my_s = 0.f;
   for (int k = 0; k < K; ++k) {
     const uint64_t m = wave_max_u64(L.key[0]);
-    float sw = 0.f;
-    if (m != 0) {
-      const uint64_t hit = __ballot(L.key[0] == m);
-      const int owner = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      sw = __shfl(L.s[0], owner, 64);
-      if (lane == owner) L.pop();
-    }
-    if (lane == 0) {
-      wave_key[wave * kMaxTopk + k] = m;
-      wave_s[wave * kMaxTopk + k] = sw;
+    if (m == 0) break;  // wave-uniform
+    const uint64_t hit = __ballot(L.key[0] == m);
+    const int owner = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L.s[0]), owner));
+    if (lane == owner) L.pop();
+    if (lane == k) {
+      my_key = m;
+      my_s = sw;
     }
   }
-  __syncthreads();
-  if (wave == 0) {
-    uint64_t mine = 0;
-    float ms = 0.f;
-    if (lane < kWaves * K) {
-      mine = wave_key[(lane / K) * kMaxTopk + lane % K];
-      ms = wave_s[(lane / K) * kMaxTopk + lane % K];
-    }
-    for (int k = 0; k < K; ++k) {
-      const uint64_t m = wave_max_u64(mine);
-      float sw = 0.f;
-      if (m != 0) {
-        const uint64_t hit = __ballot(mine == m);
-        const int owner = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        sw = __shfl(ms, owner, 64);
-        if (lane == owner) mine = 0;
-      }
-      if (lane == 0) {
-        out_key[k] = m;
-        out_s[k] = sw;
-      }
-    }
-  }
-  __syncthreads();
 }
 
 __device__ __forceinline__ double lmk_to_f64(const bf16_t* p, int d) { return static_cast<double>(to_f32(p[d])); }
@@ -229,18 +228,18 @@ __device__ __forceinline__ double landmark_dot<float>(const float* __restrict__ 
   return acc;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) {
-  __shared__ double lq_s[kDim];
-  __shared__ uint64_t wave_key[kWaves * kMaxTopk];
-  __shared__ float wave_s[kWaves * kMaxTopk];
-  __shared__ uint64_t out_key[kMaxTopk];
-  __shared__ float out_s[kMaxTopk];
+constexpr int kThreads = 256;  // four waves, each an independent work item
 
-  const int tid = threadIdx.x;
-  const int64_t bid = blockIdx.x;
-  const int blk = static_cast<int>(bid % p.nblk);
-  const int64_t rowid = bid / p.nblk;  // (g * B + b) * n_q + r
+// One wave per (row, candidate block).
+template <typename T, int KL>
+__global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) {
+  __shared__ double lq_all[kThreads / 64][kDim];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave;
+  const int64_t n_items = static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk;
+  if (item >= n_items) return;  // whole wave; no workgroup barrier below
+  const int blk = static_cast<int>(item % p.nblk);
+  const int64_t rowid = item / p.nblk;  // (g * B + b) * n_q + r
   const int64_t r = rowid % p.n_q;
   const int64_t gb = rowid / p.n_q;
   const int b = static_cast<int>(gb % p.B);
@@ -248,16 +247,16 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) 
   const int64_t i = p.base + r;
   const int64_t ncand = i < p.n_kv ? i : p.n_kv;
 
-  const T* lq = static_cast<const T*>(p.lq) + rowid * kDim;
-  if (tid < kDim) lq_s[tid] = lmk_to_f64(lq, tid);
-  __syncthreads();
+  double* lq_s = lq_all[wave];
+  lq_s[lane] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, lane);
+  __builtin_amdgcn_wave_barrier();
 
-  TopList L;
+  TopList<KL> L;
   L.clear();
   const T* lk = static_cast<const T*>(p.lk) + gb * p.n_kv * kDim;
-  const int64_t j0 = static_cast<int64_t>(blk) * kThreads * p.cpt;
+  const int64_t j0 = static_cast<int64_t>(blk) * 64 * p.cpt;
   for (int n = 0; n < p.cpt; ++n) {
-    const int64_t j = j0 + static_cast<int64_t>(n) * kThreads + tid;
+    const int64_t j = j0 + static_cast<int64_t>(n) * 64 + lane;
     if (j >= ncand) break;
     const double acc = landmark_dot<T>(lk + j * kDim, lq_s);
     const float s = canon_zero(static_cast<float>(acc) * p.score_scale);
@@ -270,56 +269,63 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) 
     L.insert(make_key(rkey, j), s);
   }
 
-  block_topk(L, p.K, wave_key, wave_s, out_key, out_s);
-
-  if (tid < p.K) {
-    const uint64_t key = out_key[tid];
+  uint64_t key;
+  float sv;
+  wave_topk<KL>(L, p.K, key, sv);
+  if (lane < p.K) {
     if (p.nblk == 1) {
-      p.idx[rowid * p.K + tid] = key_index(key);
-      p.score[rowid * p.K + tid] = key == 0 ? -__builtin_inff() : out_s[tid];
+      p.idx[rowid * p.K + lane] = key_index(key);
+      p.score[rowid * p.K + lane] = key == 0 ? -__builtin_inff() : sv;
     } else {
-      const int64_t o = (rowid * p.nblk + blk) * p.K + tid;
+      const int64_t o = (rowid * p.nblk + blk) * p.K + lane;
       p.part_key[o] = key;
-      p.part_s[o] = out_s[tid];
+      p.part_s[o] = sv;
     }
   }
 }
 
+// One wave per row: merge the row's nblk partial top-K lists.
+template <int KL>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(RetrieveParams p) {
-  __shared__ uint64_t wave_key[kWaves * kMaxTopk];
-  __shared__ float wave_s[kWaves * kMaxTopk];
-  __shared__ uint64_t out_key[kMaxTopk];
-  __shared__ float out_s[kMaxTopk];
-  const int tid = threadIdx.x;
-  const int64_t rowid = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave;
+  if (rowid >= static_cast<int64_t>(p.G) * p.B * p.n_q) return;
   const int64_t n_in = static_cast<int64_t>(p.nblk) * p.K;
   const uint64_t* keys = p.part_key + rowid * n_in;
   const float* svals = p.part_s + rowid * n_in;
-  TopList L;
+  TopList<KL> L;
   L.clear();
-  for (int64_t c = tid; c < n_in; c += kThreads) L.insert(keys[c], svals[c]);
-  block_topk(L, p.K, wave_key, wave_s, out_key, out_s);
-  if (tid < p.K) {
-    const uint64_t key = out_key[tid];
-    p.idx[rowid * p.K + tid] = key_index(key);
-    p.score[rowid * p.K + tid] = key == 0 ? -__builtin_inff() : out_s[tid];
+  for (int64_t c = lane; c < n_in; c += 64) L.insert(keys[c], svals[c]);
+  uint64_t key;
+  float sv;
+  wave_topk<KL>(L, p.K, key, sv);
+  if (lane < p.K) {
+    p.idx[rowid * p.K + lane] = key_index(key);
+    p.score[rowid * p.K + lane] = key == 0 ? -__builtin_inff() : sv;
   }
 }
 
 }  // namespace
 
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk;
-  if (f32)
-    hipLaunchKernelGGL(score_topk_kernel<float>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(score_topk_kernel<bf16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
+  const int64_t items = static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk;
+  const dim3 grid(static_cast<uint32_t>((items + 3) / 4));
+  const bool small = p.K <= 8;
+  if (f32) {
+    if (small) hipLaunchKernelGGL((score_topk_kernel<float, 8>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((score_topk_kernel<float, 16>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (small) hipLaunchKernelGGL((score_topk_kernel<bf16_t, 8>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((score_topk_kernel<bf16_t, 16>), grid, dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(p.G) * p.B * p.n_q;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
+  const int64_t rows = static_cast<int64_t>(p.G) * p.B * p.n_q;
+  const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
+  if (p.K <= 8) hipLaunchKernelGGL((topk_merge_kernel<8>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((topk_merge_kernel<16>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
