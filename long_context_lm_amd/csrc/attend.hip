@@ -14,8 +14,10 @@
 //
 // Data movement.  The tiles a workgroup walks through (K/V of each retrieved chunk, or Q/dO of
 // each retrieving chunk) are copied global -> LDS with direct 16-byte-per-lane copies into a
-// row-major, XOR-swizzled layout, double-buffered: the copy of item n+1 is in flight while item
-// n is computed, and one barrier per item both publishes the new buffer and retires the old.
+// row-major, XOR-swizzled layout.  The backward passes double-buffer them (the copy of item n+1
+// is in flight while item n is computed; one barrier per item publishes the new buffer and
+// retires the old); the forward, whose registers allow four resident waves per SIMD, uses one
+// buffer and relies on the other resident workgroups to cover the copy latency.
 // Operands read along a tile row come from ds_read_b128; operands read down a tile column (V in
 // the forward, K in dQ, Q and dO in dK/dV) come from transposing LDS reads, so no tile is ever
 // stored transposed.
@@ -127,10 +129,10 @@ __device__ __forceinline__ Frag<T> col_frag(const char* tile, int r0, int c_base
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
   using TL = Tile<T>;
-  // Two buffers, each [K tile, V tile], as separate objects so that the compiler can tell the
-  // buffer being read from the one being filled and does not wait for the fill.
+  // One [K tile, V tile] buffer per workgroup: at 16 KiB of LDS and ~120 VGPRs, four waves per
+  // SIMD are resident, and the copy latency of one workgroup is covered by the others' compute
+  // (measured faster than double buffering, which halves the resident waves).
   __shared__ __align__(1024) char buf0[2 * TL::kBytes];
-  __shared__ __align__(1024) char buf1[2 * TL::kBytes];
   __shared__ SlotTable st;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -162,8 +164,7 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
-  auto body = [&](int n, const char* cur, char* nxt) {
-    if (n + 1 < nslots) fill(n + 1, nxt);
+  auto body = [&](int n, const char* cur) {
     const char* Ks = cur;
     const char* Vs = cur + TL::kBytes;
     f32x16_t sacc[2];
@@ -208,9 +209,13 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
     wait_async_copies();
     __syncthreads();
   };
-  for (int n = 0; n < nslots; n += 2) {
-    body(n, buf0, buf1);
-    if (n + 1 < nslots) body(n + 1, buf1, buf0);
+  for (int n = 0; n < nslots; ++n) {
+    if (n > 0) {
+      fill(n, buf0);
+      wait_async_copies();
+      __syncthreads();
+    }
+    body(n, buf0);
   }
 
   T* o = static_cast<T*>(p.o) + (qrow0 + my_q) * kDim;
