@@ -51,7 +51,7 @@ def training_step_setup(seed=0):
         "idx": torch.empty((G, B, nq, K), dtype=torch.int32, device="cuda"),
         "score": torch.empty((G, B, nq, K), dtype=torch.float32, device="cuda"),
         "o": torch.empty_like(dev["q"]),
-        "lse": torch.empty((G, B, H, nq * 64, K), dtype=torch.float32, device="cuda"),
+        "lse": torch.empty((G, B, H, nq, K, 64), dtype=torch.float32, device="cuda"),
         "dq": torch.empty_like(dev["q"]),
         "dk": torch.empty_like(dev["k"]),
         "dv": torch.empty_like(dev["v"]),
@@ -91,23 +91,39 @@ def kernel_figures(shape, idx_cpu):
         "bwd_query": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + G) * T + lse + sel, "tiles": tiles},
         # key-major backward: dK and dV per tile; reads Q, dO, K, V, LSE, writes dK, dV
         "bwd_key": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + 1 + 1) * T + lse, "tiles": tiles},
-        "csr_build": {"flops": 0, "bytes": sel // 2, "tiles": 0},
+        "inverse_index": {"flops": 0, "bytes": sel // 2, "tiles": 0},
         "score_grad": {"flops": 0, "bytes": sel, "tiles": 0},
     }
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken on the
+    current kernel sources (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings)."""
+    from long_context_lm_amd import profiling
+
+    path = os.path.join(ROOT, "profiles", "gca_train16k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != profiling.source_hash() or kernel not in t.get("kernels", {}):
+        return None
+    return t["kernels"][kernel]["hbm_bytes"]
 
 
 def roofline_for(name, fig, ms):
     t = ms * 1e-3
     t_mfma = fig["flops"] / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = fig["bytes"] / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(name)
     if t_mfma >= t_hbm:
         ach = fig["flops"] / t / 1e12
         return {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "algorithmic_flops": fig["flops"], "algorithmic_bytes": fig["bytes"], "avg_launch_ms": ms}
     ach = fig["bytes"] / t / 1e9
     return {"kernel": name, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": ach / PEAK_HBM_GBS, "traffic": None,
+            "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
             "algorithmic_flops": fig["flops"], "algorithmic_bytes": fig["bytes"], "avg_launch_ms": ms}
 
 
@@ -165,6 +181,13 @@ def inference_latency(shape, iters=50):
         one()
     torch.cuda.synchronize()
     res = {}
+    gca.profile_collect()
+    gca.profile_enable(True)
+    for _ in range(iters):
+        one()
+    torch.cuda.synchronize()
+    gca.profile_enable(False)
+    res["kernels_us"] = {k: v[0] / v[1] * 1e3 for k, v in gca.profile_collect().items()}
     for mode in ("warm", "cold"):
         times = []
         for _ in range(iters):
@@ -195,6 +218,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-inference", action="store_true", help="skip the 1M/16M-history latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -247,6 +272,14 @@ def main():
     for k, v in kernels.items():
         log(f"  {k:12s} {v['avg_ms'] * 1e3:9.1f} us  x{v['launches']}"
             + (f"  {v['bound']} {v['frac'] * 100:5.1f}%" if "frac" in v else ""))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

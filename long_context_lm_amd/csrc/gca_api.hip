@@ -12,7 +12,7 @@
 namespace gca {
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd", "csr_build",
+  static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd", "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
