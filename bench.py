@@ -188,14 +188,27 @@ def inference_latency(shape, iters=50):
     torch.cuda.synchronize()
     gca.profile_enable(False)
     res["kernels_us"] = {k: v[0] / v[1] * 1e3 for k, v in gca.profile_collect().items()}
-    for mode in ("warm", "cold"):
+    # the same step captured once in a HIP graph and replayed (a serving loop's launch pattern)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        one()
+    torch.cuda.synchronize()
+    for mode in ("warm", "cold", "graph_warm", "graph_cold"):
         times = []
         for _ in range(iters):
-            if mode == "cold":
+            if mode.endswith("cold"):
                 flush.zero_()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            one()
+            if mode.startswith("graph"):
+                graph.replay()
+            else:
+                one()
             b.record()
             b.synchronize()
             times.append(a.elapsed_time(b) * 1e3)
@@ -206,7 +219,7 @@ def inference_latency(shape, iters=50):
     gather = shape.G * shape.B * shape.topk * shape.H * 2 * 64 * 64 * 2
     res["hbm_bytes"] = lmk_bytes + gather
     res["hbm_bound_us"] = res["hbm_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
-    del k, v, flush
+    del k, v, flush, graph
     torch.cuda.empty_cache()
     return res
 
@@ -296,7 +309,8 @@ def main():
             log("inference latency", label)
             infer[label] = inference_latency(shp)
             log(f"  {label}: warm {infer[label]['warm']['median_us']:.1f} us, "
-                f"cold {infer[label]['cold']['median_us']:.1f} us")
+                f"cold {infer[label]['cold']['median_us']:.1f} us; graph replay warm "
+                f"{infer[label]['graph_warm']['median_us']:.1f} us, cold {infer[label]['graph_cold']['median_us']:.1f} us")
 
     out = {
         "metric": METRIC,

@@ -17,6 +17,7 @@
  *   - All tensors are dense, row-major (last index fastest), in device memory, owned by the
  *     caller.  The library never allocates, frees or synchronises, keeps no state between
  *     calls, and enqueues all work on `stream` (a hipStream_t; NULL = the null stream).
+ *     Calls that share a workspace must be ordered on one stream.
  *   - Floating tensors q, k, v, o, dout, dq, dk, dv, lq, lk use `problem->dtype`
  *     (bf16 or fp32).  idx is int32; score, lse and dscore are fp32.
  *   - Shapes (n_q = n_q_chunks, n_kv = n_kv_chunks, S = 64, d = d_head, dl = d_lmk):
@@ -107,7 +108,8 @@ gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes)
  *   the K candidates j < min(i, n_kv) with the largest r (ties toward lower j) are written to
  *   idx[g,b,r,:] in order (r descending, j ascending) with their clean s_ij in score[g,b,r,:];
  *   unused slots get idx = -1 and score = -inf.
- * lq, lk: inputs (see shapes).  idx, score: outputs.  ws: >= gca_workspace_size(RETRIEVE).
+ * lq, lk: inputs (see shapes).  idx, score: outputs.  ws: >= gca_workspace_size(RETRIEVE)
+ * (partial top-k lists of rows longer than one block of the scan; contents need no setup).
  */
 gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* lk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);

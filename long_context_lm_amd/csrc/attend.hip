@@ -40,6 +40,7 @@ namespace {
 constexpr int kThreads = 128;  // two waves
 constexpr int kWaves = 2;
 constexpr int kEntRound = 512;  // inverse-index entries staged in LDS at a time
+constexpr int64_t kWideMaxTiles = 256;  // query tiles up to which the forward runs one slot per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2f = 0.6931471805599453f;
 
@@ -225,6 +226,164 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
     for (int a = 0; a < 4; ++a)
       store4(o + 32 * dt + 8 * a + 4 * hl, oacc[dt][4 * a], oacc[dt][4 * a + 1], oacc[dt][4 * a + 2],
              oacc[dt][4 * a + 3]);
+}
+
+// ------------------------------------------------------------------ forward, few queries
+// A decode-style step (one query chunk against a long history) gives too few query tiles to
+// occupy the chip, and the main forward would walk its K slots one after another, paying the HBM
+// latency of each retrieved tile in turn.  Here one workgroup owns 32 queries (half a chunk) of one
+// (group, batch row, head, chunk) and each of its kW waves owns one slot (slots w, w + kW, ...):
+// every wave reads its slot's index and the row's scores itself, starts its own tile copies at
+// once, and computes alone on its LDS region; the waves' weighted partial outputs are summed in
+// wave order through LDS at the end (the same sum as the main forward, in another rounding order).
+template <typename T>
+struct Wide {
+  static constexpr int kW = sizeof(T) == 2 ? 8 : 4;  // waves; LDS holds one K and V tile per wave
+  static constexpr int kThreads = 64 * kW;
+};
+
+// Fusion weight of slot k of one retrieval row, computed by every lane of the wave (lanes < K
+// read the row's scores; the softmax over valid slots is reduced across the wave).
+__device__ __forceinline__ float wave_slot_weight(const AttendParams& p, int64_t rowbase, int lane, int k,
+                                                  bool& valid_k, int32_t& j_k, uint32_t& valid_mask) {
+  int32_t j = -1;
+  float sc = -__builtin_inff();
+  if (lane < p.K) {
+    j = p.idx[rowbase + lane];
+    sc = p.score[rowbase + lane];
+  }
+  const bool v = j >= 0 && j < p.n_kv;
+  valid_mask = static_cast<uint32_t>(__ballot(v));
+  float mx = v ? sc : -__builtin_inff();
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));  // K <= 16 lanes
+  const float e = v ? expf(sc - mx) : 0.f;
+  float sum = e;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 16);
+  valid_k = (valid_mask >> k) & 1u;
+  j_k = __shfl(j, k, 64);
+  return __shfl(e, k, 64) / __shfl(sum, 0, 64);  // lanes 0..15 hold the row
+}
+
+template <typename T>
+__global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(AttendParams p) {
+  using TL = Tile<T>;
+  constexpr int kW = Wide<T>::kW;
+  constexpr int kRegion = 2 * TL::kBytes;  // one wave's K and V tiles, later its fp32 partial output
+  static_assert(kRegion >= 32 * kDim * 4, "partial output must fit in a wave's region");
+  __shared__ __align__(1024) char buf[kW * kRegion];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hl = lane >> 5;
+  // block -> (query half, tile); the tile order is the main forward's
+  const int64_t lid = blockIdx.x;
+  const int half = static_cast<int>(lid & 1);
+  const int64_t tile = lid >> 1;
+  QTileCoord c;
+  c.t = tile % p.n_q;
+  int64_t rest = tile / p.n_q;
+  c.g = static_cast<int>(rest % p.G);
+  rest /= p.G;
+  c.h = static_cast<int>(rest % p.H);
+  c.b = static_cast<int>(rest / p.H);
+  c.gbh = (static_cast<int64_t>(c.g) * p.B + c.b) * p.H + c.h;
+  const int64_t Lq = p.n_q * kChunk;
+  const int64_t qrow0 = c.gbh * Lq + c.t * kChunk + 32 * half;
+  char* region = buf + wave * kRegion;
+
+  const int64_t row = c.t - p.shift;
+  const bool has_row = row >= 0;
+  const int64_t rowbase = ((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + (has_row ? row : 0)) * p.K;
+
+  Frag<T> qf[4];
+  const T* q = static_cast<const T*>(p.q) + (qrow0 + li) * kDim;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s].load(q + 16 * s + 8 * hl);
+
+  f32x16_t oacc[2] = {zero16(), zero16()};
+  const float c2 = p.attn_scale * kLog2e;
+  for (int k = wave; k < p.K; k += kW) {  // wave-uniform
+    bool valid = false;
+    int32_t j = -1;
+    uint32_t vmask = 0;
+    float w = 0.f;
+    if (has_row) w = wave_slot_weight(p, rowbase, lane, k, valid, j, vmask);
+    float* lse_k = p.lse ? p.lse + slot_vec_offset(p, c.gbh, c.t, k) + 32 * half : nullptr;
+    if (!valid) {
+      if (lse_k && lane < 32) lse_k[lane] = -__builtin_inff();
+      continue;
+    }
+    tile_load_async<T, 1>(kv_tile<T>(p.k, p, c.b, c.h, j), region, 0);
+    tile_load_async<T, 1>(kv_tile<T>(p.v, p, c.b, c.h, j), region + TL::kBytes, 0);
+    wait_async_copies();  // this wave's own copies: visible to it once they have landed
+    const char* Ks = region;
+    const char* Vs = region + TL::kBytes;
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sacc[tt] = mma(row_frag<T>(Ks, 32 * tt + pi_row(li), 16 * s + 8 * hl), qf[s], sacc[tt]);
+    }
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+    mx = xor32_max(mx);
+    const float bias = -mx * c2;
+    float l = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
+        sacc[tt][r] = e;
+        l += e;
+      }
+    l = xor32_sum(l);
+    if (lse_k && hl == 0) lse_k[li] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
+    const float f = w / l;
+    Frag<T> pf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = sacc[s >> 1][8 * (s & 1) + e] * f;
+      pf[s].set(x);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        oacc[dt] = mma(col_frag<T>(Vs, 32 * (s >> 1) + 16 * hl + 8 * (s & 1), 32 * dt), pf[s], oacc[dt]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // tile reads done before the next refill
+  }
+
+  // Partial output of this wave, fp32 [32 queries][64], 16-byte chunk ch of query row qq stored at
+  // chunk position ch ^ (qq & 15) (conflict-free for these writes and for the reads below).
+  __syncthreads();  // (every wave is past its tile reads)
+  float* part = reinterpret_cast<float*>(region);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ch = 8 * dt + 2 * a + hl;
+      *reinterpret_cast<f32x4_t*>(part + li * kDim + 4 * (ch ^ (li & 15))) =
+          f32x4_t{oacc[dt][4 * a], oacc[dt][4 * a + 1], oacc[dt][4 * a + 2], oacc[dt][4 * a + 3]};
+    }
+  __syncthreads();
+  T* o = static_cast<T*>(p.o) + qrow0 * kDim;
+  for (int e = tid; e < 32 * kDim / 4; e += Wide<T>::kThreads) {
+    const int qq = e >> 4, ch = e & 15;
+    const int off = qq * kDim + 4 * (ch ^ (qq & 15));
+    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(buf) + off);
+#pragma unroll
+    for (int w2 = 1; w2 < kW; ++w2) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(buf + w2 * kRegion) + off);
+      acc = f32x4_t{acc[0] + x[0], acc[1] + x[1], acc[2] + x[2], acc[3] + x[3]};
+    }
+    store4(o + qq * kDim + 4 * ch, acc[0], acc[1], acc[2], acc[3]);
+  }
 }
 
 // ------------------------------------------------------------- backward, query-major (dQ)
@@ -606,6 +765,15 @@ __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
 
 hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.G) * p.B * p.H * p.n_q;
+  if (blocks <= kWideMaxTiles) {  // too few query tiles to fill the chip: one slot per wave
+    if (f32)
+      hipLaunchKernelGGL(attend_fwd_wide_kernel<float>, dim3(static_cast<uint32_t>(2 * blocks)),
+                         dim3(Wide<float>::kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(attend_fwd_wide_kernel<bf16_t>, dim3(static_cast<uint32_t>(2 * blocks)),
+                         dim3(Wide<bf16_t>::kThreads), 0, s, p);
+    return hipGetLastError();
+  }
   if (f32)
     hipLaunchKernelGGL(attend_fwd_kernel<float>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
   else
@@ -613,7 +781,7 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_csr_build(const AttendParams& p, hipStream_t s) {
+hipError_t launch_inverse_index(const AttendParams& p, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.B) * ((p.n_kv + 63) / 64);
   hipLaunchKernelGGL(inverse_index_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kIdxThreads), 0, s, p);
   return hipGetLastError();

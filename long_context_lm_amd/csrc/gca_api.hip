@@ -31,12 +31,13 @@ struct ProfState {
 };
 thread_local ProfState t_prof;
 
-// Retrieval: one wave scores a block of 64 * cpt candidates of one row.  Rows of at most 256
-// candidates take one block (cpt 4); longer rows are split into at most kRetrieveMaxBlocks
-// blocks of at least 1024 candidates, whose partial lists a second kernel merges.
-constexpr int64_t kRetrieveShortRow = 256;
-constexpr int64_t kRetrieveLongBlock = 1024;
-constexpr int64_t kRetrieveMaxBlocks = 256;
+// Retrieval: one workgroup scores a block of 256 * cpt candidates of one row (one candidate per
+// lane per pass).  cpt starts at 1 and doubles while the grid would exceed kRetrieveMaxGroups
+// workgroups (four resident per CU) and a row still spans several blocks; rows spanning several
+// blocks are merged by a second kernel.  The 16M-token history (262,144 candidates per row, two
+// rows) runs as 1,024 workgroups of two candidates per lane, whose loads are all in flight at once.
+constexpr int64_t kRetrieveBlock = 256;
+constexpr int64_t kRetrieveMaxGroups = 1024;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -98,18 +99,21 @@ struct RetrievePlan {
 };
 
 RetrievePlan plan_retrieve(const gca_problem* p) {
-  RetrievePlan r{1, 4, 0};
+  RetrievePlan r{1, 1, 0};
   if (p->n_q_chunks == 0) return r;
   const int64_t last_row = p->q_chunk_base + p->n_q_chunks - 1;
   const int64_t max_cand = last_row < p->n_kv_chunks ? last_row : p->n_kv_chunks;
-  if (max_cand <= kRetrieveShortRow) return r;
-  int64_t nblk = (max_cand + kRetrieveLongBlock - 1) / kRetrieveLongBlock;
-  if (nblk > kRetrieveMaxBlocks) nblk = kRetrieveMaxBlocks;
-  const int64_t cpt = (max_cand + 64 * nblk - 1) / (64 * nblk);
+  const int64_t rows = static_cast<int64_t>(p->G) * p->B * p->n_q_chunks;
+  int64_t cpt = 1;
+  int64_t nblk = max_cand > 0 ? (max_cand + kRetrieveBlock - 1) / kRetrieveBlock : 1;
+  while (nblk > 1 && rows * nblk > kRetrieveMaxGroups) {
+    cpt *= 2;
+    nblk = (max_cand + kRetrieveBlock * cpt - 1) / (kRetrieveBlock * cpt);
+  }
   r.nblk = static_cast<int32_t>(nblk);
   r.cpt = static_cast<int32_t>(cpt);
   if (nblk > 1) {
-    const size_t n = static_cast<size_t>(p->G) * p->B * p->n_q_chunks * nblk * p->topk;
+    const size_t n = static_cast<size_t>(rows) * nblk * p->topk;
     r.ws = align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(float));
   }
   return r;
@@ -312,7 +316,7 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   // With no query chunk, only the inverse index (empty lists) and the key-major pass (which
   // writes zero dk, dv for chunks nobody retrieved) run.
   if (any) GCA_TRY(launch(kBwdQuery, s, [&] { return launch_bwd_query(a, f32, s); }));
-  if (kv) GCA_TRY(launch(kCsrBuild, s, [&] { return launch_csr_build(a, s); }));
+  if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
   if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
   return GCA_OK;

@@ -180,10 +180,10 @@ __device__ __forceinline__ void copy16_async(const void* gsrc, char* lds_wave_ba
 // Start copying one 64x64 tile (global row stride 64 elements) into swizzled LDS.  All threads of
 // a workgroup of kWaves waves call it; each wave issues its share of the 1 KiB wave copies.  The
 // data is usable after wait_async_copies() and a workgroup barrier.
+// `wave` is the caller's wave index within the kWaves waves that share the copy.
 template <typename T, int kWaves>
-__device__ __forceinline__ void tile_load_async(const T* __restrict__ g, char* lds) {
+__device__ __forceinline__ void tile_load_async(const T* __restrict__ g, char* lds, int wave) {
   using TL = Tile<T>;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const char* gb = reinterpret_cast<const char*>(g);
 #pragma unroll
@@ -196,6 +196,11 @@ __device__ __forceinline__ void tile_load_async(const T* __restrict__ g, char* l
     const uint32_t off = static_cast<uint32_t>(row * TL::kRowBytes + chunk * 16);
     copy16_async(gb + off, lds + blk * 1024);
   }
+}
+
+template <typename T, int kWaves>
+__device__ __forceinline__ void tile_load_async(const T* __restrict__ g, char* lds) {
+  tile_load_async<T, kWaves>(g, lds, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
 }
 
 __device__ __forceinline__ void wait_async_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -11,7 +11,7 @@ enum KernelId {
   kScoreTopk = 0,
   kTopkMerge,
   kAttendFwd,
-  kCsrBuild,
+  kInverseIndex,
   kBwdQuery,
   kBwdKey,
   kScoreGrad,
@@ -24,7 +24,7 @@ struct RetrieveParams {
   const void* lk;
   int32_t* idx;
   float* score;
-  uint64_t* part_key;   // [rows, nblk, K] partial keys (two-stage only)
+  uint64_t* part_key;   // [rows, nblk, K] partial keys (long rows only)
   float* part_s;        // [rows, nblk, K] partial clean scores
   int64_t n_q, base, n_kv;
   int32_t G, B, K;
@@ -66,7 +66,7 @@ struct AttendParams {
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s);
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s);
 hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s);
-hipError_t launch_csr_build(const AttendParams& p, hipStream_t s);
+hipError_t launch_inverse_index(const AttendParams& p, hipStream_t s);
 hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_score_grad(const AttendParams& p, hipStream_t s);

@@ -12,10 +12,11 @@
 // above the complement of j, so the largest key is the best score with the lowest j.  Key 0
 // never occurs for a finite score and marks an empty slot.
 //
-// One wave scores one block of candidates of one row (cpt candidates per lane); each lane keeps
-// a sorted list of its best keys and the wave extracts the top K with K rounds of a wave-wide
-// maximum.  Rows with more candidates than one block are split over several waves whose partial
-// top-K lists a second kernel merges (the 16M-token history: 262,144 candidates per row).
+// One workgroup scores one block of candidates of one row (cpt candidates per lane, 256 lanes);
+// each lane keeps a sorted list of its best keys, each wave extracts its top K with K rounds of a
+// wave-wide maximum, and the four wave lists are merged through LDS.  Rows with more candidates
+// than one block are split over several workgroups whose partial top-K lists a second kernel
+// merges (the 16M-token history: 262,144 candidates per row, 512 blocks of 512).
 #include "gca_device.hpp"
 #include "gca_internal.hpp"
 
@@ -133,55 +134,54 @@ struct TopList {
   }
 };
 
-// Wave-wide maximum of a 64-bit key, in every lane.  Within each 16-lane row the partners come
+// Wave-wide maximum of a 32-bit value, in every lane.  Within each 16-lane row the partners come
 // from DPP lane permutations (xor 1, xor 2, then the half-row and row mirrors, which act as xor 4
 // and xor 8 once the quads agree); across rows from v_permlane16_swap / v_permlane32_swap.  No
 // LDS traffic, so the K selection rounds are not bound by LDS latency.
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
+// (Every lane has a source lane under these permutations; the zero "old" value and bound_ctrl
+// let the compiler fold the move into the max as one v_max_u32_dpp.)
 template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(v), kCtrl, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(v >> 32), kCtrl, 0xf, 0xf, false);
-  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xf, 0xf, true));
 }
 
-__device__ __forceinline__ uint64_t swap_max_u64(uint64_t v, bool rows16) {
-  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  auto l = rows16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
-                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-  auto h = rows16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
-                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-  const uint64_t a = (static_cast<uint64_t>(h[0]) << 32) | l[0];
-  const uint64_t b = (static_cast<uint64_t>(h[1]) << 32) | l[1];
-  return max_u64(a, b);
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 0<->1, 2<->3
+  v = max(r[0], r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves
+  return max(h[0], h[1]);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
-  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
-  v = swap_max_u64(v, true);          // rows 0<->1, 2<->3
-  v = swap_max_u64(v, false);         // halves
-  return v;
-}
-
-// Top K of the wave's lists; lane k (< K) returns the k-th best key and its clean score.
+// Top K of the wave's lists; lane k (< K) returns the k-th best key and its clean score.  Each
+// round finds the largest head key: first the largest high (score) word, then, only if several
+// lanes share it, the largest low word (the lowest chunk index) among those lanes.  A finite score
+// never has a zero high word and a chunk index never a zero low word, so zero marks an empty list.
 template <int KL>
 __device__ __forceinline__ void wave_topk(TopList<KL>& L, int K, uint64_t& my_key, float& my_s) {
   const int lane = threadIdx.x & 63;
   my_key = 0;
   my_s = 0.f;
   for (int k = 0; k < K; ++k) {
-    const uint64_t m = wave_max_u64(L.key[0]);
-    if (m == 0) break;  // wave-uniform
-    const uint64_t hit = __ballot(L.key[0] == m);
+    const uint32_t hh = static_cast<uint32_t>(L.key[0] >> 32);
+    const uint32_t hl = static_cast<uint32_t>(L.key[0]);
+    const uint32_t mh = wave_max_u32(hh);
+    if (mh == 0) break;  // wave-uniform: every list is empty
+    const bool top = hh == mh;
+    uint64_t hit = __ballot(top);
+    if (__popcll(hit) > 1) {
+      const uint32_t ml = wave_max_u32(top ? hl : 0u);
+      hit = __ballot(top && hl == ml);
+    }
     const int owner = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    const uint32_t wl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hl), owner));
     const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L.s[0]), owner));
     if (lane == owner) L.pop();
     if (lane == k) {
-      my_key = m;
+      my_key = (static_cast<uint64_t>(mh) << 32) | wl;
       my_s = sw;
     }
   }
@@ -190,54 +190,96 @@ __device__ __forceinline__ void wave_topk(TopList<KL>& L, int K, uint64_t& my_ke
 __device__ __forceinline__ double lmk_to_f64(const bf16_t* p, int d) { return static_cast<double>(to_f32(p[d])); }
 __device__ __forceinline__ double lmk_to_f64(const float* p, int d) { return static_cast<double>(p[d]); }
 
-// Exact sequential float64 dot product of one key landmark row with the query row in LDS.
+// One key-landmark row held in registers, so that the next row's load can be in flight while
+// this one is scored.
 template <typename T>
-__device__ __forceinline__ double landmark_dot(const T* __restrict__ row, const double* lq_s);
+struct LmkRow;
 
 template <>
-__device__ __forceinline__ double landmark_dot<bf16_t>(const bf16_t* __restrict__ row, const double* lq_s) {
-  const u32x4_t* r4 = reinterpret_cast<const u32x4_t*>(row);
-  u32x4_t chunk[8];
+struct LmkRow<bf16_t> {
+  u32x4_t c[8];
+  __device__ __forceinline__ void load(const bf16_t* row) {
+    const u32x4_t* r4 = reinterpret_cast<const u32x4_t*>(row);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) chunk[c] = r4[c];
-  double acc = 0.0;
+    for (int k = 0; k < 8; ++k) c[k] = r4[k];
+  }
+  // Exact sequential float64 dot product with the query landmark in LDS.
+  __device__ __forceinline__ double dot(const double* lq_s) const {
+    double acc = 0.0;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+    for (int k = 0; k < 8; ++k) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t pair = chunk[c][w];
-      const double lo = static_cast<double>(__uint_as_float(pair << 16));
-      const double hi = static_cast<double>(__uint_as_float(pair & 0xffff0000u));
-      acc = __builtin_fma(lq_s[8 * c + 2 * w], lo, acc);
-      acc = __builtin_fma(lq_s[8 * c + 2 * w + 1], hi, acc);
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t pair = c[k][w];
+        const double lo = static_cast<double>(__uint_as_float(pair << 16));
+        const double hi = static_cast<double>(__uint_as_float(pair & 0xffff0000u));
+        acc = __builtin_fma(lq_s[8 * k + 2 * w], lo, acc);
+        acc = __builtin_fma(lq_s[8 * k + 2 * w + 1], hi, acc);
+      }
     }
+    return acc;
   }
-  return acc;
-}
+};
 
 template <>
-__device__ __forceinline__ double landmark_dot<float>(const float* __restrict__ row, const double* lq_s) {
-  const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(row);
-  double acc = 0.0;
+struct LmkRow<float> {
+  f32x4_t c[16];
+  __device__ __forceinline__ void load(const float* row) {
+    const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(row);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const f32x4_t x = r4[c];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) acc = __builtin_fma(lq_s[4 * c + w], static_cast<double>(x[w]), acc);
+    for (int k = 0; k < 16; ++k) c[k] = r4[k];
   }
-  return acc;
+  __device__ __forceinline__ double dot(const double* lq_s) const {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc = __builtin_fma(lq_s[4 * k + w], static_cast<double>(c[k][w]), acc);
+    return acc;
+  }
+};
+
+constexpr int kThreads = 256;            // four waves
+constexpr int kWaves = kThreads / 64;
+constexpr int kBlockCand = kThreads;     // candidates of one block per pass (one per lane)
+constexpr int kMergeThreads = 1024;      // sixteen waves per merged row
+constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeBatch = 8;           // partial entries each merge thread loads at once
+
+// Merge the K-best lists of `nw` waves (lane k < K of wave w holds entry k) through LDS; wave 0
+// returns the top K of the union, lane k holding entry k.  Every thread of the workgroup calls it.
+template <int KL>
+__device__ __forceinline__ void workgroup_topk(int nw, int K, uint64_t key, float sv, uint64_t* lkey, float* ls,
+                                               uint64_t& out_key, float& out_s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane < K) {
+    lkey[wave * K + lane] = key;
+    ls[wave * K + lane] = sv;
+  }
+  __syncthreads();
+  out_key = 0;
+  out_s = 0.f;
+  if (wave == 0) {
+    TopList<KL> L;
+    L.clear();
+    for (int e = lane; e < nw * K; e += 64)
+      if (lkey[e] != 0) L.insert(lkey[e], ls[e]);
+    wave_topk<KL>(L, K, out_key, out_s);
+  }
 }
 
-constexpr int kThreads = 256;  // four waves, each an independent work item
-
-// One wave per (row, candidate block).
+// One workgroup per (row, block of 256 * cpt candidates).  Lane c of the workgroup scores the
+// candidates j = block start + c + 256 n (n < cpt), so every pass of the four waves reads 256
+// consecutive key-landmark rows; the next row's load is issued before the current one is scored.
+// At most 128 VGPRs for bf16 landmarks and lists of 8 (four resident workgroups per CU, enough
+// loads in flight to stream a long history); fp32 rows and lists of 16 are larger and keep two.
 template <typename T, int KL>
-__global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) {
-  __shared__ double lq_all[kThreads / 64][kDim];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave;
-  const int64_t n_items = static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk;
-  if (item >= n_items) return;  // whole wave; no workgroup barrier below
+__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
+  __shared__ double lq_s[kDim];
+  __shared__ uint64_t lkey[kWaves * kMaxTopk];
+  __shared__ float ls[kWaves * kMaxTopk];
+  const int lane = threadIdx.x & 63;
+  const int64_t item = blockIdx.x;
   const int blk = static_cast<int>(item % p.nblk);
   const int64_t rowid = item / p.nblk;  // (g * B + b) * n_q + r
   const int64_t r = rowid % p.n_q;
@@ -247,18 +289,28 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) 
   const int64_t i = p.base + r;
   const int64_t ncand = i < p.n_kv ? i : p.n_kv;
 
-  double* lq_s = lq_all[wave];
-  lq_s[lane] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, lane);
-  __builtin_amdgcn_wave_barrier();
-
   TopList<KL> L;
   L.clear();
   const T* lk = static_cast<const T*>(p.lk) + gb * p.n_kv * kDim;
-  const int64_t j0 = static_cast<int64_t>(blk) * 64 * p.cpt;
-  for (int n = 0; n < p.cpt; ++n) {
-    const int64_t j = j0 + static_cast<int64_t>(n) * 64 + lane;
-    if (j >= ncand) break;
-    const double acc = landmark_dot<T>(lk + j * kDim, lq_s);
+  const int64_t jb = static_cast<int64_t>(blk) * kBlockCand * p.cpt + threadIdx.x;
+  int mine = 0;  // candidates of this lane
+  if (jb < ncand) {
+    const int64_t m = (ncand - jb + kBlockCand - 1) / kBlockCand;
+    mine = m < p.cpt ? static_cast<int>(m) : p.cpt;
+  }
+  LmkRow<T> cur, nxt;
+  if (mine > 0) cur.load(lk + jb * kDim);  // in flight while the query landmark is staged
+  if (threadIdx.x < kDim) lq_s[threadIdx.x] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, threadIdx.x);
+  __syncthreads();
+
+  for (int n = 0; n < mine; ++n) {
+    const int64_t j = jb + static_cast<int64_t>(n) * kBlockCand;
+    if (n + 1 < mine) nxt.load(lk + (j + kBlockCand) * kDim);
+    // an opaque zero offset keeps the query landmark in LDS (read per candidate) instead of in
+    // 128 registers hoisted out of the loop
+    int zero = 0;
+    asm volatile("" : "+v"(zero));
+    const double acc = cur.dot(lq_s + zero);
     const float s = canon_zero(static_cast<float>(acc) * p.score_scale);
     float rkey = s;
     if (p.use_gumbel) {
@@ -267,41 +319,60 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(RetrieveParams p) 
       rkey = canon_zero(s + noise);
     }
     L.insert(make_key(rkey, j), s);
+    cur = nxt;
   }
 
-  uint64_t key;
-  float sv;
+  uint64_t key, bkey;
+  float sv, bs;
   wave_topk<KL>(L, p.K, key, sv);
-  if (lane < p.K) {
-    if (p.nblk == 1) {
-      p.idx[rowid * p.K + lane] = key_index(key);
-      p.score[rowid * p.K + lane] = key == 0 ? -__builtin_inff() : sv;
-    } else {
-      const int64_t o = (rowid * p.nblk + blk) * p.K + lane;
-      p.part_key[o] = key;
-      p.part_s[o] = sv;
+  workgroup_topk<KL>(kWaves, p.K, key, sv, lkey, ls, bkey, bs);
+  if (p.nblk == 1) {
+    if (threadIdx.x < p.K) {
+      p.idx[rowid * p.K + lane] = key_index(bkey);
+      p.score[rowid * p.K + lane] = bkey == 0 ? -__builtin_inff() : bs;
     }
+    return;
+  }
+
+  if (threadIdx.x < p.K) {
+    const int64_t o = (rowid * p.nblk + blk) * p.K + lane;
+    p.part_key[o] = bkey;
+    p.part_s[o] = bs;
   }
 }
 
-// One wave per row: merge the row's nblk partial top-K lists.
+// One workgroup of sixteen waves per long row merges the row's nblk partial top-K lists; each
+// thread loads its share of the entries in batches whose loads are in flight together.
 template <int KL>
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(RetrieveParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave;
-  if (rowid >= static_cast<int64_t>(p.G) * p.B * p.n_q) return;
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(RetrieveParams p) {
+  __shared__ uint64_t lkey[kMergeWaves * kMaxTopk];
+  __shared__ float ls[kMergeWaves * kMaxTopk];
+  const int64_t rowid = blockIdx.x;
   const int64_t n_in = static_cast<int64_t>(p.nblk) * p.K;
   const uint64_t* keys = p.part_key + rowid * n_in;
   const float* svals = p.part_s + rowid * n_in;
   TopList<KL> L;
   L.clear();
-  for (int64_t c = lane; c < n_in; c += 64) L.insert(keys[c], svals[c]);
-  uint64_t key;
-  float sv;
+  for (int64_t c0 = threadIdx.x; c0 < n_in; c0 += static_cast<int64_t>(kMergeThreads) * kMergeBatch) {
+    uint64_t kb[kMergeBatch];
+    float sb[kMergeBatch];
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int64_t c = c0 + static_cast<int64_t>(e) * kMergeThreads;
+      kb[e] = c < n_in ? keys[c] : 0;
+      sb[e] = c < n_in ? svals[c] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e)
+      if (kb[e] != 0) L.insert(kb[e], sb[e]);
+  }
+  uint64_t key, bkey;
+  float sv, bs;
   wave_topk<KL>(L, p.K, key, sv);
-  if (lane < p.K) {
-    p.idx[rowid * p.K + lane] = key_index(key);
-    p.score[rowid * p.K + lane] = key == 0 ? -__builtin_inff() : sv;
+  workgroup_topk<KL>(kMergeWaves, p.K, key, sv, lkey, ls, bkey, bs);
+  if (threadIdx.x < p.K) {
+    p.idx[rowid * p.K + threadIdx.x] = key_index(bkey);
+    p.score[rowid * p.K + threadIdx.x] = bkey == 0 ? -__builtin_inff() : bs;
   }
 }
 
@@ -309,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(RetrieveParams p) 
 
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s) {
   const int64_t items = static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk;
-  const dim3 grid(static_cast<uint32_t>((items + 3) / 4));
+  const dim3 grid(static_cast<uint32_t>(items));
   const bool small = p.K <= 8;
   if (f32) {
     if (small) hipLaunchKernelGGL((score_topk_kernel<float, 8>), grid, dim3(kThreads), 0, s, p);
@@ -322,10 +393,9 @@ hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s) {
 }
 
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(p.G) * p.B * p.n_q;
-  const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
-  if (p.K <= 8) hipLaunchKernelGGL((topk_merge_kernel<8>), grid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((topk_merge_kernel<16>), grid, dim3(kThreads), 0, s, p);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.n_q));
+  if (p.K <= 8) hipLaunchKernelGGL((topk_merge_kernel<8>), grid, dim3(kMergeThreads), 0, s, p);
+  else hipLaunchKernelGGL((topk_merge_kernel<16>), grid, dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 

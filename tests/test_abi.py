@@ -108,9 +108,12 @@ def test_workspace_sizes():
     assert gca.workspace_size(gca.OP_FORWARD, c) == 0
     bw = gca.workspace_size(gca.OP_BACKWARD, c)
     assert bw >= 2 * 8 * 12 * 256 * 64 * 8 * 4  # per-(token, slot) e values
-    # 16M-token history: 256 partial lists of 8 keys per row and group
+    # 16M-token history: 512 blocks of 512 candidates per row and group, 8 partial keys each
     c = gca.Config(B=1, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
-    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 2 * 256 * 8 * 8 + 2 * 256 * 8 * 4
+    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 2 * 512 * 8 * 8 + 2 * 512 * 8 * 4
+    # more rows: blocks grow (cpt doubles) until the grid is at most 1024 workgroups
+    c = gca.Config(B=8, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
+    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 16 * 64 * 8 * 8 + 16 * 64 * 8 * 4
     # (group, row, slot) codes of the inverse index must fit in int32
     c = gca.Config(B=1, G=4, H=1, n_q=1 << 26, n_kv=1024, topk=16)
     with pytest.raises(gca.GcaError):

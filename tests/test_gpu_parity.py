@@ -62,14 +62,17 @@ def _run_case(shape, dtype, scale=1.0, seed=0, need_bwd=True, **cfgkw):
 
 
 # ------------------------------------------------------------------ small shapes, full check
+# The forward has two kernels: up to 256 query tiles (G*B*H*n_q) one workgroup per tile computes
+# the slots in parallel (decode-style steps); above that, one workgroup per tile walks its slots.
+# The cases below cover both, in both dtypes.
 def test_tiny_fp32_forward_backward():
-    """B=1, L=1024 (16 chunks), H=2, K=4, fp32, N(0,1) inputs, no Gumbel."""
+    """B=1, L=1024 (16 chunks), H=2, K=4, fp32, N(0,1) inputs, no Gumbel (32 query tiles)."""
     _run_case(I.TINY_FP32, "f32")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_small_gumbel_two_groups(dtype):
-    shape = I.Shape(B=2, G=2, H=3, n_q=21, n_kv=21, topk=8)
+    shape = I.Shape(B=2, G=2, H=4, n_q=21, n_kv=21, topk=8)  # 336 query tiles
     _run_case(shape, dtype, scale=0.125, use_gumbel=True, seed=5, tau=1.0)
 
 
@@ -148,12 +151,33 @@ def test_retrieval_gumbel_long_rows_two_stage():
     n_kv = 5000
     shape = I.Shape(B=1, G=2, H=1, n_q=3, n_kv=n_kv, topk=8, q_chunk_base=n_kv - 1, shift=0)
     host = I.make_inputs(shape, "bf16", seed=9, scale=0.125, names=("lq", "lk"))
-    for gumbel in (False, True):
+    # one workspace for every call (its contents need no setup)
+    ws = torch.empty(gca.workspace_size(gca.OP_RETRIEVE, config_for(shape, "bf16")), dtype=torch.uint8,
+                     device="cuda")
+    for gumbel in (False, True, False):
         cfg = config_for(shape, "bf16", use_gumbel=gumbel, seed=77)
-        idx, sc = gca.retrieve(cfg, host["lq"].cuda(), host["lk"].cuda())
+        idx, sc = gca.retrieve(cfg, host["lq"].cuda(), host["lk"].cuda(), ws=ws)
         torch.cuda.synchronize()
         r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8, use_gumbel=gumbel,
                                  seed=77, q_chunk_base=n_kv - 1, n_kv=n_kv)
+        np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+        np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+
+
+def test_retrieval_several_candidates_per_lane():
+    """Grids capped at 2048 workgroups: many rows with long histories give one block per row of
+    several candidates per lane (single stage); few rows with a very long history give several
+    candidates per lane in each of many blocks (two stages)."""
+    cases = [(I.Shape(B=2, G=2, H=1, n_q=600, n_kv=600, topk=8), True),   # 2400 rows, 4 per lane
+             (I.Shape(B=2, G=2, H=1, n_q=1, n_kv=300_000, topk=8, q_chunk_base=300_000, shift=0), False)]
+    for shape, gumbel in cases:
+        say("case", shape, "gumbel", gumbel)
+        host = I.make_inputs(shape, "bf16", seed=4, scale=0.125, names=("lq", "lk"))
+        cfg = config_for(shape, "bf16", use_gumbel=gumbel, seed=11)
+        idx, sc = gca.retrieve(cfg, host["lq"].cuda(), host["lk"].cuda())
+        torch.cuda.synchronize()
+        r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8, use_gumbel=gumbel, seed=11,
+                                 q_chunk_base=shape.q_chunk_base, n_kv=shape.n_kv)
         np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
         np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
 
@@ -191,6 +215,56 @@ def test_determinism_and_causality_on_device():
     assert torch.equal(e[1][:, :, :c], a[1][:, :, :c])
     assert torch.equal(e[2][:, :, :, : 64 * (c + 1)], a[2][:, :, :, : 64 * (c + 1)])
     assert torch.equal(e[3][:, :, :, : c + 1], a[3][:, :, :, : c + 1])
+
+
+@pytest.mark.parametrize("case", ["decode", "train"])
+def test_graph_replay_matches_eager(case):
+    """The step captured once in a HIP graph: each replay, with fresh inputs copied into the
+    captured buffers and eager work in between, equals the eager call bit for bit."""
+    if case == "decode":  # two-stage retrieval over 3000 chunks, few-query forward
+        shape = I.Shape(B=1, G=2, H=2, n_q=1, n_kv=3000, topk=8, q_chunk_base=3000, shift=0)
+        names, bwd = ("lq", "lk", "q", "k", "v"), False
+    else:
+        shape = I.Shape(B=2, G=2, H=2, n_q=9, n_kv=9, topk=4)
+        names, bwd = ("lq", "lk", "q", "k", "v", "dout"), True
+    cfg = config_for(shape, "bf16", use_gumbel=bwd, seed=6)
+    buf = upload(I.make_inputs(shape, "bf16", seed=20, scale=0.125, names=names))
+    nws = gca.workspace_size(gca.OP_RETRIEVE, cfg)
+    rws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    bws = torch.empty(max(gca.workspace_size(gca.OP_BACKWARD, cfg), 1), dtype=torch.uint8, device="cuda")
+
+    def step(out=None):
+        idx, sc = gca.retrieve(cfg, buf["lq"], buf["lk"], *(out[:2] if out else (None, None)), ws=rws)
+        o, lse = gca.forward(cfg, buf["q"], buf["k"], buf["v"], idx, sc, need_lse=bwd,
+                             o=out[2] if out else None, lse=out[3] if out and bwd else None)
+        res = [idx, sc, o] + ([lse] if bwd else [])
+        if bwd:
+            res += list(gca.backward(cfg, buf["q"], buf["k"], buf["v"], idx, sc, lse, buf["dout"], ws=bws,
+                                     out=out[4:] if out else None))
+        return res
+
+    outs = step()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(outs)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(outs)
+    for rep in range(3):
+        fresh = I.make_inputs(shape, "bf16", seed=100 + rep, scale=0.125, names=names)
+        for n in names:
+            buf[n].copy_(fresh[n])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        ref = step()  # eager, into fresh buffers
+        torch.cuda.synchronize()
+        for n, (x, y) in enumerate(zip(got, ref)):
+            assert torch.equal(x, y), f"replay {rep}: output {n} differs from the eager call"
+        say("replay", rep, "matches eager")
 
 
 # ------------------------------------------------------------------ full training shape
