@@ -127,16 +127,127 @@ __device__ __forceinline__ Frag<T> col_frag(const char* tile, int r0, int c_base
 }
 
 // ------------------------------------------------------------------------------ forward
-template <typename T>
+// Per-lane LDS offsets of the forward's operand reads and tile copies.  They do not change from
+// slot to slot, so they are computed once and pinned in registers (opaque to the compiler, which
+// would otherwise recompute the swizzles in every iteration of the slot loop).
+template <typename T, int kWaves>
+struct FwdOffsets {
+  // bf16: K row fragments [s] (rows 32..63 at +4096); transposing V reads [(s & 1), dt, lo/hi]
+  // (rows 32..63 at +4096); copy offsets of this lane's 16-byte pieces [n] of a tile.
+  static constexpr int kCopies = Tile<T>::kChunks / 64 / kWaves;
+  uint32_t k[4], v[8], cp[kCopies];
+
+  __device__ __forceinline__ void init(int wave) {
+    using TL = Tile<T>;
+    const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int n = 0; n < kCopies; ++n) {
+      const int pos = (n * kWaves + wave) * 64 + lane;
+      const int row = pos / TL::kChunksPerRow;
+      cp[n] = static_cast<uint32_t>(TL::chunk_offset(row, pos % TL::kChunksPerRow));
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) k[s] = static_cast<uint32_t>(TL::chunk_offset(pi_row(li), 2 * s + hl));
+      const int j = lane & 15, bb = (lane >> 4) & 1;
+#pragma unroll
+      for (int s1 = 0; s1 < 2; ++s1)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int row = 16 * hl + 8 * s1 + (j >> 2), col = 32 * dt + 16 * bb + 4 * (j & 3);
+          v[4 * s1 + 2 * dt] = static_cast<uint32_t>(TL::elem_offset(row, col));
+          v[4 * s1 + 2 * dt + 1] = static_cast<uint32_t>(TL::elem_offset(row + 4, col));
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(k[i]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i]));
+    }
+#pragma unroll
+    for (int n = 0; n < kCopies; ++n) asm volatile("" : "+v"(cp[n]));
+  }
+
+  // Copy one 64x64 tile (global row stride 64; `g` uniform) into swizzled LDS: kCopies vector
+  // memory operations per wave, untracked by the compiler (see copy16_async_untracked).
+  __device__ __forceinline__ void copy(const T* __restrict__ g, char* lds, int wave) const {
+#pragma unroll
+    for (int n = 0; n < kCopies; ++n) copy16_async_untracked(g, cp[n], lds + (n * kWaves + wave) * 1024);
+  }
+
+  __device__ __forceinline__ Frag<T> kfrag(const char* Ks, int tt, int s) const {
+    if constexpr (sizeof(T) == 2) {
+      Frag<T> f;
+      f.v = *reinterpret_cast<const u32x4_t*>(Ks + k[s] + 4096 * tt);
+      return f;
+    } else {
+      const int li = threadIdx.x & 31, hl = (threadIdx.x >> 5) & 1;
+      return frag_row(Ks, 32 * tt + pi_row(li), 16 * s + 8 * hl, static_cast<T*>(nullptr));
+    }
+  }
+
+  // V^T operand: rows 32 (s >> 1) + 16 hl + 8 (s & 1) .. +7 of columns 32 dt .. 32 dt + 31.
+  __device__ __forceinline__ Frag<T> vfrag(const char* Vs, int s, int dt) const {
+    if constexpr (sizeof(T) == 2) {
+      typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+      const char* base = Vs + 4096 * (s >> 1);
+      const int i = 4 * (s & 1) + 2 * dt;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + v[i]));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + v[i + 1]));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+      const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+      Frag<T> f;
+      f.v = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+      return f;
+    } else {
+      const int hl = (threadIdx.x >> 5) & 1;
+      return frag_col(Vs, 32 * (s >> 1) + 16 * hl + 8 * (s & 1), 32 * dt, static_cast<T*>(nullptr));
+    }
+  }
+};
+
+// Softmax of one 64-key tile held as S^T accumulators (16 keys per lane per 32-key half, the
+// other 32 keys in lane ^ 32): returns the row maximum; sacc becomes exp2((s - max) * c2) and l
+// their sum.
+__device__ __forceinline__ float tile_softmax(f32x16_t (&sacc)[2], float c2, float& l) {
+  float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[1][0], sacc[1][1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) {  // three-operand maxima
+    m0 = fmaxf(fmaxf(m0, sacc[0][r]), sacc[0][r + 1]);
+    m1 = fmaxf(fmaxf(m1, sacc[1][r]), sacc[1][r + 1]);
+  }
+  const float mx = xor32_max(fmaxf(m0, m1));
+  const float bias = -mx * c2;
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sacc[0][r] = fast_exp2(__builtin_fmaf(sacc[0][r], c2, bias));
+    sacc[1][r] = fast_exp2(__builtin_fmaf(sacc[1][r], c2, bias));
+    l0 += sacc[0][r];
+    l1 += sacc[1][r];
+  }
+  l = xor32_sum(l0 + l1);
+  return mx;
+}
+
+// Slot loop, software-pipelined over one K and one V buffer (16 KiB of LDS for bf16, so four
+// waves per SIMD stay resident): once every wave has read K(n) for the scores, K(n+1) is copied
+// in behind the softmax and P V of slot n; once every wave has read V(n), V(n+1) is copied in
+// behind the scores and softmax of slot n+1.  Each wave waits only for its own copies (counted
+// with vmcnt, in issue order) and a barrier then publishes them to the other wave.  kLse: the
+// log-sum-exp output is written (one store per slot, which the counts include).
+template <typename T, bool kLse>
 __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
   using TL = Tile<T>;
-  // One [K tile, V tile] buffer per workgroup: at 16 KiB of LDS and ~120 VGPRs, four waves per
-  // SIMD are resident, and the copy latency of one workgroup is covered by the others' compute
-  // (measured faster than double buffering, which halves the resident waves).
-  __shared__ __align__(1024) char buf0[2 * TL::kBytes];
+  using Off = FwdOffsets<T, kWaves>;
+  constexpr int kC = Off::kCopies;  // copies per wave per tile
+  // Separate arrays, so that the compiler's own tracking of LDS copies never makes a read of
+  // one buffer wait for the copy into the other.
+  __shared__ __align__(1024) char Ks[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
   __shared__ SlotTable st;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
   const QTileCoord c = query_tile_coord(p);
   const int64_t Lq = p.n_q * kChunk;
@@ -148,52 +259,41 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
   const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s].load(q + 16 * s + 8 * hl);
+  Off off;
+  off.init(wave);
   __syncthreads();
 
   const int nslots = st.n;
-  auto fill = [&](int n, char* buf) {
-    tile_load_async<T, kWaves>(kv_tile<T>(p.k, p, c.b, c.h, st.j[n]), buf);
-    tile_load_async<T, kWaves>(kv_tile<T>(p.v, p, c.b, c.h, st.j[n]), buf + TL::kBytes);
-  };
-  if (nslots > 0) fill(0, buf0);
-  if (p.lse) {  // invalid slots: -inf
+  float* const lse_q = kLse ? p.lse + slot_vec_offset(p, c.gbh, c.t, 0) + my_q : nullptr;
+  if (kLse) {  // invalid slots: -inf (before any copy, so the copy counts below stay exact)
     for (int e = tid; e < p.K * kChunk; e += kThreads)
       if (!((st.valid_mask >> (e / kChunk)) & 1u)) p.lse[slot_vec_offset(p, c.gbh, c.t, 0) + e] = -__builtin_inff();
   }
-  wait_async_copies();
-  __syncthreads();
+  auto chunk_of = [&](int n) { return __builtin_amdgcn_readfirstlane(st.j[n]); };  // uniform
+  if (nslots > 0) {
+    const int32_t j = chunk_of(0);
+    off.copy(kv_tile<T>(p.k, p, c.b, c.h, j), Ks, wave);
+    off.copy(kv_tile<T>(p.v, p, c.b, c.h, j), Vs, wave);
+    barrier_copies_landed<kC>();  // K(0) landed and visible; V(0) may still be in flight
+  }
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
-  auto body = [&](int n, const char* cur) {
-    const char* Ks = cur;
-    const char* Vs = cur + TL::kBytes;
+  for (int n = 0; n < nslots; ++n) {
+    const bool more = n + 1 < nslots;
     f32x16_t sacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       sacc[tt] = zero16();
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[tt] = mma(row_frag<T>(Ks, 32 * tt + pi_row(li), 16 * s + 8 * hl), qf[s], sacc[tt]);
+      for (int s = 0; s < 4; ++s) sacc[tt] = mma(off.kfrag(Ks, tt, s), qf[s], sacc[tt]);
     }
-    // softmax over the 64 keys of this chunk (32 in this lane, 32 in lane ^ 32)
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
-    mx = xor32_max(mx);
-    const float bias = -mx * c2;
-    float l = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
-        sacc[tt][r] = e;
-        l += e;
-      }
-    l = xor32_sum(l);
-    if (p.lse && hl == 0)
-      p.lse[slot_vec_offset(p, c.gbh, c.t, st.slot[n]) + my_q] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
-    const float f = st.w[n] / l;
+    barrier_lds_reads_done();  // every wave has read K(n)
+    if (more) off.copy(kv_tile<T>(p.k, p, c.b, c.h, chunk_of(n + 1)), Ks, wave);
+
+    float l;
+    const float mx = tile_softmax(sacc, c2, l);
+    const float f = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st.w[n]))) * __builtin_amdgcn_rcpf(l);
     Frag<T> pf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -202,21 +302,19 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
       for (int e = 0; e < 8; ++e) x[e] = sacc[s >> 1][8 * (s & 1) + e] * f;
       pf[s].set(x);
     }
+    if (more) barrier_copies_landed<kC>();  // V(n) landed and visible (K(n+1) may be in flight)
+    else barrier_copies_landed<0>();
+    if (kLse && hl == 0)
+      lse_q[__builtin_amdgcn_readfirstlane(st.slot[n]) * kChunk] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        oacc[dt] = mma(col_frag<T>(Vs, 32 * (s >> 1) + 16 * hl + 8 * (s & 1), 32 * dt), pf[s], oacc[dt]);
-    wait_async_copies();
-    __syncthreads();
-  };
-  for (int n = 0; n < nslots; ++n) {
-    if (n > 0) {
-      fill(n, buf0);
-      wait_async_copies();
-      __syncthreads();
+      for (int s = 0; s < 4; ++s) oacc[dt] = mma(off.vfrag(Vs, s, dt), pf[s], oacc[dt]);
+    if (more) {
+      barrier_lds_reads_done();  // every wave has read V(n)
+      off.copy(kv_tile<T>(p.v, p, c.b, c.h, chunk_of(n + 1)), Vs, wave);
+      barrier_copies_landed<kC + (kLse ? 1 : 0)>();  // K(n+1) landed (the lse store, V(n+1) may not)
     }
-    body(n, buf0);
   }
 
   T* o = static_cast<T*>(p.o) + (qrow0 + my_q) * kDim;
@@ -226,6 +324,162 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
     for (int a = 0; a < 4; ++a)
       store4(o + 32 * dt + 8 * a + 4 * hl, oacc[dt][4 * a], oacc[dt][4 * a + 1], oacc[dt][4 * a + 2],
              oacc[dt][4 * a + 3]);
+}
+
+// ------------------------------------------------------------ forward, one wave per tile (bf16)
+// One wave owns a whole 64-query tile: K and V fragments are read from LDS once per slot and
+// used for both 32-query halves (half the LDS reads of two waves sharing the tile), the two
+// halves give the wave independent MFMA and softmax work to interleave, and a single-wave
+// workgroup needs no barriers.  The slot list lives in registers (lane k < K holds slot k).  The
+// same one-buffer pipeline as above: K(next) is copied in once K(n) is in registers, V(next)
+// once V(n) is, each wait counted in vector memory operations (in issue order).
+struct WaveSlots {
+  int32_t j;        // lane k: chunk of slot k
+  float w;          // lane k: fusion weight of slot k (0 if invalid)
+  uint32_t valid;   // bit k: slot k valid
+};
+
+// Fusion weights of one retrieval row, as build_slot_table computes them (maximum over the
+// valid slots, exp, then the sum in slot order).
+__device__ __forceinline__ WaveSlots wave_slots(const AttendParams& p, int g, int b, int64_t row) {
+  const int lane = threadIdx.x & 63;
+  WaveSlots ws{-1, 0.f, 0u};
+  if (row < 0) return ws;
+  const int64_t base = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K;
+  float sc = -__builtin_inff();
+  if (lane < p.K) {
+    ws.j = p.idx[base + lane];
+    sc = p.score[base + lane];
+  }
+  const bool v = lane < p.K && ws.j >= 0 && ws.j < p.n_kv;
+  ws.valid = static_cast<uint32_t>(__ballot(v));
+  float mx = v ? sc : -__builtin_inff();
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+  mx = __shfl(mx, 0, 64);
+  const float e = v ? expf(sc - mx) : 0.f;
+  float sum = 0.f;
+  for (int k = 0; k < p.K; ++k)
+    if ((ws.valid >> k) & 1u) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), k));
+  ws.w = v ? e / sum : 0.f;
+  return ws;
+}
+
+template <bool kLse>
+__global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
+  using T = bf16_t;
+  using TL = Tile<T>;
+  using Off = FwdOffsets<T, 1>;
+  constexpr int kC = Off::kCopies;  // 8 copies per tile
+  __shared__ __align__(1024) char Ks[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+
+  const int lane = threadIdx.x, li = lane & 31, hl = lane >> 5;
+  const QTileCoord c = query_tile_coord(p);
+  const int64_t Lq = p.n_q * kChunk;
+  const int64_t qrow0 = c.gbh * Lq + c.t * kChunk;
+
+  const WaveSlots sl = wave_slots(p, c.g, c.b, c.t - p.shift);
+  Frag<T> qf[2][4];
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const T* q = static_cast<const T*>(p.q) + (qrow0 + 32 * qh + li) * kDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qh][s].load(q + 16 * s + 8 * hl);
+  }
+  Off off;
+  off.init(0);
+
+  // lane (li, hl) writes the lse of query 32 hl + li
+  float* const lse_q = kLse ? p.lse + slot_vec_offset(p, c.gbh, c.t, 0) + lane : nullptr;
+  if (kLse) {  // invalid slots: -inf (before any copy, so the copy counts below stay exact)
+    for (int k = 0; k < p.K; ++k)
+      if (!((sl.valid >> k) & 1u)) lse_q[k * kChunk] = -__builtin_inff();
+  }
+  uint32_t rem = sl.valid;
+  int k = rem ? __builtin_ctz(rem) : -1;
+  rem &= rem - 1;
+  auto tile_of = [&](const void* base, int slot) {
+    return kv_tile<T>(base, p, c.b, c.h, __builtin_amdgcn_readlane(sl.j, slot));
+  };
+  if (k >= 0) {
+    off.copy(tile_of(p.k, k), Ks, 0);
+    off.copy(tile_of(p.v, k), Vs, 0);
+  }
+
+  f32x16_t oacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+  const float c2 = p.attn_scale * kLog2e;
+  bool first = true;
+  while (k >= 0) {  // wave-uniform
+    const int kn = rem ? __builtin_ctz(rem) : -1;
+    rem &= rem - 1;
+    if (first) wait_vm_outstanding<kC>();  // K(k) landed: only V(k) may be in flight
+    else wait_vm_outstanding<kC + (kLse ? 1 : 0)>();  // only the last lse store and V(k)
+    first = false;
+    Frag<T> kf[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[tt][s] = off.kfrag(Ks, tt, s);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K(k) in registers: the buffer is free
+    if (kn >= 0) off.copy(tile_of(p.k, kn), Ks, 0);
+
+    f32x16_t sacc[2][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sacc[qh][tt] = zero16();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[qh][tt] = mma(kf[tt][s], qf[qh][s], sacc[qh][tt]);
+      }
+    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sl.w), k));
+    float lse_v[2];
+    Frag<T> pf[2][4];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float l;
+      const float mx = tile_softmax(sacc[qh], c2, l);
+      lse_v[qh] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
+      const float f = wk * __builtin_amdgcn_rcpf(l);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sacc[qh][s >> 1][8 * (s & 1) + e] * f;
+        pf[qh][s].set(x);
+      }
+    }
+    if (kLse) lse_q[k * kChunk] = hl ? lse_v[1] : lse_v[0];
+
+    if (kn >= 0) wait_vm_outstanding<kC + (kLse ? 1 : 0)>();  // V(k) landed: K(kn), lse may not
+    else wait_vm_outstanding<kLse ? 1 : 0>();
+    Frag<T> vf[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) vf[s][dt] = off.vfrag(Vs, s, dt);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V(k) in registers: the buffer is free
+    if (kn >= 0) off.copy(tile_of(p.v, kn), Vs, 0);
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) oacc[qh][dt] = mma(vf[s][dt], pf[qh][s], oacc[qh][dt]);
+    k = kn;
+  }
+
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    T* o = static_cast<T*>(p.o) + (qrow0 + 32 * qh + li) * kDim;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        store4(o + 32 * dt + 8 * a + 4 * hl, oacc[qh][dt][4 * a], oacc[qh][dt][4 * a + 1],
+               oacc[qh][dt][4 * a + 2], oacc[qh][dt][4 * a + 3]);
+  }
 }
 
 // ------------------------------------------------------------------ forward, few queries
@@ -774,10 +1028,14 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
                          dim3(Wide<bf16_t>::kThreads), 0, s, p);
     return hipGetLastError();
   }
-  if (f32)
-    hipLaunchKernelGGL(attend_fwd_kernel<float>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(attend_fwd_kernel<bf16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (f32) {
+    if (p.lse) hipLaunchKernelGGL((attend_fwd_kernel<float, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attend_fwd_kernel<float, false>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (p.lse) hipLaunchKernelGGL((attend_fwd_wave_kernel<true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((attend_fwd_wave_kernel<false>), grid, dim3(64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

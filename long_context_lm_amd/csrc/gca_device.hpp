@@ -177,6 +177,15 @@ __device__ __forceinline__ void copy16_async(const void* gsrc, char* lds_wave_ba
   __builtin_amdgcn_global_load_lds((gbl_void_t*)(gsrc), (lds_void_t*)(lds_wave_base), 16, 0, 0);
 }
 
+// The same copy issued from inline assembly: the compiler does not see it as a write to LDS, so
+// it never makes later LDS reads wait for it.  The caller must order every read of the target
+// after the copy itself (wait_vm_outstanding / barrier_copies_landed, then a barrier).  Extra
+// vector memory operations the compiler does not count only make its own waits stricter.
+__device__ __forceinline__ void copy16_async_untracked(const void* gbase, uint32_t lane_off, char* lds_wave_base) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(lds_wave_base)));
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(gbase), "{m0}"(lds_addr) : "memory");
+}
+
 // Start copying one 64x64 tile (global row stride 64 elements) into swizzled LDS.  All threads of
 // a workgroup of kWaves waves call it; each wave issues its share of the 1 KiB wave copies.  The
 // data is usable after wait_async_copies() and a workgroup barrier.
@@ -204,6 +213,28 @@ __device__ __forceinline__ void tile_load_async(const T* __restrict__ g, char* l
 }
 
 __device__ __forceinline__ void wait_async_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N of this wave's vector memory operations are outstanding.  On gfx950 they
+// retire in issue order (loads, stores and LDS copies alike), so this waits for everything
+// issued before the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vm_outstanding() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barriers without the memory fence of __syncthreads() (which waits for every
+// outstanding global access, in-flight prefetch copies included).  Each wave first waits for what
+// the other waves rely on: its LDS reads of a buffer about to be refilled, or its own copies
+// into a buffer about to be read (all but the N most recent vector memory operations).
+__device__ __forceinline__ void barrier_lds_reads_done() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void barrier_copies_landed() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // MFMA operand holding 8 consecutive columns of one tile row: lane gets X[row][col0 .. col0+7].
 __device__ __forceinline__ Frag<bf16_t> frag_row(const char* lds, int row, int col0, bf16_t*) {
