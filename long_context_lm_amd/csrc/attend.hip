@@ -31,6 +31,8 @@
 // inverse index lists, per (batch row, key chunk), the (group, row, slot) retrievals that
 // selected it in a fixed order; one workgroup per (batch row, head, key chunk) walks that list
 // and accumulates in registers.  d(score) sums the per-head partials in a fixed order.
+#include <type_traits>
+
 #include "gca_device.hpp"
 #include "gca_internal.hpp"
 
@@ -127,11 +129,13 @@ __device__ __forceinline__ Frag<T> col_frag(const char* tile, int r0, int c_base
 }
 
 // ------------------------------------------------------------------------------ forward
-// Per-lane LDS offsets of the forward's operand reads and tile copies.  They do not change from
-// slot to slot, so they are computed once and pinned in registers (opaque to the compiler, which
-// would otherwise recompute the swizzles in every iteration of the slot loop).
+// Per-lane LDS offsets of the MFMA operand reads and tile copies.  They do not change from slot
+// to slot, so they are computed once and pinned in registers (opaque to the compiler, which would
+// otherwise recompute the swizzles in every iteration of the slot loops).  kfrag reads an operand
+// along tile rows (rows pi(l % 32), as S^T = X Q^T wants them); vfrag reads one down tile columns
+// with the transposing LDS read (X^T as the A operand of O^T = X^T P^T).
 template <typename T, int kWaves>
-struct FwdOffsets {
+struct TileOffsets {
   // bf16: K row fragments [s] (rows 32..63 at +4096); transposing V reads [(s & 1), dt, lo/hi]
   // (rows 32..63 at +4096); copy offsets of this lane's 16-byte pieces [n] of a tile.
   static constexpr int kCopies = Tile<T>::kChunks / 64 / kWaves;
@@ -238,7 +242,7 @@ __device__ __forceinline__ float tile_softmax(f32x16_t (&sacc)[2], float c2, flo
 template <typename T, bool kLse>
 __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
   using TL = Tile<T>;
-  using Off = FwdOffsets<T, kWaves>;
+  using Off = TileOffsets<T, kWaves>;
   constexpr int kC = Off::kCopies;  // copies per wave per tile
   // Separate arrays, so that the compiler's own tracking of LDS copies never makes a read of
   // one buffer wait for the copy into the other.
@@ -369,7 +373,7 @@ template <bool kLse>
 __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
   using T = bf16_t;
   using TL = Tile<T>;
-  using Off = FwdOffsets<T, 1>;
+  using Off = TileOffsets<T, 1>;
   constexpr int kC = Off::kCopies;  // 8 copies per tile
   __shared__ __align__(1024) char Ks[TL::kBytes];
   __shared__ __align__(1024) char Vs[TL::kBytes];
@@ -641,15 +645,37 @@ __global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(Atte
 }
 
 // ------------------------------------------------------------- backward, query-major (dQ)
+// Sum over the 32 queries of a wave of a per-query value (lanes l and l ^ 32 hold the same
+// query): DPP steps within each 16-lane row, then the row pair.  Fixed order: deterministic.
+__device__ __forceinline__ float sum_queries32(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, true));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One workgroup of two waves per query tile walks the tile's slots.  Per slot: S = K Q^T and
+// dP' = V dO^T from row reads, P = exp(z - lse), e = sum_u P dP', dz = P (w dP' - w e), and
+// dQ^T += K^T dz^T from transposing reads of the same K tile.  K is double-buffered (the next
+// slot's K copy starts with the slot); V is read only at the start of a slot, so the next V is
+// copied into the single V buffer as soon as both waves have read it.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
   using TL = Tile<T>;
-  __shared__ __align__(1024) char buf0[2 * TL::kBytes];  // [K tile, V tile]
-  __shared__ __align__(1024) char buf1[2 * TL::kBytes];
+  using Off = TileOffsets<T, kWaves>;
+  __shared__ __align__(1024) char Ka[TL::kBytes];
+  __shared__ __align__(1024) char Kb[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
   __shared__ float dw_s[2][kMaxTopk];
   __shared__ SlotTable st;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
   const QTileCoord c = query_tile_coord(p);
   const int64_t Lq = p.n_q * kChunk;
@@ -667,29 +693,39 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     qf[s].load(q + 16 * s + 8 * hl);
     df[s].load(dout + 16 * s + 8 * hl);
   }
+  Off off;
+  off.init(wave);
   __syncthreads();
 
   const int nslots = st.n;
-  float lse_next = 0.f;
-  auto fill = [&](int n, char* buf) {
-    tile_load_async<T, kWaves>(kv_tile<T>(p.k, p, c.b, c.h, st.j[n]), buf);
-    tile_load_async<T, kWaves>(kv_tile<T>(p.v, p, c.b, c.h, st.j[n]), buf + TL::kBytes);
-    lse_next = p.lse_in[slot_vec_offset(p, c.gbh, c.t, st.slot[n]) + my_q];
-  };
-  if (nslots > 0) fill(0, buf0);
   if (c.h == 0 && row >= 0 && tid < p.K)
     p.wts[((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.K + tid] = st.w_all[tid];
-  wait_async_copies();
-  __syncthreads();
+  const float* lse_q = p.lse_in + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
+  f32x2_t* delta_q = reinterpret_cast<f32x2_t*>(p.delta) + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
+  auto chunk_of = [&](int n) { return __builtin_amdgcn_readfirstlane(st.j[n]); };
+  auto slot_of = [&](int n) { return __builtin_amdgcn_readfirstlane(st.slot[n]); };
+  float lse_cur = 0.f;
+  if (nslots > 0) {
+    const int32_t j = chunk_of(0);
+    off.copy(kv_tile<T>(p.k, p, c.b, c.h, j), Ka, wave);
+    off.copy(kv_tile<T>(p.v, p, c.b, c.h, j), Vs, wave);
+    lse_cur = lse_q[slot_of(0) * kChunk];
+    barrier_copies_landed<0>();
+  }
 
   f32x16_t dqacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
-  auto body = [&](int n, const char* cur, char* nxt) {
-    const int slot = st.slot[n];
-    const float lse_b = lse_next * kLog2e;
-    if (n + 1 < nslots) fill(n + 1, nxt);
-    const char* Ks = cur;
-    const char* Vs = cur + TL::kBytes;
+  for (int n = 0; n < nslots; ++n) {
+    const bool more = n + 1 < nslots;
+    char* const Kc = (n & 1) ? Kb : Ka;
+    char* const Kn = (n & 1) ? Ka : Kb;
+    const int slot = slot_of(n);
+    const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st.w[n])));
+    float lse_nxt = 0.f;
+    if (more) {  // the other K buffer was released by the previous slot's closing barrier
+      off.copy(kv_tile<T>(p.k, p, c.b, c.h, chunk_of(n + 1)), Kn, wave);
+      lse_nxt = lse_q[slot_of(n + 1) * kChunk];
+    }
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -697,29 +733,30 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
       pacc[tt] = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sacc[tt] = mma(row_frag<T>(Ks, 32 * tt + pi_row(li), 16 * s + 8 * hl), qf[s], sacc[tt]);
-        pacc[tt] = mma(row_frag<T>(Vs, 32 * tt + pi_row(li), 16 * s + 8 * hl), df[s], pacc[tt]);
+        sacc[tt] = mma(off.kfrag(Kc, tt, s), qf[s], sacc[tt]);
+        pacc[tt] = mma(off.kfrag(Vs, tt, s), df[s], pacc[tt]);
       }
     }
-    // P_w = w exp(z - lse) (log2 w folded into the bias); e = sum_u P dP' = (sum_u P_w dP') / w
-    const float w = st.w[n];
-    const float bias = __builtin_amdgcn_logf(w) - lse_b;
-    float ew = 0.f;
+    barrier_lds_reads_done();  // every wave has read V(n)
+    if (more) off.copy(kv_tile<T>(p.v, p, c.b, c.h, chunk_of(n + 1)), Vs, wave);
+
+    // P = exp(z - lse); e = sum_u P dP' = <dO, O_slot>; dz = w P (dP' - e)
+    const float bias = -lse_cur * kLog2e;
+    float e = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
         sacc[tt][r] = pr;
-        ew = __builtin_fmaf(pr, pacc[tt][r], ew);
+        e = __builtin_fmaf(pr, pacc[tt][r], e);
       }
-    ew = xor32_sum(ew);
-    const float e = w > 0.f ? ew / w : 0.f;  // w underflows to 0 only if P_w (and dz) is 0 anyway
-    if (hl == 0) p.delta[slot_vec_offset(p, c.gbh, c.t, slot) + my_q] = e;
-    float es = e;  // per-wave sum of e over its 32 queries, fixed butterfly order
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) es += __shfl_xor(es, off, 64);
+    e = xor32_sum(e);
+    // for the key-major pass: P_w = exp2(z log2e + bias) with bias = log2 w - lse log2 e, and e
+    if (hl == 0) delta_q[slot * kChunk] = f32x2_t{__builtin_amdgcn_logf(w) + bias, e};
+    const float es = sum_queries32(e);
     if (lane == 0) dw_s[wave][slot] = es;
+    const float we = -w * e;
     Frag<T> zf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -727,21 +764,18 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 #pragma unroll
       for (int ee = 0; ee < 8; ++ee) {
         const int tt = s >> 1, r = 8 * (s & 1) + ee;
-        x[ee] = sacc[tt][r] * (pacc[tt][r] - e);
+        x[ee] = sacc[tt][r] * __builtin_fmaf(w, pacc[tt][r], we);
       }
       zf[s].set(x);
     }
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dqacc[dt] = mma(col_frag<T>(Ks, 32 * (s >> 1) + 16 * hl + 8 * (s & 1), 32 * dt), zf[s], dqacc[dt]);
-    wait_async_copies();
-    __syncthreads();
-  };
-  for (int n = 0; n < nslots; n += 2) {
-    body(n, buf0, buf1);
-    if (n + 1 < nslots) body(n + 1, buf1, buf0);
+      for (int s = 0; s < 4; ++s) dqacc[dt] = mma(off.vfrag(Kc, s, dt), zf[s], dqacc[dt]);
+    lse_cur = lse_nxt;
+    // K(n+1), the lse and V(n+1) landed (the delta store may not have): the next slot can start;
+    // every wave has also read K(n), whose buffer the next slot refills
+    if (more) barrier_copies_landed_reads_done<1>();
   }
 
   T* dq = static_cast<T*>(p.dq) + (qrow0 + my_q) * kDim;
@@ -752,6 +786,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     for (int a = 0; a < 4; ++a)
       store4(dq + 32 * dt + 8 * a + 4 * hl, sc * dqacc[dt][4 * a], sc * dqacc[dt][4 * a + 1],
              sc * dqacc[dt][4 * a + 2], sc * dqacc[dt][4 * a + 3]);
+  __syncthreads();
   if (row >= 0 && tid < p.K) {
     const int64_t o = (((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.H + c.h) * p.K + tid;
     p.dw_part[o] = dw_s[0][tid] + dw_s[1][tid];
@@ -777,15 +812,20 @@ __device__ __forceinline__ PairRef decode_pair(const AttendParams& p, int32_t co
   return r;
 }
 
+// One workgroup of two waves per (batch row, head, key chunk); each wave owns 32 of its keys and
+// walks the chunk's retrievals, double-buffered: the next entry's Q and dO tiles and its 64
+// {bias, e} pairs are copied in at the start of the current one.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   using TL = Tile<T>;
-  constexpr int kVecBytes = 2 * kChunk * 4;                      // lse and e of one pair
-  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];  // [Q tile, dO tile, lse, e]
+  using Off = TileOffsets<T, kWaves>;
+  constexpr int kVecBytes = kChunk * 8;  // {bias, e} of the 64 queries of one entry
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];  // [Q tile, dO tile, vectors]
   __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
   __shared__ i32x2_t ents[kEntRound];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
   const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
   const int64_t j = lid % p.n_kv;
@@ -803,6 +843,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     kf[s].load(kp + 16 * s + 8 * hl);
     vf[s].load(vp + 16 * s + 8 * hl);
   }
+  Off off;
+  off.init(wave);
   f32x16_t dkacc[2] = {zero16(), zero16()};
   f32x16_t dvacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
@@ -811,80 +853,71 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   const int32_t count = p.counts[segment];
   const i32x2_t* list = reinterpret_cast<const i32x2_t*>(p.pairs) + segment * p.pair_cap;
 
-  // The list is walked in rounds of up to kEntRound entries {code, weight}, staged in LDS so
-  // that the pipelined loop never waits on a global load.
-  float w_next = 0.f;
+  // The list is walked in rounds of up to kEntRound entries {code, weight}, staged in LDS.  Each
+  // wave issues kCopies per tile plus one vector copy (lanes < 16) per entry.
   auto fill = [&](const i32x2_t ent, char* buf) {
     const PairRef r = decode_pair(p, ent[0]);
-    w_next = __int_as_float(__builtin_amdgcn_readfirstlane(ent[1]));
     const int64_t gbh = (static_cast<int64_t>(r.g) * p.B + b) * p.H + h;
     const int64_t qrow0 = gbh * Lq + r.t * kChunk;
-    tile_load_async<T, kWaves>(static_cast<const T*>(p.q) + qrow0 * kDim, buf);
-    tile_load_async<T, kWaves>(static_cast<const T*>(p.dout) + qrow0 * kDim, buf + TL::kBytes);
-    if (lane < 16) {  // wave 0 copies the 64 lse values, wave 1 the 64 e values
-      const float* src = (wave == 0 ? p.lse_in : p.delta) + slot_vec_offset(p, gbh, r.t, r.slot) + 4 * lane;
-      copy16_async(src, buf + 2 * TL::kBytes + wave * kChunk * 4);
-    }
+    off.copy(static_cast<const T*>(p.q) + qrow0 * kDim, buf, wave);
+    off.copy(static_cast<const T*>(p.dout) + qrow0 * kDim, buf + TL::kBytes, wave);
+    // wave w copies the pairs of queries 32 w .. 32 w + 31 (16 bytes per lane, lanes < 16)
+    const float* src = p.delta + 2 * (slot_vec_offset(p, gbh, r.t, r.slot) + 32 * wave);
+    if (lane < 16) copy16_async_untracked(src, 16u * lane, buf + 2 * TL::kBytes + 256 * wave);
   };
 
   int32_t n = 0;  // entries in the current round
   auto body = [&](int32_t pr, const char* cur, char* nxt) {
-    const float w = w_next;
     if (pr + 1 < n) fill(ents[pr + 1], nxt);
     const char* Qs = cur;
     const char* Ds = cur + TL::kBytes;
-    const float* lse_v = reinterpret_cast<const float*>(cur + 2 * TL::kBytes);
-    const float* del_v = lse_v + kChunk;
+    const f32x4_t* vec = reinterpret_cast<const f32x4_t*>(cur + 2 * TL::kBytes);  // {b, e, b, e}
     // The two 32-query tiles are processed one after the other (dK, dV need no reduction over
     // queries), which halves the live score registers.
-    const float lw = __builtin_amdgcn_logf(w);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       // S[q][u] and dP'[q][u] for the 32 queries of this tile and this wave's 32 keys
       f32x16_t sacc = zero16(), pacc = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sacc = mma(row_frag<T>(Qs, 32 * qt + pi_row(li), 16 * s + 8 * hl), kf[s], sacc);
-        pacc = mma(row_frag<T>(Ds, 32 * qt + pi_row(li), 16 * s + 8 * hl), vf[s], pacc);
+        sacc = mma(off.kfrag(Qs, qt, s), kf[s], sacc);
+        pacc = mma(off.kfrag(Ds, qt, s), vf[s], pacc);
       }
-      // lane holds queries 32 qt + 16 hl + r; P_w = w exp(z - lse), log2(w) folded in the bias
+      // lane holds queries 32 qt + 16 hl + r: P_w = w exp(z - lse) = exp2(z log2e + bias)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int q0 = 32 * qt + 16 * hl + 8 * half;
-        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(lse_v + q0);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(lse_v + q0 + 4);
-        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(del_v + q0);
-        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(del_v + q0 + 4);
+        f32x4_t be[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) be[i] = vec[q0 / 2 + i];
         float xp[8], xz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const float lse_q = e < 4 ? l0[e] : l1[e - 4];
-          const float del_q = e < 4 ? d0[e] : d1[e - 4];
-          const float pw = fast_exp2(__builtin_fmaf(sacc[r], c2, __builtin_fmaf(-lse_q, kLog2e, lw)));
+          const float bias_q = be[e >> 1][2 * (e & 1)], e_q = be[e >> 1][2 * (e & 1) + 1];
+          const float pw = fast_exp2(__builtin_fmaf(sacc[r], c2, bias_q));
           xp[e] = pw;
-          xz[e] = pw * (pacc[r] - del_q);
+          xz[e] = pw * (pacc[r] - e_q);
         }
         Frag<T> pf, zf;
         pf.set(xp);
         zf.set(xz);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          dvacc[dt] = mma(col_frag<T>(Ds, q0, 32 * dt), pf, dvacc[dt]);
-          dkacc[dt] = mma(col_frag<T>(Qs, q0, 32 * dt), zf, dkacc[dt]);
+          dvacc[dt] = mma(off.vfrag(Ds, 2 * qt + half, dt), pf, dvacc[dt]);
+          dkacc[dt] = mma(off.vfrag(Qs, 2 * qt + half, dt), zf, dkacc[dt]);
         }
       }
     }
-    wait_async_copies();
-    __syncthreads();
+    // the next entry's copies landed, and every wave is done with this entry's buffer
+    barrier_copies_landed_reads_done<0>();
   };
   for (int32_t round0 = 0; round0 < count; round0 += kEntRound) {
     n = count - round0 < kEntRound ? count - round0 : kEntRound;
     for (int e = tid; e < n; e += kThreads) ents[e] = list[round0 + e];
     __syncthreads();
     fill(ents[0], buf0);
-    wait_async_copies();
-    __syncthreads();
+    barrier_copies_landed_reads_done<0>();
     for (int32_t pr = 0; pr < n; pr += 2) {
       body(pr, buf0, buf1);
       if (pr + 1 < n) body(pr + 1, buf1, buf0);

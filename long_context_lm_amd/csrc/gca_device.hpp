@@ -235,6 +235,12 @@ __device__ __forceinline__ void barrier_copies_landed() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// Both: this wave's copies landed (all but the N most recent) and its LDS reads finished.
+template <int N>
+__device__ __forceinline__ void barrier_copies_landed_reads_done() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // MFMA operand holding 8 consecutive columns of one tile row: lane gets X[row][col0 .. col0+7].
 __device__ __forceinline__ Frag<bf16_t> frag_row(const char* lds, int row, int col0, bf16_t*) {

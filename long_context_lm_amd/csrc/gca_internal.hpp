@@ -50,7 +50,7 @@ struct AttendParams {
   void* dk;
   void* dv;
   float* dscore;
-  float* delta;         // [G, B, H, n_q, K, 64]  e_{t,k} = <dout_t, O_{t,k}>
+  float* delta;         // [G, B, H, n_q, K, 64, 2] {log2 w_k - lse_{t,k} log2 e, e_{t,k} = <dout_t, O_{t,k}>}
   float* dw_part;       // [G, B, n_q, H, K] per-head sums of e over a chunk's tokens
   float* wts;           // [G, B, n_q, K] fusion weights (0 on invalid slots)
   int32_t* pairs;       // [B, n_kv, pair_cap, 2] {(g, row, slot) code, fusion weight} per retrieval of
