@@ -2,14 +2,14 @@
 
 Two kinds of run, each its own process under rocprofv3 (commands in the summaries):
 
-  kernel stats     rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run --
-                       python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-inference
+  kernel stats     rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py
+                   (the default benchmark command; its JSON line goes to BENCH_LOG)
   HBM traffic      rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o run --
                        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-inference --copy-calibration
                    (then the same with WRITE_SIZE into DIR_W)
 
-    python -m long_context_lm_amd.profiling stats DIR OUT.md
-    python -m long_context_lm_amd.profiling traffic DIR_F DIR_W OUT.json
+    python -m long_context_lm_amd.profiling stats DIR OUT.md BENCH_LOG COMMAND...
+    python -m long_context_lm_amd.profiling traffic DIR_F DIR_W OUT.json COMMAND_F COMMAND_W
 
 The traffic summary scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the
 bytes-per-KiB the same counter reads for a plain device copy of known size (torch copy_ of
@@ -57,17 +57,25 @@ def _rows(directory: str, suffix: str):
         return list(csv.DictReader(fh))
 
 
-def stats(directory: str, out_md: str, command: str, warmup: int = 2) -> None:
-    """Per-kernel durations from the kernel trace, leaving out each kernel's first `warmup`
-    dispatches (the benchmark's warm-up steps), plus rocprofv3's own all-dispatch statistics."""
+def stats(directory: str, out_md: str, command: str, bench_log: str | None = None, warmup: int = 5,
+          steps: int = 20) -> None:
+    """Per-kernel durations of the timed training steps from the kernel trace: dispatches
+    [warmup, warmup + steps) of each kernel in time order (the inference runs that follow are left
+    out), next to the bench's own event-timed averages read from the JSON line of the same run."""
     per = {}
     for r in sorted(_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
         s = short_name(r["Kernel_Name"])
         if s is None or s == "copy":
             continue
         per.setdefault(s, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    rows = _rows(directory, "kernel_stats.csv")
-    allstat = {short_name(r["Name"]): r for r in rows if short_name(r["Name"]) not in (None, "copy")}
+    bench = {}
+    if bench_log:
+        with open(bench_log) as fh:
+            line = [l for l in fh if l.startswith("{")][-1]
+        res = json.loads(line)
+        bench = {k: v["avg_ms"] * 1e3 for k, v in res["kernels"].items()}
+        bench["_step_ms"] = res["ms_per_step"]
+        bench["_dominant"] = res["roofline"]["kernel"]
     lines = [
         "# Kernel durations: GCA retrieve + forward + backward, 16K training workload",
         "",
@@ -75,18 +83,69 @@ def stats(directory: str, out_md: str, command: str, warmup: int = 2) -> None:
         "",
         f"Command (repository root, on an MI355X): `{command}`",
         "",
-        f"Kernel sources hash: `{source_hash()}`.  Timed columns leave out each kernel's first "
-        f"{warmup} dispatches (warm-up steps); the last columns are rocprofv3 --stats over all calls.",
+        f"Kernel sources hash: `{source_hash()}`.  Trace columns: dispatches {warmup}..{warmup + steps - 1} of "
+        "each kernel (the timed training steps; warm-up and the inference runs left out).  Last column: the "
+        "average that bench.py itself measured with HIP events around each launch in the same run"
+        + (f" (step {bench['_step_ms']:.3f} ms; roofline kernel `{bench['_dominant']}`)." if bench else "."),
         "",
-        "| kernel | timed calls | average (us) | min (us) | max (us) | all calls | all-call average (us) |",
-        "|---|---|---|---|---|---|---|",
+        "| kernel | timed calls | trace average (us) | min (us) | max (us) | bench events average (us) |",
+        "|---|---|---|---|---|---|",
     ]
-    order = sorted(per, key=lambda k: -sum(per[k][warmup:] or per[k]))
+    order = sorted(per, key=lambda k: -sum(per[k][warmup:warmup + steps]))
+    if bench:  # only the kernels of the training step (not those that run only in inference)
+        order = [k for k in order if k in bench]
     for k in order:
-        d = per[k][warmup:] or per[k]
-        a = allstat.get(k)
-        lines.append(f"| {k} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} | "
-                     f"{a['Calls'] if a else ''} | {float(a['AverageNs']) / 1e3 if a else 0:.1f} |")
+        d = per[k][warmup:warmup + steps] or per[k]
+        ev = f"{bench[k]:.1f}" if k in bench else ""
+        lines.append(f"| {k} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} | {ev} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> None:
+    """Decode-step kernels of the same run (the 1M- and 16M-token history latency runs), one row
+    per kernel and launch shape, next to the per-step latencies bench.py reported."""
+    groups = {}
+    for r in _rows(directory, "kernel_trace.csv"):
+        s = short_name(r["Kernel_Name"])
+        if s not in ("score_topk", "topk_merge", "attend_fwd"):
+            continue
+        wg = int(r["Workgroup_Size_X"])
+        blocks = int(r["Grid_Size_X"]) // wg
+        groups.setdefault((s, blocks, wg), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    with open(bench_log) as fh:
+        res = json.loads([l for l in fh if l.startswith("{")][-1])
+    inf = res.get("inference_latency") or {}
+    # launch shapes of the decode steps (G = 2 rows of one batch row, H = 12, K = 8)
+    shapes = {("score_topk", 128, 256): "1M scan (2 rows x 64 blocks)", ("topk_merge", 2, 1024): "1M / 16M merge",
+              ("score_topk", 1024, 256): "16M scan (2 rows x 512 blocks)", ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)"}
+    lines = [
+        "# Kernel durations: one decode step over a 1M- / 16M-token history (retrieve + attend)",
+        "",
+        "Workload: B=1, G=2, H=12, d=64, K=8, one new 64-token chunk; history 16,384 / 262,144 chunks of bf16 K, V "
+        "and landmarks resident in HBM.",
+        "",
+        f"Command (repository root, on an MI355X): `{command}`",
+        "",
+        f"Kernel sources hash: `{source_hash()}`.  All dispatches of each launch shape in the run (warm and "
+        "cold repetitions, eager and graph replay).",
+        "",
+        "| kernel | launch (workgroups x threads) | workload | dispatches | average (us) | min (us) |",
+        "|---|---|---|---|---|---|",
+    ]
+    for key in sorted(groups, key=lambda k: (k[0], k[1])):
+        if key not in shapes:
+            continue
+        d = groups[key]
+        lines.append(f"| {key[0]} | {key[1]} x {key[2]} | {shapes[key]} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} |")
+    lines += ["", "Per-step latency measured by bench.py in the same run, under the profiler, whose per-dispatch "
+              "overhead inflates these figures (HIP events around retrieve + forward; the unprofiled bench "
+              "line carries the reported latencies):", "",
+              "| history | warm median (us) | cold median (us) | graph replay warm (us) | graph replay cold (us) |",
+              "|---|---|---|---|---|"]
+    for label, v in inf.items():
+        lines.append(f"| {label} | {v['warm']['median_us']:.1f} | {v['cold']['median_us']:.1f} | "
+                     f"{v['graph_warm']['median_us']:.1f} | {v['graph_cold']['median_us']:.1f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -124,8 +183,11 @@ def traffic(dir_fetch: str, dir_write: str, out_json: str, commands) -> None:
 
 if __name__ == "__main__":
     what = sys.argv[1]
-    if what == "stats":
-        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]) or "see long_context_lm_amd/profiling.py")
+    if what == "stats":  # stats DIR OUT.md BENCH_LOG COMMAND...
+        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]) or "see long_context_lm_amd/profiling.py",
+              bench_log=sys.argv[4])
+    elif what == "infer":  # infer DIR OUT.md BENCH_LOG COMMAND...
+        infer_stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), sys.argv[4])
     elif what == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     else:
