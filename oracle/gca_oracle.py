@@ -309,3 +309,41 @@ def backward(q, k, v, idx, score, dout, *, shift=1, attn_scale=0.125):
                 wdw = float((w * dw).sum())
                 dscore[g, b, row] = np.where(valid, w * (dw - wdw), 0.0)
     return dq, dk, dv, dscore
+
+
+# ---------------------------------------------------------------------------------------
+# Landmark gradients
+# ---------------------------------------------------------------------------------------
+def landmark_backward(lq, lk, idx, dscore, *, score_scale=0.125, q_chunk_base=0, n_kv=None):
+    """Gradients that reach the landmarks through the retrieval scores, selection held fixed.
+
+    The retrieval scores weight the fused outputs, so the language-model loss differentiates
+    them [Notes, Key designs: GCA]; a score relates the landmark of a chunk to the landmark of
+    an earlier chunk [Notes, Key designs: causal retrieval].  With s_ij = score_scale <lq_i, lk_j>
+    (reading R1 without its float32 roundings, which carry no gradient) and dscore the gradient of
+    the loss with respect to the clean score of each slot:
+      dlq[g,b,r] = score_scale * sum_k dscore[g,b,r,k] lk[g,b,idx[g,b,r,k]]
+      dlk[g,b,j] = score_scale * sum over (r, k) with idx[g,b,r,k] = j of dscore[g,b,r,k] lq[g,b,r]
+    Slots count when 0 <= idx < min(q_chunk_base + r, n_kv) (the candidates of reading R3).
+    Returns float64 arrays shaped like lq and lk.
+    """
+    lq = np.asarray(lq, dtype=np.float64)
+    lk = np.asarray(lk, dtype=np.float64)
+    dscore = np.asarray(dscore, dtype=np.float64)
+    G, B, n_q, _ = lq.shape
+    if n_kv is None:
+        n_kv = lk.shape[2]
+    K = idx.shape[-1]
+    scale = float(np.float32(score_scale))
+    dlq = np.zeros_like(lq)
+    dlk = np.zeros_like(lk)
+    for g in range(G):
+        for b in range(B):
+            for r in range(n_q):
+                limit = min(q_chunk_base + r, n_kv)
+                for kk in range(K):
+                    j = int(idx[g, b, r, kk])
+                    if 0 <= j < limit:
+                        dlq[g, b, r] += dscore[g, b, r, kk] * lk[g, b, j]
+                        dlk[g, b, j] += dscore[g, b, r, kk] * lq[g, b, r]
+    return scale * dlq, scale * dlk

@@ -411,3 +411,80 @@ def test_backward_invariants():
         if j not in used:
             assert np.all(dk[:, :, 64 * j:64 * j + 64] == 0)
             assert np.all(dv[:, :, 64 * j:64 * j + 64] == 0)
+
+
+# ------------------------------------------------------------------ landmark gradients
+def _landmark_case(seed=0, G=2, B=2, n=9, K=3, base=0, n_kv=None):
+    n_kv = n if n_kv is None else n_kv
+    shp = I.Shape(B=B, G=G, H=1, n_q=n, n_kv=n_kv, topk=K, q_chunk_base=base, shift=0)
+    t = I.make_inputs(shp, "f32", seed=seed, names=("lq", "lk"))
+    lq, lk = I.as_f64(t["lq"]), I.as_f64(t["lk"])
+    idx, _ = O.retrieve(lq, lk, K, q_chunk_base=base, n_kv=n_kv)
+    rng = np.random.default_rng(seed + 100)
+    ds = np.where(idx >= 0, rng.standard_normal(idx.shape), 0.0)
+    return lq, lk, idx, ds
+
+
+@pytest.mark.parametrize("base,n_kv", [(0, 9), (5, 7)])
+def test_landmark_backward_matches_autograd(base, n_kv):
+    """Autograd of L = sum dscore * score_scale <lq_r, lk_idx> written with torch matmuls."""
+    lq, lk, idx, ds = _landmark_case(seed=4, base=base, n_kv=n_kv)
+    dlq, dlk = O.landmark_backward(lq, lk, idx, ds, q_chunk_base=base, n_kv=n_kv)
+    lq_t = torch.tensor(lq, requires_grad=True)
+    lk_t = torch.tensor(lk, requires_grad=True)
+    loss = 0
+    G, B, n, _ = lq.shape
+    for g in range(G):
+        for b in range(B):
+            S = 0.125 * (lq_t[g, b] @ lk_t[g, b].T)  # [n_q, n_kv]
+            for r in range(n):
+                for kk in range(idx.shape[-1]):
+                    j = int(idx[g, b, r, kk])
+                    if j >= 0:
+                        loss = loss + float(ds[g, b, r, kk]) * S[r, j]
+    loss.backward()
+    np.testing.assert_allclose(dlq, lq_t.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dlk, lk_t.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_landmark_backward_bilinear_identity():
+    """L is bilinear in (lq, lk): <lq, dL/dlq> = <lk, dL/dlk> = L.  Unretrieved chunks get 0."""
+    lq, lk, idx, ds = _landmark_case(seed=7, G=2, B=3, n=11, K=4)
+    dlq, dlk = O.landmark_backward(lq, lk, idx, ds)
+    L = 0.0
+    for g, b, r, kk in np.ndindex(*idx.shape):
+        j = int(idx[g, b, r, kk])
+        if j >= 0:
+            L += ds[g, b, r, kk] * 0.125 * float(np.dot(lq[g, b, r], lk[g, b, j]))
+    np.testing.assert_allclose((lq * dlq).sum(), L, rtol=1e-12)
+    np.testing.assert_allclose((lk * dlk).sum(), L, rtol=1e-12)
+    for g, b in np.ndindex(*idx.shape[:2]):
+        used = set(int(j) for j in idx[g, b].ravel() if j >= 0)
+        for j in range(lk.shape[2]):
+            if j not in used:
+                assert np.all(dlk[g, b, j] == 0)
+
+
+def test_landmark_backward_chains_with_gca_backward():
+    """End to end: scores computed from the landmarks (score_scale <lq, lk>, selection fixed)
+    feed the GCA forward; autograd of sum(dout * O) with respect to the landmarks equals the
+    landmark gradient of the oracle's d(score)."""
+    shp, x, idx, _ = _small_case(seed=9, G=2, B=1, H=2, n=7, K=3)
+    rng = np.random.default_rng(5)
+    dout = rng.standard_normal(x["q"].shape)
+    lq_t = torch.tensor(x["lq"], requires_grad=True)
+    lk_t = torch.tensor(x["lk"], requires_grad=True)
+    neg_inf = torch.tensor(-math.inf, dtype=torch.float64)
+    flat = []
+    for g, b, r, kk in np.ndindex(*idx.shape):
+        j = int(idx[g, b, r, kk])
+        flat.append(0.125 * (lq_t[g, b, r] * lk_t[g, b, j]).sum() if j >= 0 else neg_inf)
+    score = torch.stack(flat).reshape(idx.shape)
+    q, k, v = (torch.tensor(x[n]) for n in ("q", "k", "v"))
+    out = _torch_gca(q, k, v, idx, score, 1, 0.125)
+    out.backward(torch.from_numpy(dout))
+    sc = score.detach().numpy()
+    _, _, _, ds = O.backward(x["q"], x["k"], x["v"], idx, sc, dout, shift=1)
+    dlq, dlk = O.landmark_backward(x["lq"], x["lk"], idx, ds)
+    np.testing.assert_allclose(dlq, lq_t.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dlk, lk_t.grad.numpy(), rtol=1e-9, atol=1e-11)
