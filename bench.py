@@ -152,6 +152,40 @@ def cpu_baseline(shape, host):
                       f"{dt:.1f} s on {os.cpu_count()} host CPUs (BLAS threads {threads})"}
 
 
+def landmark_timing(shape, cfg, dev, bufs, iters=50):
+    """gca_landmark_backward on the step's own indices and d(score) (a row beyond the timed step:
+    the gradients that reach the landmarks through the retrieval scores)."""
+    import torch
+
+    from long_context_lm_amd import gca
+
+    ws = torch.empty(max(gca.workspace_size(gca.OP_LANDMARK_BACKWARD, cfg), 1), dtype=torch.uint8, device="cuda")
+    out = (torch.empty_like(dev["lq"]), torch.empty_like(dev["lk"]))
+
+    def one():
+        gca.landmark_backward(cfg, dev["lq"], dev["lk"], bufs["idx"], bufs["dscore"], ws=ws, out=out)
+
+    for _ in range(5):
+        one()
+    torch.cuda.synchronize()
+    gca.profile_collect()
+    gca.profile_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    gca.profile_enable(False)
+    kern = {k: v[0] / v[1] * 1e3 for k, v in gca.profile_collect().items()}
+    us = a.elapsed_time(b) / iters * 1e3
+    G, B, nq, nkv, K = shape.G, shape.B, shape.n_q, shape.n_kv, shape.topk
+    # compulsory bytes: lq, lk read, dlq, dlk written (bf16), idx and d(score) read
+    nbytes = 2 * G * B * (nq + nkv) * 64 * 2 + G * B * nq * K * 8
+    return {"us_per_call": us, "kernels_us": kern, "algorithmic_bytes": nbytes,
+            "hbm_bound_us": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6}
+
+
 def inference_latency(shape, iters=50):
     """Per-chunk retrieve + attend latency over a long history held in HBM (warm and cold)."""
     import torch
@@ -294,6 +328,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    log("landmark gradients (gca_landmark_backward) on the step's indices and d(score)")
+    lmk = landmark_timing(shape, cfg, dev, bufs)
+    log(f"  {lmk['us_per_call']:.1f} us per call " + ", ".join(f"{k} {v:.1f}" for k, v in lmk["kernels_us"].items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -332,6 +370,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "inference_latency": infer,
+        "landmark_backward": lmk,
     }
     print(json.dumps(out), flush=True)
 

@@ -64,7 +64,12 @@ typedef enum {
 
 typedef enum { GCA_BF16 = 0, GCA_F32 = 1 } gca_dtype;
 
-typedef enum { GCA_OP_RETRIEVE = 0, GCA_OP_FORWARD = 1, GCA_OP_BACKWARD = 2 } gca_op;
+typedef enum {
+  GCA_OP_RETRIEVE = 0,
+  GCA_OP_FORWARD = 1,
+  GCA_OP_BACKWARD = 2,
+  GCA_OP_LANDMARK_BACKWARD = 3
+} gca_op;
 
 /* Sizes and options of one problem.  Fields are read, never written. */
 typedef struct {
@@ -147,6 +152,29 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
                         const int32_t* idx, const float* score, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, float* dscore, void* ws,
                         size_t ws_bytes, void* stream);
+
+/*
+ * Landmark gradients [Notes, Key designs: GCA; Key designs: causal retrieval]: the scores weight
+ * the fused outputs, so the loss differentiates them, and a score relates the landmark of chunk i
+ * to the landmark of an earlier chunk j; this carries d(score) on to both landmarks.  With
+ * s_ij = score_scale <lq_i, lk_j> (the float32 roundings of the canonical score carry no
+ * gradient) and the retrieved indices held fixed:
+ *   dlq[g,b,r,:] = score_scale * sum over slots k of dscore[g,b,r,k] * lk[g,b,idx[g,b,r,k],:]
+ *   dlk[g,b,j,:] = score_scale * sum over the (r, k) with idx[g,b,r,k] = j, in (r, k) order, of
+ *                  dscore[g,b,r,k] * lq[g,b,r,:]
+ * Slots count when 0 <= idx < min(q_chunk_base + r, n_kv) (every candidate gca_retrieve can
+ * produce; pass dscore = 0 for slots that must not contribute).  Sums run in a fixed order,
+ * without atomics, accumulated in fp32 and rounded once to the problem dtype: results are
+ * bit-identical from run to run.
+ * lq [G,B,n_q,dl], lk [G,B,n_kv,dl], idx, dscore [G,B,n_q,K]: inputs; dlq (like lq) and dlk
+ * (like lk): outputs, fully overwritten (zero rows for chunks no slot selected).  dscore is fp32
+ * (as gca_backward writes it); lq, lk, dlq, dlk use problem->dtype.  ws: >=
+ * gca_workspace_size(LANDMARK_BACKWARD) (an inverse retrieval index; contents need no setup).
+ * Uses only n_q_chunks, n_kv_chunks, q_chunk_base, B, G, topk, dtype, score_scale of problem.
+ */
+gca_status gca_landmark_backward(const gca_problem* problem, const void* lq, const void* lk,
+                                 const int32_t* idx, const float* dscore, void* dlq, void* dlk,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Static English text for a status code ("unknown status" for values outside the enum). */
 const char* gca_status_string(gca_status status);

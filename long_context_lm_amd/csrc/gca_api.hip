@@ -12,8 +12,9 @@
 namespace gca {
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd", "inverse_index",
-                                           "bwd_query",  "bwd_key",    "score_grad"};
+  static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
+                                           "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
+                                           "lmk_key_grad"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -119,6 +120,25 @@ RetrievePlan plan_retrieve(const gca_problem* p) {
   return r;
 }
 
+// Landmark gradients: the inverse retrieval index (entry lists per key chunk) and its counts.
+struct LandmarkLayout {
+  size_t pairs, counts, total;
+};
+
+LandmarkLayout plan_landmark(const gca_problem* p) {
+  LandmarkLayout l{};
+  if (p->n_kv_chunks == 0) return l;  // no key landmarks: only dlq (zeros or gathers) is written
+  const size_t G = p->G, B = p->B;
+  const size_t nq = static_cast<size_t>(p->n_q_chunks), nkv = static_cast<size_t>(p->n_kv_chunks);
+  size_t off = 0;
+  l.pairs = off;
+  off += align_up(B * nkv * G * nq * 2 * sizeof(int32_t));
+  l.counts = off;
+  off += align_up(B * nkv * sizeof(int32_t));
+  l.total = off;
+  return l;
+}
+
 struct BackwardLayout {
   size_t delta, dw_part, wts, pairs, counts, total;
 };
@@ -194,6 +214,7 @@ gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes)
     case GCA_OP_BACKWARD:
       *bytes = plan_backward(problem).total;
       return GCA_OK;
+    case GCA_OP_LANDMARK_BACKWARD: *bytes = plan_landmark(problem).total; return GCA_OK;
     default: return GCA_ERR_INVALID_ARGUMENT;
   }
 }
@@ -319,6 +340,58 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
   if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
+  return GCA_OK;
+}
+
+gca_status gca_landmark_backward(const gca_problem* problem, const void* lq, const void* lk,
+                                 const int32_t* idx, const float* dscore, void* dlq, void* dlk, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  GCA_TRY(validate_problem(problem));
+  const gca_problem* p = problem;
+  const bool any = p->n_q_chunks > 0;
+  const bool kv = p->n_kv_chunks > 0;
+  GCA_TRY(check_tensor(lq, any, 16));
+  GCA_TRY(check_tensor(lk, kv, 16));
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(dscore, any, 4));
+  GCA_TRY(check_tensor(dlq, any, 16));
+  GCA_TRY(check_tensor(dlk, kv, 16));
+  const LandmarkLayout L = plan_landmark(p);
+  GCA_TRY(check_ws(L.total, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!any && !kv) return GCA_OK;
+
+  char* w = static_cast<char*>(ws);
+  const bool f32 = p->dtype == GCA_F32;
+  LandmarkParams m{};
+  m.lq = lq;
+  m.lk = lk;
+  m.idx = idx;
+  m.dscore = dscore;
+  m.dlq = dlq;
+  m.dlk = dlk;
+  m.n_q = p->n_q_chunks;
+  m.n_kv = p->n_kv_chunks;
+  m.q_base = p->q_chunk_base;
+  m.G = p->G;
+  m.B = p->B;
+  m.K = p->topk;
+  m.pair_cap = static_cast<int32_t>(static_cast<int64_t>(p->G) * p->n_q_chunks);
+  m.score_scale = p->score_scale;
+  if (kv) {
+    m.pairs = reinterpret_cast<const int32_t*>(w + L.pairs);
+    m.counts = reinterpret_cast<const int32_t*>(w + L.counts);
+    // the backward's inverse index, over every row (shift 0) and with d(score) as the entry value
+    AttendParams a = attend_params(p);
+    a.idx = idx;
+    a.wts = const_cast<float*>(dscore);
+    a.shift = 0;
+    a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
+    a.counts = reinterpret_cast<int32_t*>(w + L.counts);
+    GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
+  }
+  if (any) GCA_TRY(launch(kLmkQueryGrad, s, [&] { return launch_lmk_query_grad(m, f32, s); }));
+  if (kv) GCA_TRY(launch(kLmkKeyGrad, s, [&] { return launch_lmk_key_grad(m, f32, s); }));
   return GCA_OK;
 }
 

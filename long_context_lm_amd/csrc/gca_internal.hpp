@@ -15,6 +15,8 @@ enum KernelId {
   kBwdQuery,
   kBwdKey,
   kScoreGrad,
+  kLmkQueryGrad,
+  kLmkKeyGrad,
   kNumKernels
 };
 const char* kernel_name(int id);
@@ -62,6 +64,21 @@ struct AttendParams {
   float attn_scale;
 };
 
+struct LandmarkParams {
+  const void* lq;
+  const void* lk;
+  const int32_t* idx;
+  const float* dscore;
+  void* dlq;
+  void* dlk;
+  const int32_t* pairs;   // inverse retrieval index with d(score) as the entry value
+  const int32_t* counts;
+  int64_t n_q, n_kv, q_base;
+  int32_t G, B, K;
+  int32_t pair_cap;       // G * n_q
+  float score_scale;
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s);
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s);
@@ -70,5 +87,7 @@ hipError_t launch_inverse_index(const AttendParams& p, hipStream_t s);
 hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_score_grad(const AttendParams& p, hipStream_t s);
+hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t s);
+hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 
 }  // namespace gca

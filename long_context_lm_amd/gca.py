@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgca.so")
 
 GCA_OK = 0
-OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
+OP_RETRIEVE, OP_FORWARD, OP_BACKWARD, OP_LANDMARK_BACKWARD = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "f32": 1}
 
 
@@ -82,7 +82,8 @@ def load() -> ctypes.CDLL:
     lib.gca_retrieve.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward",
+    lib.gca_landmark_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gca_status_string.argtypes = [ctypes.c_int]
@@ -216,6 +217,22 @@ def backward(cfg: Config, q, k, v, idx, score, lse, dout, ws=None, out=None):
                                                _ptr(score), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                                _ptr(dv), _ptr(dscore), _ptr(ws), n, _stream()))
     return dq, dk, dv, dscore
+
+
+def landmark_backward(cfg: Config, lq, lk, idx, dscore, ws=None, out=None):
+    """gca_landmark_backward: returns (dlq like lq, dlk like lk)."""
+    import torch
+
+    dlq, dlk = (torch.empty_like(lq), torch.empty_like(lk)) if out is None else out
+    if ws is None:
+        ws, n = _workspace(OP_LANDMARK_BACKWARD, cfg, lq.device)
+    else:
+        n = ws.numel()
+    prob = cfg.problem()
+    _check("gca_landmark_backward", load().gca_landmark_backward(ctypes.byref(prob), _ptr(lq), _ptr(lk), _ptr(idx),
+                                                                 _ptr(dscore), _ptr(dlq), _ptr(dlk), _ptr(ws), n,
+                                                                 _stream()))
+    return dlq, dlk
 
 
 def profile_enable(on: bool = True):

@@ -83,12 +83,13 @@ def ws_size(p, op):
 def test_problem_validation(field, value, status):
     p = good(**{field: value})
     lib = gca.load()
-    for op in (0, 1, 2):
+    for op in (0, 1, 2, 3):
         assert ws_size(p, op)[0] == status
     z = ctypes.c_void_p(FAKE)
     assert lib.gca_retrieve(ctypes.byref(p), z, z, z, z, None, 0, None) == status
     assert lib.gca_forward(ctypes.byref(p), z, z, z, z, z, z, z, None, 0, None) == status
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, None, 0, None) == status
+    assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, None, 0, None) == status
 
 
 def test_null_problem_and_bad_op():
@@ -96,7 +97,8 @@ def test_null_problem_and_bad_op():
     n = ctypes.c_size_t(0)
     assert lib.gca_workspace_size(0, None, ctypes.byref(n)) == INVALID
     p = good()
-    assert lib.gca_workspace_size(3, ctypes.byref(p), ctypes.byref(n)) == INVALID
+    assert lib.gca_workspace_size(4, ctypes.byref(p), ctypes.byref(n)) == INVALID
+    assert lib.gca_workspace_size(-1, ctypes.byref(p), ctypes.byref(n)) == INVALID
     assert lib.gca_workspace_size(0, ctypes.byref(p), None) == INVALID
     assert lib.gca_retrieve(None, None, None, None, None, None, 0, None) == INVALID
 
@@ -114,6 +116,10 @@ def test_workspace_sizes():
     # more rows: blocks grow (cpt doubles) until the grid is at most 1024 workgroups
     c = gca.Config(B=8, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
     assert gca.workspace_size(gca.OP_RETRIEVE, c) == 16 * 64 * 8 * 8 + 16 * 64 * 8 * 4
+    # landmark gradients: the inverse index over every row ({code, value} pairs) and its counts
+    c = gca.Config(B=8, G=2, H=12, n_q=256, n_kv=256, topk=8)
+    assert gca.workspace_size(gca.OP_LANDMARK_BACKWARD, c) == 8 * 256 * 2 * 256 * 2 * 4 + 8 * 256 * 4
+    assert gca.workspace_size(gca.OP_LANDMARK_BACKWARD, gca.Config(B=1, G=1, H=1, n_q=3, n_kv=0, topk=2)) == 0
     # (group, row, slot) codes of the inverse index must fit in int32
     c = gca.Config(B=1, G=4, H=1, n_q=1 << 26, n_kv=1024, topk=16)
     with pytest.raises(gca.GcaError):
@@ -141,6 +147,15 @@ def test_pointer_checks():
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z,
                             ctypes.c_void_p(FAKE + 16), need, None) == MISALIGNED
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, mis, z, z, z, need, None) == MISALIGNED
+    # landmark gradients: tensors, then the workspace
+    st, need = ws_size(p, 3)
+    assert st == OK and need > 0
+    assert lib.gca_landmark_backward(ctypes.byref(p), None, z, z, z, z, z, z, need, None) == INVALID
+    assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, mis, z, z, need, None) == MISALIGNED
+    assert lib.gca_landmark_backward(ctypes.byref(p), z, z, ctypes.c_void_p(FAKE + 2), z, z, z, z, need,
+                                     None) == MISALIGNED
+    assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, z, need - 1, None) == WS_SMALL
+    assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, None, need, None) == INVALID
     # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
     big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED
@@ -153,6 +168,7 @@ def test_empty_problem_is_a_noop_without_gpu():
     assert lib.gca_forward(ctypes.byref(p), None, None, None, None, None, None, None, None, 0, None) == OK
     p = good(n_q_chunks=0, n_kv_chunks=0)
     assert lib.gca_backward(ctypes.byref(p), *([None] * 11), None, 0, None) == OK
+    assert lib.gca_landmark_backward(ctypes.byref(p), *([None] * 6), None, 0, None) == OK
 
 
 def test_status_strings_and_error_state():
