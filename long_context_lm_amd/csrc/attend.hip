@@ -984,12 +984,20 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
       const int32_t g = gr / nq, row = gr - g * nq;
       const int64_t rbase = ((static_cast<int64_t>(g) * p.B + b) * nq + row) * K;
       const bool live = row >= row_lo && row < row_hi;
-      for (int k = 0; k < K; ++k) {
-        const int32_t jj = p.idx[rbase + k];
-        idx_s[lr][k] = jj;
-        wts_s[lr][k] = p.wts[rbase + k];
-        if (live && jj >= j0 && jj < j0 + 64 && jj < p.n_kv)
-          atomicOr(&mask[lr >> 5][jj - j0], 1u << (lr & 31));
+      int32_t jv[kMaxTopk];
+      float wv[kMaxTopk];
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {  // all of the row's loads in flight together
+        jv[k] = k < K ? p.idx[rbase + k] : -1;
+        wv[k] = k < K ? p.wts[rbase + k] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {
+        if (k >= K) break;
+        idx_s[lr][k] = jv[k];
+        wts_s[lr][k] = wv[k];
+        if (live && jv[k] >= j0 && jv[k] < j0 + 64 && jv[k] < p.n_kv)
+          atomicOr(&mask[lr >> 5][jv[k] - j0], 1u << (lr & 31));
       }
     }
     __syncthreads();

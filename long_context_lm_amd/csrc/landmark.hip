@@ -46,8 +46,11 @@ __global__ __launch_bounds__(kThreads) void lmk_query_grad_kernel(LandmarkParams
   from_f32(static_cast<T*>(p.dlq) + rowid * kDim + lane, acc * p.score_scale);
 }
 
+// The chunk's entry list is read 64 entries at a time, one per lane (one coalesced load), and
+// the entries are then taken in list order from the lanes, eight row gathers in flight at once.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void lmk_key_grad_kernel(LandmarkParams p) {
+  constexpr int kGather = 8;
   const int lane = threadIdx.x & 63;
   const int64_t outid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   if (outid >= static_cast<int64_t>(p.G) * p.B * p.n_kv) return;  // whole wave
@@ -61,20 +64,28 @@ __global__ __launch_bounds__(kThreads) void lmk_key_grad_kernel(LandmarkParams p
   const T* lq = static_cast<const T*>(p.lq) + gb * p.n_q * kDim;
   const int32_t nqk = static_cast<int32_t>(p.n_q) * p.K;  // entry code = (g n_q + row) K + slot
   float acc = 0.f;
-  for (int32_t e0 = 0; e0 < count; e0 += kBatch) {
-    float x[kBatch], d[kBatch];
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e) {
-      const bool in = e0 + e < count;
-      const int32_t code = in ? __builtin_amdgcn_readfirstlane(list[e0 + e][0]) : -1;
-      const int32_t row = (code % nqk) / p.K;
-      // entries are grouped by g, rows ascending; j < q_base + row as for dlq
-      const bool use = in && code / nqk == g && j < p.q_base + row;
-      d[e] = use ? __int_as_float(__builtin_amdgcn_readfirstlane(list[e0 + e][1])) : 0.f;
-      x[e] = use ? to_f32(lq[static_cast<int64_t>(row) * kDim + lane]) : 0.f;
+  for (int32_t e0 = 0; e0 < count; e0 += 64) {
+    const int32_t n = count - e0 < 64 ? count - e0 : 64;
+    // lane e: entry e0 + e, decoded; entries are grouped by g, rows ascending; j < q_base + row
+    int32_t row = 0;
+    float d = 0.f;
+    if (lane < n) {
+      const i32x2_t ent = list[e0 + lane];
+      row = (ent[0] % nqk) / p.K;
+      if (ent[0] / nqk == g && j < p.q_base + row) d = __int_as_float(ent[1]);
     }
+    for (int32_t e = 0; e < n; e += kGather) {
+      float x[kGather], dd[kGather];
 #pragma unroll
-    for (int e = 0; e < kBatch; ++e) acc = __builtin_fmaf(d[e], x[e], acc);
+      for (int u = 0; u < kGather; ++u) {
+        const int src = e + u < n ? e + u : 0;
+        dd[u] = e + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), src)) : 0.f;
+        const int32_t r = __builtin_amdgcn_readlane(row, src);
+        x[u] = dd[u] != 0.f ? to_f32(lq[static_cast<int64_t>(r) * kDim + lane]) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) acc = __builtin_fmaf(dd[u], x[u], acc);
+    }
   }
   from_f32(static_cast<T*>(p.dlk) + outid * kDim + lane, acc * p.score_scale);
 }
