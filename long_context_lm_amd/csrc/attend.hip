@@ -715,10 +715,9 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 
   f32x16_t dqacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
-  for (int n = 0; n < nslots; ++n) {
+  // unrolled twice below, so that both K buffers are fixed LDS bases (immediate offsets)
+  auto slot_step = [&](int n, char* const Kc, char* const Kn) {
     const bool more = n + 1 < nslots;
-    char* const Kc = (n & 1) ? Kb : Ka;
-    char* const Kn = (n & 1) ? Ka : Kb;
     const int slot = slot_of(n);
     const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st.w[n])));
     float lse_nxt = 0.f;
@@ -742,16 +741,15 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 
     // P = exp(z - lse); e = sum_u P dP' = <dO, O_slot>; dz = w P (dP' - e)
     const float bias = -lse_cur * kLog2e;
-    float e = 0.f;
+    float e0 = 0.f, e1 = 0.f;  // two interleaved chains (the key halves)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
-        sacc[tt][r] = pr;
-        e = __builtin_fmaf(pr, pacc[tt][r], e);
-      }
-    e = xor32_sum(e);
+    for (int r = 0; r < 16; ++r) {
+      sacc[0][r] = fast_exp2(__builtin_fmaf(sacc[0][r], c2, bias));
+      sacc[1][r] = fast_exp2(__builtin_fmaf(sacc[1][r], c2, bias));
+      e0 = __builtin_fmaf(sacc[0][r], pacc[0][r], e0);
+      e1 = __builtin_fmaf(sacc[1][r], pacc[1][r], e1);
+    }
+    const float e = xor32_sum(e0 + e1);
     // for the key-major pass: P_w = exp2(z log2e + bias) with bias = log2 w - lse log2 e, and e
     if (hl == 0) delta_q[slot * kChunk] = f32x2_t{__builtin_amdgcn_logf(w) + bias, e};
     const float es = sum_queries32(e);
@@ -776,6 +774,10 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     // K(n+1), the lse and V(n+1) landed (the delta store may not have): the next slot can start;
     // every wave has also read K(n), whose buffer the next slot refills
     if (more) barrier_copies_landed_reads_done<1>();
+  };
+  for (int n = 0; n < nslots; n += 2) {
+    slot_step(n, Ka, Kb);
+    if (n + 1 < nslots) slot_step(n + 1, Kb, Ka);
   }
 
   T* dq = static_cast<T*>(p.dq) + (qrow0 + my_q) * kDim;
