@@ -440,8 +440,9 @@ __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
     const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sl.w), k));
     float lse_v[2];
     Frag<T> pf[2][4];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
+    // softmax of half qh -> its P^T operand (scaled by w / l); written per half so that the P V
+    // product of half 0 and the softmax of half 1 are independent work side by side
+    auto half_softmax = [&](int qh) {
       float l;
       const float mx = tile_softmax(sacc[qh], c2, l);
       lse_v[qh] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
@@ -453,11 +454,11 @@ __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
         for (int e = 0; e < 8; ++e) x[e] = sacc[qh][s >> 1][8 * (s & 1) + e] * f;
         pf[qh][s].set(x);
       }
-    }
-    if (kLse) lse_q[k * kChunk] = hl ? lse_v[1] : lse_v[0];
+    };
+    half_softmax(0);
 
-    if (kn >= 0) wait_vm_outstanding<kC + (kLse ? 1 : 0)>();  // V(k) landed: K(kn), lse may not
-    else wait_vm_outstanding<kLse ? 1 : 0>();
+    if (kn >= 0) wait_vm_outstanding<kC>();  // V(k) landed: K(kn) may not have
+    else wait_vm_outstanding<0>();
     Frag<T> vf[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -466,11 +467,15 @@ __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V(k) in registers: the buffer is free
     if (kn >= 0) off.copy(tile_of(p.v, kn), Vs, 0);
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int s = 0; s < 4; ++s) oacc[0][dt] = mma(vf[s][dt], pf[0][s], oacc[0][dt]);
+    half_softmax(1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) oacc[qh][dt] = mma(vf[s][dt], pf[qh][s], oacc[qh][dt]);
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) oacc[1][dt] = mma(vf[s][dt], pf[1][s], oacc[1][dt]);
+    if (kLse) lse_q[k * kChunk] = hl ? lse_v[1] : lse_v[0];
     k = kn;
   }
 
@@ -874,18 +879,24 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     const char* Qs = cur;
     const char* Ds = cur + TL::kBytes;
     const f32x4_t* vec = reinterpret_cast<const f32x4_t*>(cur + 2 * TL::kBytes);  // {b, e, b, e}
-    // The two 32-query tiles are processed one after the other (dK, dV need no reduction over
-    // queries), which halves the live score registers.
+    // Both 32-query tiles' scores first, then each tile's elementwise work beside the other
+    // tile's matrix-core work (the second tile's S and dP' products run beside the first tile's
+    // exp and dz, the first tile's dK and dV products beside the second tile's).
+    f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      // S[q][u] and dP'[q][u] for the 32 queries of this tile and this wave's 32 keys
-      f32x16_t sacc = zero16(), pacc = zero16();
+      sacc[qt] = zero16();
+      pacc[qt] = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sacc = mma(off.kfrag(Qs, qt, s), kf[s], sacc);
-        pacc = mma(off.kfrag(Ds, qt, s), vf[s], pacc);
+        sacc[qt] = mma(off.kfrag(Qs, qt, s), kf[s], sacc[qt]);
+        pacc[qt] = mma(off.kfrag(Ds, qt, s), vf[s], pacc[qt]);
       }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
       // lane holds queries 32 qt + 16 hl + r: P_w = w exp(z - lse) = exp2(z log2e + bias)
+      Frag<T> pf[2], zf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int q0 = 32 * qt + 16 * hl + 8 * half;
@@ -897,19 +908,20 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
           const float bias_q = be[e >> 1][2 * (e & 1)], e_q = be[e >> 1][2 * (e & 1) + 1];
-          const float pw = fast_exp2(__builtin_fmaf(sacc[r], c2, bias_q));
+          const float pw = fast_exp2(__builtin_fmaf(sacc[qt][r], c2, bias_q));
           xp[e] = pw;
-          xz[e] = pw * (pacc[r] - e_q);
+          xz[e] = pw * (pacc[qt][r] - e_q);
         }
-        Frag<T> pf, zf;
-        pf.set(xp);
-        zf.set(xz);
+        pf[half].set(xp);
+        zf[half].set(xz);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          dvacc[dt] = mma(off.vfrag(Ds, 2 * qt + half, dt), pf, dvacc[dt]);
-          dkacc[dt] = mma(off.vfrag(Qs, 2 * qt + half, dt), zf, dkacc[dt]);
+          dvacc[dt] = mma(off.vfrag(Ds, 2 * qt + half, dt), pf[half], dvacc[dt]);
+          dkacc[dt] = mma(off.vfrag(Qs, 2 * qt + half, dt), zf[half], dkacc[dt]);
         }
-      }
     }
     // the next entry's copies landed, and every wave is done with this entry's buffer
     barrier_copies_landed_reads_done<0>();
