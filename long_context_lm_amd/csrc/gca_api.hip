@@ -32,13 +32,15 @@ struct ProfState {
 };
 thread_local ProfState t_prof;
 
-// Retrieval: one workgroup scores a block of 256 * cpt candidates of one row (one candidate per
-// lane per pass).  cpt starts at 1 and doubles while the grid would exceed kRetrieveMaxGroups
-// workgroups (four resident per CU) and a row still spans several blocks; rows spanning several
-// blocks are merged by a second kernel.  The 16M-token history (262,144 candidates per row, two
-// rows) runs as 1,024 workgroups of two candidates per lane, whose loads are all in flight at once.
-constexpr int64_t kRetrieveBlock = 256;
-constexpr int64_t kRetrieveMaxGroups = 1024;
+// Retrieval: one workgroup of nw waves scores a block of 64 nw cpt candidates of one row (one
+// candidate per lane per pass).  Many rows (training) take one wave per block; few rows (a decode
+// step) take four, so that a long history still gives enough waves.  cpt starts at 1 and doubles
+// while the grid would exceed kRetrieveMaxWaves waves and a row still spans several blocks; rows
+// spanning several blocks are merged by a second kernel.  The 16M-token history (262,144
+// candidates per row, two rows) runs as 1,024 workgroups of four waves, two candidates per lane,
+// whose loads are all in flight at once; the 16K training step as 4,096 single waves of four.
+constexpr int64_t kRetrieveMaxWaves = 4096;
+constexpr int64_t kRetrieveManyRows = 1024;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -95,24 +97,27 @@ gca_status validate_problem(const gca_problem* p) {
 }
 
 struct RetrievePlan {
-  int32_t nblk, cpt;
+  int32_t nblk, cpt, nw;
   size_t ws;
 };
 
 RetrievePlan plan_retrieve(const gca_problem* p) {
-  RetrievePlan r{1, 1, 0};
+  RetrievePlan r{1, 1, 4, 0};
   if (p->n_q_chunks == 0) return r;
   const int64_t last_row = p->q_chunk_base + p->n_q_chunks - 1;
   const int64_t max_cand = last_row < p->n_kv_chunks ? last_row : p->n_kv_chunks;
   const int64_t rows = static_cast<int64_t>(p->G) * p->B * p->n_q_chunks;
+  const int64_t nw = rows >= kRetrieveManyRows ? 1 : 4;
+  const int64_t block = 64 * nw;
   int64_t cpt = 1;
-  int64_t nblk = max_cand > 0 ? (max_cand + kRetrieveBlock - 1) / kRetrieveBlock : 1;
-  while (nblk > 1 && rows * nblk > kRetrieveMaxGroups) {
+  int64_t nblk = max_cand > 0 ? (max_cand + block - 1) / block : 1;
+  while (nblk > 1 && rows * nblk * nw > kRetrieveMaxWaves) {
     cpt *= 2;
-    nblk = (max_cand + kRetrieveBlock * cpt - 1) / (kRetrieveBlock * cpt);
+    nblk = (max_cand + block * cpt - 1) / (block * cpt);
   }
   r.nblk = static_cast<int32_t>(nblk);
   r.cpt = static_cast<int32_t>(cpt);
+  r.nw = static_cast<int32_t>(nw);
   if (nblk > 1) {
     const size_t n = static_cast<size_t>(rows) * nblk * p->topk;
     r.ws = align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(float));
@@ -245,6 +250,7 @@ gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* 
   rp.K = p->topk;
   rp.nblk = plan.nblk;
   rp.cpt = plan.cpt;
+  rp.nw = plan.nw;
   rp.score_scale = p->score_scale;
   rp.use_gumbel = p->use_gumbel;
   rp.seed = p->seed;

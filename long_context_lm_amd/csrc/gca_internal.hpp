@@ -32,6 +32,7 @@ struct RetrieveParams {
   int32_t G, B, K;
   int32_t nblk;         // candidate blocks per row (1 = single stage)
   int32_t cpt;          // candidates per thread per block
+  int32_t nw;           // waves per block (1 or 4): 64 nw cpt candidates per block
   float score_scale;
   int32_t use_gumbel;
   uint64_t seed;

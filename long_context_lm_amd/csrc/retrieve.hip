@@ -239,9 +239,6 @@ struct LmkRow<float> {
   }
 };
 
-constexpr int kThreads = 256;            // four waves
-constexpr int kWaves = kThreads / 64;
-constexpr int kBlockCand = kThreads;     // candidates of one block per pass (one per lane)
 constexpr int kMergeThreads = 1024;      // sixteen waves per merged row
 constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeBatch = 8;           // partial entries each merge thread loads at once
@@ -268,16 +265,19 @@ __device__ __forceinline__ void workgroup_topk(int nw, int K, uint64_t key, floa
   }
 }
 
-// One workgroup per (row, block of 256 * cpt candidates).  Lane c of the workgroup scores the
-// candidates j = block start + c + 256 n (n < cpt), so every pass of the four waves reads 256
+// One workgroup of NW waves per (row, block of 64 NW cpt candidates).  Lane c of the workgroup
+// scores the candidates j = block start + c + 64 NW n (n < cpt), so every pass reads 64 NW
 // consecutive key-landmark rows; the next row's load is issued before the current one is scored.
-// At most 128 VGPRs for bf16 landmarks and lists of 8 (four resident workgroups per CU, enough
-// loads in flight to stream a long history); fp32 rows and lists of 16 are larger and keep two.
-template <typename T, int KL>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
+// NW = 4 for a few long rows (a decode step over a long history: many blocks per row, their lists
+// merged by the workgroup and then by topk_merge); NW = 1 for many short rows (training: one wave
+// per row).  At most 128 VGPRs for bf16 landmarks and lists of 8 (four resident waves per SIMD,
+// enough loads in flight to stream a long history); fp32 rows and lists of 16 keep two.
+template <typename T, int KL, int NW>
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
+  constexpr int kBlockCand = 64 * NW;  // candidates of one block per pass (one per lane)
   __shared__ double lq_s[kDim];
-  __shared__ uint64_t lkey[kWaves * kMaxTopk];
-  __shared__ float ls[kWaves * kMaxTopk];
+  __shared__ uint64_t lkey[NW * kMaxTopk];
+  __shared__ float ls[NW * kMaxTopk];
   const int lane = threadIdx.x & 63;
   const int64_t item = blockIdx.x;
   const int blk = static_cast<int>(item % p.nblk);
@@ -325,7 +325,12 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void
   uint64_t key, bkey;
   float sv, bs;
   wave_topk<KL>(L, p.K, key, sv);
-  workgroup_topk<KL>(kWaves, p.K, key, sv, lkey, ls, bkey, bs);
+  if constexpr (NW > 1) {
+    workgroup_topk<KL>(NW, p.K, key, sv, lkey, ls, bkey, bs);
+  } else {
+    bkey = key;
+    bs = sv;
+  }
   if (p.nblk == 1) {
     if (threadIdx.x < p.K) {
       p.idx[rowid * p.K + lane] = key_index(bkey);
@@ -378,17 +383,22 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(RetrieveParam
 
 }  // namespace
 
-hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s) {
-  const int64_t items = static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk;
-  const dim3 grid(static_cast<uint32_t>(items));
+template <int NW>
+void launch_score_topk_nw(const RetrieveParams& p, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk)), block(64 * NW);
   const bool small = p.K <= 8;
   if (f32) {
-    if (small) hipLaunchKernelGGL((score_topk_kernel<float, 8>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((score_topk_kernel<float, 16>), grid, dim3(kThreads), 0, s, p);
+    if (small) hipLaunchKernelGGL((score_topk_kernel<float, 8, NW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((score_topk_kernel<float, 16, NW>), grid, block, 0, s, p);
   } else {
-    if (small) hipLaunchKernelGGL((score_topk_kernel<bf16_t, 8>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((score_topk_kernel<bf16_t, 16>), grid, dim3(kThreads), 0, s, p);
+    if (small) hipLaunchKernelGGL((score_topk_kernel<bf16_t, 8, NW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((score_topk_kernel<bf16_t, 16, NW>), grid, block, 0, s, p);
   }
+}
+
+hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s) {
+  if (p.nw == 1) launch_score_topk_nw<1>(p, f32, s);
+  else launch_score_topk_nw<4>(p, f32, s);
   return hipGetLastError();
 }
 
