@@ -12,9 +12,9 @@
 // above the complement of j, so the largest key is the best score with the lowest j.  Key 0
 // never occurs for a finite score and marks an empty slot.
 //
-// One workgroup scores one block of candidates of one row (cpt candidates per lane, 256 lanes);
-// each lane keeps a sorted list of its best keys, each wave extracts its top K with K rounds of a
-// wave-wide maximum, and the four wave lists are merged through LDS.  Rows with more candidates
+// One workgroup scores one block of candidates of one row (cpt candidates per lane, one or four
+// waves); each lane keeps a sorted list of its best keys, each wave extracts its top K with K
+// rounds of a wave-wide maximum, and the wave lists are merged through LDS.  Rows with more candidates
 // than one block are split over several workgroups whose partial top-K lists a second kernel
 // merges (the 16M-token history: 262,144 candidates per row, 512 blocks of 512).
 #include "gca_device.hpp"
@@ -99,22 +99,23 @@ __device__ __forceinline__ int32_t key_index(uint64_t key) {
 }
 
 // --------------------------------------------------------------- per-lane sorted list
-template <int KL>
+// LL entries, at least min(K, entries the lane sees), so that no lane drops one of the K best.
+template <int LL>
 struct TopList {
-  uint64_t key[KL];
-  float s[KL];
+  uint64_t key[LL];
+  float s[LL];
   __device__ __forceinline__ void clear() {
 #pragma unroll
-    for (int e = 0; e < KL; ++e) {
+    for (int e = 0; e < LL; ++e) {
       key[e] = 0;
       s[e] = 0.f;
     }
   }
   // Insert keeping key[] descending; the smallest entry falls off the end.
   __device__ __forceinline__ void insert(uint64_t k, float sv) {
-    if (k <= key[KL - 1]) return;
+    if (k <= key[LL - 1]) return;
 #pragma unroll
-    for (int e = 0; e < KL; ++e) {
+    for (int e = 0; e < LL; ++e) {
       const bool take = k > key[e];
       const uint64_t tk = key[e];
       const float ts = s[e];
@@ -126,11 +127,11 @@ struct TopList {
   }
   __device__ __forceinline__ void pop() {
 #pragma unroll
-    for (int e = 0; e + 1 < KL; ++e) {
+    for (int e = 0; e + 1 < LL; ++e) {
       key[e] = key[e + 1];
       s[e] = s[e + 1];
     }
-    key[KL - 1] = 0;
+    key[LL - 1] = 0;
   }
 };
 
@@ -160,8 +161,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // round finds the largest head key: first the largest high (score) word, then, only if several
 // lanes share it, the largest low word (the lowest chunk index) among those lanes.  A finite score
 // never has a zero high word and a chunk index never a zero low word, so zero marks an empty list.
-template <int KL>
-__device__ __forceinline__ void wave_topk(TopList<KL>& L, int K, uint64_t& my_key, float& my_s) {
+template <int LL>
+__device__ __forceinline__ void wave_topk(TopList<LL>& L, int K, uint64_t& my_key, float& my_s) {
   const int lane = threadIdx.x & 63;
   my_key = 0;
   my_s = 0.f;
@@ -190,64 +191,84 @@ __device__ __forceinline__ void wave_topk(TopList<KL>& L, int K, uint64_t& my_ke
 __device__ __forceinline__ double lmk_to_f64(const bf16_t* p, int d) { return static_cast<double>(to_f32(p[d])); }
 __device__ __forceinline__ double lmk_to_f64(const float* p, int d) { return static_cast<double>(p[d]); }
 
-// One key-landmark row held in registers, so that the next row's load can be in flight while
-// this one is scored.
+// Key-landmark rows move through LDS so that global reads are whole-row coalesced while each lane
+// still scores one row in dimension order.  A pass covers 64 consecutive rows (one per lane).
+// Wave load k reads rows [kR, kR + R) as one contiguous span (lane i: 16-byte piece i % P of row
+// kR + i / P); the pieces are written to the wave's LDS area and lane r then reads row r back.
+// Piece p of row r sits in slot p ^ f(r), which keeps both the row-wide writes and the per-lane
+// row reads free of bank conflicts (eight lanes of a row cover all slots; rows r and r + 8 use
+// different slots).
 template <typename T>
-struct LmkRow;
+struct RowStage {
+  static constexpr int P = kDim * static_cast<int>(sizeof(T)) / 16;  // 16-byte pieces per row
+  static constexpr int R = 64 / P;                                   // rows per wave load
+  static constexpr int kRowBytes = kDim * static_cast<int>(sizeof(T));
+  u32x4_t v[P];
 
-template <>
-struct LmkRow<bf16_t> {
-  u32x4_t c[8];
-  __device__ __forceinline__ void load(const bf16_t* row) {
-    const u32x4_t* r4 = reinterpret_cast<const u32x4_t*>(row);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = r4[k];
+  __device__ static __forceinline__ int slot(int r, int piece) {
+    const int f = P == 8 ? ((r & 7) ^ ((r >> 3) & 1)) : (r & (P - 1));
+    return piece ^ f;
   }
-  // Exact sequential float64 dot product with the query landmark in LDS.
-  __device__ __forceinline__ double dot(const double* lq_s) const {
-    double acc = 0.0;
+  // Rows [row0, row0 + 64) of lk; rows at or beyond nrows are not read.
+  __device__ __forceinline__ void load(const T* lk, int64_t row0, int64_t nrows, int lane) {
+    const char* base = reinterpret_cast<const char*>(lk) + (lane % P) * 16;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t pair = c[k][w];
-        const double lo = static_cast<double>(__uint_as_float(pair << 16));
-        const double hi = static_cast<double>(__uint_as_float(pair & 0xffff0000u));
-        acc = __builtin_fma(lq_s[8 * k + 2 * w], lo, acc);
-        acc = __builtin_fma(lq_s[8 * k + 2 * w + 1], hi, acc);
-      }
+    for (int k = 0; k < P; ++k) {
+      const int64_t row = row0 + k * R + lane / P;
+      if (row < nrows) v[k] = *reinterpret_cast<const u32x4_t*>(base + row * kRowBytes);
     }
-    return acc;
+  }
+  __device__ __forceinline__ void store(u32x4_t* area, int lane) const {
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int r = k * R + lane / P;
+      area[r * P + slot(r, lane % P)] = v[k];
+    }
   }
 };
 
-template <>
-struct LmkRow<float> {
-  f32x4_t c[16];
-  __device__ __forceinline__ void load(const float* row) {
-    const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(row);
+// Exact sequential float64 dot product of row `lane` of the wave's LDS area with the query
+// landmark (float64, in LDS).
+__device__ __forceinline__ double row_dot(const u32x4_t* area, int lane, const double* lq_s, const bf16_t*) {
+  using S = RowStage<bf16_t>;
+  double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) c[k] = r4[k];
+  for (int k = 0; k < S::P; ++k) {
+    const u32x4_t c = area[lane * S::P + S::slot(lane, k)];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t pair = c[w];
+      const double lo = static_cast<double>(__uint_as_float(pair << 16));
+      const double hi = static_cast<double>(__uint_as_float(pair & 0xffff0000u));
+      acc = __builtin_fma(lq_s[8 * k + 2 * w], lo, acc);
+      acc = __builtin_fma(lq_s[8 * k + 2 * w + 1], hi, acc);
+    }
   }
-  __device__ __forceinline__ double dot(const double* lq_s) const {
-    double acc = 0.0;
+  return acc;
+}
+
+__device__ __forceinline__ double row_dot(const u32x4_t* area, int lane, const double* lq_s, const float*) {
+  using S = RowStage<float>;
+  double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+  for (int k = 0; k < S::P; ++k) {
+    const u32x4_t c = area[lane * S::P + S::slot(lane, k)];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc = __builtin_fma(lq_s[4 * k + w], static_cast<double>(c[k][w]), acc);
-    return acc;
+    for (int w = 0; w < 4; ++w) acc = __builtin_fma(lq_s[4 * k + w], static_cast<double>(__uint_as_float(c[w])), acc);
   }
-};
+  return acc;
+}
 
 constexpr int kMergeThreads = 1024;      // sixteen waves per merged row
 constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeBatch = 8;           // partial entries each merge thread loads at once
 
-// Merge the K-best lists of `nw` waves (lane k < K of wave w holds entry k) through LDS; wave 0
+// Merge the K-best lists of NWAVES waves (lane k < K of wave w holds entry k) through LDS; wave 0
 // returns the top K of the union, lane k holding entry k.  Every thread of the workgroup calls it.
-template <int KL>
-__device__ __forceinline__ void workgroup_topk(int nw, int K, uint64_t key, float sv, uint64_t* lkey, float* ls,
+template <int NWAVES>
+__device__ __forceinline__ void workgroup_topk(int K, uint64_t key, float sv, uint64_t* lkey, float* ls,
                                                uint64_t& out_key, float& out_s) {
+  constexpr int kPerLane = (NWAVES * kMaxTopk + 63) / 64;  // entries each lane of wave 0 takes
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane < K) {
     lkey[wave * K + lane] = key;
@@ -257,28 +278,32 @@ __device__ __forceinline__ void workgroup_topk(int nw, int K, uint64_t key, floa
   out_key = 0;
   out_s = 0.f;
   if (wave == 0) {
-    TopList<KL> L;
+    TopList<kPerLane> L;
     L.clear();
-    for (int e = lane; e < nw * K; e += 64)
+    for (int e = lane; e < NWAVES * K; e += 64)
       if (lkey[e] != 0) L.insert(lkey[e], ls[e]);
-    wave_topk<KL>(L, K, out_key, out_s);
+    wave_topk<kPerLane>(L, K, out_key, out_s);
   }
 }
 
-// One workgroup of NW waves per (row, block of 64 NW cpt candidates).  Lane c of the workgroup
-// scores the candidates j = block start + c + 64 NW n (n < cpt), so every pass reads 64 NW
-// consecutive key-landmark rows; the next row's load is issued before the current one is scored.
-// NW = 4 for a few long rows (a decode step over a long history: many blocks per row, their lists
-// merged by the workgroup and then by topk_merge); NW = 1 for many short rows (training: one wave
-// per row).  At most 128 VGPRs for bf16 landmarks and lists of 8 (four resident waves per SIMD,
-// enough loads in flight to stream a long history); fp32 rows and lists of 16 keep two.
-template <typename T, int KL, int NW>
-__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
+// One workgroup of NW waves per (row, block of 64 NW cpt candidates).  Pass n of wave w scores
+// the 64 consecutive candidates starting at block start + 64 (NW n + w), one per lane; the next
+// pass's rows are loaded while the current pass is scored.  NW = 4 for a few long rows (a decode
+// step over a long history: many blocks per row, their lists merged by the workgroup and then by
+// topk_merge); NW = 1 for many short rows (training: one wave per row).  At most 128 VGPRs for
+// bf16 landmarks and lists of 8 (four resident waves per SIMD, enough loads in flight to stream a
+// long history); fp32 rows and lists of 16 keep two.  Each lane's list holds LL = min(K, cpt)
+// entries (rounded up to a power of two).
+template <typename T, int LL, int NW>
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && LL <= 8) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
+  using Stage = RowStage<T>;
   constexpr int kBlockCand = 64 * NW;  // candidates of one block per pass (one per lane)
   __shared__ double lq_s[kDim];
+  __shared__ u32x4_t rows_s[NW][64 * Stage::P];
   __shared__ uint64_t lkey[NW * kMaxTopk];
   __shared__ float ls[NW * kMaxTopk];
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int64_t item = blockIdx.x;
   const int blk = static_cast<int>(item % p.nblk);
   const int64_t rowid = item / p.nblk;  // (g * B + b) * n_q + r
@@ -289,44 +314,48 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void 
   const int64_t i = p.base + r;
   const int64_t ncand = i < p.n_kv ? i : p.n_kv;
 
-  TopList<KL> L;
+  TopList<LL> L;
   L.clear();
   const T* lk = static_cast<const T*>(p.lk) + gb * p.n_kv * kDim;
-  const int64_t jb = static_cast<int64_t>(blk) * kBlockCand * p.cpt + threadIdx.x;
-  int mine = 0;  // candidates of this lane
-  if (jb < ncand) {
-    const int64_t m = (ncand - jb + kBlockCand - 1) / kBlockCand;
-    mine = m < p.cpt ? static_cast<int>(m) : p.cpt;
+  const int64_t jw = static_cast<int64_t>(blk) * kBlockCand * p.cpt + 64 * wave;  // first row, pass 0
+  int passes = 0;  // wave-uniform
+  if (jw < ncand) {
+    const int64_t m = (ncand - jw + kBlockCand - 1) / kBlockCand;
+    passes = m < p.cpt ? static_cast<int>(m) : p.cpt;
   }
-  LmkRow<T> cur, nxt;
-  if (mine > 0) cur.load(lk + jb * kDim);  // in flight while the query landmark is staged
+  Stage st;
+  if (passes > 0) st.load(lk, jw, ncand, lane);  // in flight while the query landmark is staged
   if (threadIdx.x < kDim) lq_s[threadIdx.x] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, threadIdx.x);
   __syncthreads();
 
-  for (int n = 0; n < mine; ++n) {
-    const int64_t j = jb + static_cast<int64_t>(n) * kBlockCand;
-    if (n + 1 < mine) nxt.load(lk + (j + kBlockCand) * kDim);
-    // an opaque zero offset keeps the query landmark in LDS (read per candidate) instead of in
-    // 128 registers hoisted out of the loop
-    int zero = 0;
-    asm volatile("" : "+v"(zero));
-    const double acc = cur.dot(lq_s + zero);
-    const float s = canon_zero(static_cast<float>(acc) * p.score_scale);
-    float rkey = s;
-    if (p.use_gumbel) {
+  u32x4_t* area = rows_s[wave];
+  for (int n = 0; n < passes; ++n) {
+    const int64_t j0 = jw + static_cast<int64_t>(n) * kBlockCand;
+    st.store(area, lane);
+    if (n + 1 < passes) st.load(lk, j0 + kBlockCand, ncand, lane);
+    const int64_t j = j0 + lane;
+    if (j < ncand) {
+      // an opaque zero offset keeps the query landmark in LDS (read per candidate) instead of in
+      // 128 registers hoisted out of the loop
+      int zero = 0;
+      asm volatile("" : "+v"(zero));
+      const double acc = row_dot(area, lane, lq_s + zero, static_cast<const T*>(nullptr));
+      const float s = canon_zero(static_cast<float>(acc) * p.score_scale);
+      float rkey = s;
+      if (p.use_gumbel) {
 #pragma clang fp contract(off)
-      const float noise = p.tau * gumbel(p.seed, g, b, i, j);
-      rkey = canon_zero(s + noise);
+        const float noise = p.tau * gumbel(p.seed, g, b, i, j);
+        rkey = canon_zero(s + noise);
+      }
+      L.insert(make_key(rkey, j), s);
     }
-    L.insert(make_key(rkey, j), s);
-    cur = nxt;
   }
 
   uint64_t key, bkey;
   float sv, bs;
-  wave_topk<KL>(L, p.K, key, sv);
+  wave_topk<LL>(L, p.K, key, sv);
   if constexpr (NW > 1) {
-    workgroup_topk<KL>(NW, p.K, key, sv, lkey, ls, bkey, bs);
+    workgroup_topk<NW>(p.K, key, sv, lkey, ls, bkey, bs);
   } else {
     bkey = key;
     bs = sv;
@@ -348,7 +377,9 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && KL <= 8) ? 4 : 2) void 
 
 // One workgroup of sixteen waves per long row merges the row's nblk partial top-K lists; each
 // thread loads its share of the entries in batches whose loads are in flight together.
-template <int KL>
+// Each thread takes entries threadIdx.x + kMergeThreads e of the row's partial lists and keeps the
+// best LL of them (LL = min(K, entries per thread), rounded up to a power of two).
+template <int LL>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(RetrieveParams p) {
   __shared__ uint64_t lkey[kMergeWaves * kMaxTopk];
   __shared__ float ls[kMergeWaves * kMaxTopk];
@@ -356,7 +387,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(RetrieveParam
   const int64_t n_in = static_cast<int64_t>(p.nblk) * p.K;
   const uint64_t* keys = p.part_key + rowid * n_in;
   const float* svals = p.part_s + rowid * n_in;
-  TopList<KL> L;
+  TopList<LL> L;
   L.clear();
   for (int64_t c0 = threadIdx.x; c0 < n_in; c0 += static_cast<int64_t>(kMergeThreads) * kMergeBatch) {
     uint64_t kb[kMergeBatch];
@@ -373,39 +404,57 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(RetrieveParam
   }
   uint64_t key, bkey;
   float sv, bs;
-  wave_topk<KL>(L, p.K, key, sv);
-  workgroup_topk<KL>(kMergeWaves, p.K, key, sv, lkey, ls, bkey, bs);
+  wave_topk<LL>(L, p.K, key, sv);
+  workgroup_topk<kMergeWaves>(p.K, key, sv, lkey, ls, bkey, bs);
   if (threadIdx.x < p.K) {
     p.idx[rowid * p.K + threadIdx.x] = key_index(bkey);
     p.score[rowid * p.K + threadIdx.x] = bkey == 0 ? -__builtin_inff() : bs;
   }
 }
 
-}  // namespace
+// Entries each lane's list needs: min(K, what the lane sees), as a power of two of at most 16.
+int list_len(int K, int64_t per_lane) {
+  const int cap = K <= 8 ? 8 : 16;
+  int l = 1;
+  while (l < per_lane && l < cap) l *= 2;
+  return l;
+}
 
-template <int NW>
-void launch_score_topk_nw(const RetrieveParams& p, bool f32, hipStream_t s) {
+template <typename T, int NW>
+void launch_scan(const RetrieveParams& p, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.n_q * p.nblk)), block(64 * NW);
-  const bool small = p.K <= 8;
-  if (f32) {
-    if (small) hipLaunchKernelGGL((score_topk_kernel<float, 8, NW>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((score_topk_kernel<float, 16, NW>), grid, block, 0, s, p);
-  } else {
-    if (small) hipLaunchKernelGGL((score_topk_kernel<bf16_t, 8, NW>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((score_topk_kernel<bf16_t, 16, NW>), grid, block, 0, s, p);
+  switch (list_len(p.K, p.cpt)) {
+    case 1: hipLaunchKernelGGL((score_topk_kernel<T, 1, NW>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((score_topk_kernel<T, 2, NW>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((score_topk_kernel<T, 4, NW>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((score_topk_kernel<T, 8, NW>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((score_topk_kernel<T, 16, NW>), grid, block, 0, s, p); break;
   }
 }
 
+}  // namespace
+
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s) {
-  if (p.nw == 1) launch_score_topk_nw<1>(p, f32, s);
-  else launch_score_topk_nw<4>(p, f32, s);
+  if (f32) {
+    if (p.nw == 1) launch_scan<float, 1>(p, s);
+    else launch_scan<float, 4>(p, s);
+  } else {
+    if (p.nw == 1) launch_scan<bf16_t, 1>(p, s);
+    else launch_scan<bf16_t, 4>(p, s);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s) {
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.n_q));
-  if (p.K <= 8) hipLaunchKernelGGL((topk_merge_kernel<8>), grid, dim3(kMergeThreads), 0, s, p);
-  else hipLaunchKernelGGL((topk_merge_kernel<16>), grid, dim3(kMergeThreads), 0, s, p);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.n_q)), block(kMergeThreads);
+  const int64_t n_in = static_cast<int64_t>(p.nblk) * p.K;
+  switch (list_len(p.K, (n_in + kMergeThreads - 1) / kMergeThreads)) {
+    case 1: hipLaunchKernelGGL((topk_merge_kernel<1>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((topk_merge_kernel<2>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((topk_merge_kernel<4>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((topk_merge_kernel<8>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((topk_merge_kernel<16>), grid, block, 0, s, p); break;
+  }
   return hipGetLastError();
 }
 
