@@ -96,13 +96,15 @@ struct QTileCoord {
   int64_t gbh;  // (g * B + b) * H + h
 };
 
+// Group fastest, then query chunk: both groups' tiles of one (batch row, head) and chunk run side
+// by side and share each K/V tile while it is in L2.
 __device__ __forceinline__ QTileCoord query_tile_coord(const AttendParams& p) {
   const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
   QTileCoord c;
-  c.t = lid % p.n_q;
-  int64_t rest = lid / p.n_q;
-  c.g = static_cast<int>(rest % p.G);
-  rest /= p.G;
+  c.g = static_cast<int>(lid % p.G);
+  int64_t rest = lid / p.G;
+  c.t = rest % p.n_q;
+  rest /= p.n_q;
   c.h = static_cast<int>(rest % p.H);
   c.b = static_cast<int>(rest / p.H);
   c.gbh = (static_cast<int64_t>(c.g) * p.B + c.b) * p.H + c.h;
