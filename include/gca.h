@@ -154,6 +154,25 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
                         size_t ws_bytes, void* stream);
 
 /*
+ * Fetch of retrieved chunks [Notes, Key designs: memory-offload inference]: the K/V of past
+ * chunks may be kept in host memory, and the chunks a retrieval selects are loaded back to the
+ * device before the next chunk attends to them.  For every retrieval slot (g, b, r, k) whose
+ * chunk j = idx[g,b,r,k] satisfies 0 <= j < n_kv, and every head h, the tiles k[b,h,j] and
+ * v[b,h,j] are copied to k_out[b,h,c] and v_out[b,h,c] with c = (g * n_q + r) * K + k, and
+ * idx_out[g,b,r,k] = c; idx_out is -1 for the other slots, whose output tiles are left as they
+ * were.  gca_forward over (k_out, v_out, idx_out) with n_kv_chunks = G * n_q * K then computes
+ * exactly what it computes over (k, v, idx).
+ * k, v [B,H,n_kv,64,64] (problem->dtype): device memory, or pinned host memory from hipHostMalloc
+ * (read through its device mapping, so every byte crosses the host link); pageable host memory
+ * is refused with GCA_ERR_INVALID_ARGUMENT.  idx [G,B,n_q,K]: device input.  k_out, v_out
+ * [B,H,G*n_q*K,64,64] and idx_out [G,B,n_q,K]: device outputs.
+ * Uses n_q_chunks, n_kv_chunks, B, G, H, topk, dtype of problem.
+ */
+gca_status gca_fetch_chunks(const gca_problem* problem, const int32_t* idx, const void* k,
+                            const void* v, void* k_out, void* v_out, int32_t* idx_out,
+                            void* stream);
+
+/*
  * Landmark gradients [Notes, Key designs: GCA; Key designs: causal retrieval]: the scores weight
  * the fused outputs, so the loss differentiates them, and a score relates the landmark of chunk i
  * to the landmark of an earlier chunk j; this carries d(score) on to both landmarks.  With

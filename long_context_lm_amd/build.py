@@ -16,7 +16,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/retrieve.hip", "csrc/attend.hip", "csrc/landmark.hip", "csrc/gca_api.hip"]
+SOURCES = ["csrc/retrieve.hip", "csrc/attend.hip", "csrc/landmark.hip", "csrc/fetch.hip", "csrc/gca_api.hip"]
 # Per-file device flags.  The attention kernels never produce or test NaN (inputs are finite,
 # masked values are -inf), so fmax needs no NaN quieting there; infinities stay honoured.  The
 # retrieval kernels keep strict IEEE semantics for their bit-exact scores.

@@ -14,7 +14,7 @@ namespace gca {
 const char* kernel_name(int id) {
   static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
-                                           "lmk_key_grad"};
+                                           "lmk_key_grad", "fetch_chunks"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -399,6 +399,62 @@ gca_status gca_landmark_backward(const gca_problem* problem, const void* lq, con
   if (any) GCA_TRY(launch(kLmkQueryGrad, s, [&] { return launch_lmk_query_grad(m, f32, s); }));
   if (kv) GCA_TRY(launch(kLmkKeyGrad, s, [&] { return launch_lmk_key_grad(m, f32, s); }));
   return GCA_OK;
+}
+
+// The device address of a K/V source: device memory as it is; pinned host memory (hipHostMalloc)
+// through its mapping into the device's address space.  Pageable host memory, which a kernel
+// cannot read, is refused.
+static gca_status device_address(const void* ptr, const void** out) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return GCA_ERR_INVALID_ARGUMENT;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = ptr;
+    return GCA_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    *out = attr.devicePointer;
+    return GCA_OK;
+  }
+  return GCA_ERR_INVALID_ARGUMENT;
+}
+
+gca_status gca_fetch_chunks(const gca_problem* problem, const int32_t* idx, const void* k, const void* v,
+                            void* k_out, void* v_out, int32_t* idx_out, void* stream) {
+  GCA_TRY(validate_problem(problem));
+  const gca_problem* p = problem;
+  const bool any = p->n_q_chunks > 0;
+  const bool kv = any && p->n_kv_chunks > 0;
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(idx_out, any, 4));
+  GCA_TRY(check_tensor(k, kv, 16));
+  GCA_TRY(check_tensor(v, kv, 16));
+  GCA_TRY(check_tensor(k_out, any, 16));
+  GCA_TRY(check_tensor(v_out, any, 16));
+  if (!any) return GCA_OK;
+  FetchParams f{};
+  f.idx = idx;
+  f.k = k;
+  f.v = v;
+  if (kv) {
+    GCA_TRY(device_address(k, &f.k));
+    GCA_TRY(device_address(v, &f.v));
+  }
+  f.k_out = k_out;
+  f.v_out = v_out;
+  f.idx_out = idx_out;
+  f.n_q = p->n_q_chunks;
+  f.n_kv = p->n_kv_chunks;
+  f.n_c = static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk;
+  f.G = p->G;
+  f.B = p->B;
+  f.H = p->H;
+  f.K = p->topk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = p->dtype == GCA_F32;
+  return launch(kFetchChunks, s, [&] { return launch_fetch_chunks(f, f32, s); });
 }
 
 const char* gca_status_string(gca_status status) {

@@ -17,6 +17,7 @@ enum KernelId {
   kScoreGrad,
   kLmkQueryGrad,
   kLmkKeyGrad,
+  kFetchChunks,
   kNumKernels
 };
 const char* kernel_name(int id);
@@ -80,6 +81,17 @@ struct LandmarkParams {
   float score_scale;
 };
 
+struct FetchParams {
+  const int32_t* idx;
+  const void* k;        // [B, H, n_kv, 64, 64] device-visible address (device or pinned host memory)
+  const void* v;
+  void* k_out;          // [B, H, n_c, 64, 64], n_c = G n_q K
+  void* v_out;
+  int32_t* idx_out;     // [G, B, n_q, K]
+  int64_t n_q, n_kv, n_c;
+  int32_t G, B, H, K;
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s);
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s);
@@ -90,5 +102,6 @@ hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_score_grad(const AttendParams& p, hipStream_t s);
 hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);
+hipError_t launch_fetch_chunks(const FetchParams& p, bool f32, hipStream_t s);
 
 }  // namespace gca

@@ -8,6 +8,7 @@ fallback: if the library is missing or a call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import math
 import os
 from dataclasses import dataclass
@@ -83,6 +84,7 @@ def load() -> ctypes.CDLL:
     lib.gca_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_landmark_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gca_fetch_chunks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
@@ -233,6 +235,30 @@ def landmark_backward(cfg: Config, lq, lk, idx, dscore, ws=None, out=None):
                                                                  _ptr(dscore), _ptr(dlq), _ptr(dlk), _ptr(ws), n,
                                                                  _stream()))
     return dlq, dlk
+
+
+def fetched_config(cfg: Config) -> Config:
+    """The problem over the chunks gca_fetch_chunks gathered: n_kv = G * n_q * K."""
+    return dataclasses.replace(cfg, n_kv=cfg.G * cfg.n_q * cfg.topk)
+
+
+def fetch_chunks(cfg: Config, idx, k, v, out=None):
+    """gca_fetch_chunks: returns (k_out, v_out [B,H,G*n_q*K*64,64] on idx's device, idx_out).
+
+    k, v may be device tensors or pinned host tensors (torch pin_memory)."""
+    import torch
+
+    n_c = cfg.G * cfg.n_q * cfg.topk
+    dev = idx.device
+    if out is None:
+        shape = (cfg.B, cfg.H, n_c * 64, 64)
+        out = (torch.empty(shape, dtype=k.dtype, device=dev), torch.empty(shape, dtype=v.dtype, device=dev),
+               torch.empty_like(idx))
+    k_out, v_out, idx_out = out
+    prob = cfg.problem()
+    _check("gca_fetch_chunks", load().gca_fetch_chunks(ctypes.byref(prob), _ptr(idx), _ptr(k), _ptr(v), _ptr(k_out),
+                                                       _ptr(v_out), _ptr(idx_out), _stream()))
+    return k_out, v_out, idx_out
 
 
 def profile_enable(on: bool = True):

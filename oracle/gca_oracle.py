@@ -347,3 +347,38 @@ def landmark_backward(lq, lk, idx, dscore, *, score_scale=0.125, q_chunk_base=0,
                         dlq[g, b, r] += dscore[g, b, r, kk] * lk[g, b, j]
                         dlk[g, b, j] += dscore[g, b, r, kk] * lq[g, b, r]
     return scale * dlq, scale * dlk
+
+
+def fetch_chunks(idx, k, v, n_kv=None):
+    """The retrieved chunks' K/V tiles, gathered for the chunk that attends to them.
+
+    In inference the K/V of past chunks may be kept in host memory and the chunks a retrieval
+    selects are loaded back before the next chunk attends to them [Notes, Key designs:
+    memory-offload inference].  k, v [B, H, n_kv*64, d]; idx [G, B, n_q, K].  Slot (g, b, r, s)
+    with 0 <= j = idx[g,b,r,s] < n_kv gets compact chunk c = (g*n_q + r)*K + s:
+      k_out[b, h, c] = k[b, h, j],  v_out[b, h, c] = v[b, h, j],  idx_out[g, b, r, s] = c,
+    and idx_out = -1 elsewhere (those tiles stay zero).  Returns (k_out, v_out, idx_out) with
+    k_out, v_out [B, H, G*n_q*K*64, d] in the input dtype and idx_out int32.
+    """
+    k = np.asarray(k)
+    v = np.asarray(v)
+    G, B, n_q, K = idx.shape
+    _, H, L, d = k.shape
+    if n_kv is None:
+        n_kv = L // CHUNK
+    n_c = G * n_q * K
+    k_out = np.zeros((B, H, n_c * CHUNK, d), dtype=k.dtype)
+    v_out = np.zeros((B, H, n_c * CHUNK, d), dtype=v.dtype)
+    idx_out = np.full(idx.shape, -1, dtype=np.int32)
+    for g in range(G):
+        for b in range(B):
+            for r in range(n_q):
+                for s in range(K):
+                    j = int(idx[g, b, r, s])
+                    if not 0 <= j < n_kv:
+                        continue
+                    c = (g * n_q + r) * K + s
+                    idx_out[g, b, r, s] = c
+                    k_out[b, :, c * CHUNK:(c + 1) * CHUNK] = k[b, :, j * CHUNK:(j + 1) * CHUNK]
+                    v_out[b, :, c * CHUNK:(c + 1) * CHUNK] = v[b, :, j * CHUNK:(j + 1) * CHUNK]
+    return k_out, v_out, idx_out

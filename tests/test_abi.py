@@ -90,6 +90,7 @@ def test_problem_validation(field, value, status):
     assert lib.gca_forward(ctypes.byref(p), z, z, z, z, z, z, z, None, 0, None) == status
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, None, 0, None) == status
     assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, None, 0, None) == status
+    assert lib.gca_fetch_chunks(ctypes.byref(p), z, z, z, z, z, z, None) == status
 
 
 def test_null_problem_and_bad_op():
@@ -156,6 +157,13 @@ def test_pointer_checks():
                                      None) == MISALIGNED
     assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, z, need - 1, None) == WS_SMALL
     assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, None, need, None) == INVALID
+    # fetch of retrieved chunks: null and misaligned tensors are refused before any HIP call
+    assert lib.gca_fetch_chunks(ctypes.byref(p), None, z, z, z, z, z, None) == INVALID
+    assert lib.gca_fetch_chunks(ctypes.byref(p), z, None, z, z, z, z, None) == INVALID
+    assert lib.gca_fetch_chunks(ctypes.byref(p), z, z, z, z, z, None, None) == INVALID
+    assert lib.gca_fetch_chunks(ctypes.byref(p), z, mis, z, z, z, z, None) == MISALIGNED
+    assert lib.gca_fetch_chunks(ctypes.byref(p), z, z, z, z, mis, z, None) == MISALIGNED
+    assert lib.gca_fetch_chunks(ctypes.byref(p), ctypes.c_void_p(FAKE + 2), z, z, z, z, z, None) == MISALIGNED
     # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
     big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED
@@ -169,6 +177,9 @@ def test_empty_problem_is_a_noop_without_gpu():
     p = good(n_q_chunks=0, n_kv_chunks=0)
     assert lib.gca_backward(ctypes.byref(p), *([None] * 11), None, 0, None) == OK
     assert lib.gca_landmark_backward(ctypes.byref(p), *([None] * 6), None, 0, None) == OK
+    assert lib.gca_fetch_chunks(ctypes.byref(p), *([None] * 6), None) == OK
+    p = good(n_q_chunks=0)  # no rows: nothing to fetch, even from a history
+    assert lib.gca_fetch_chunks(ctypes.byref(p), *([None] * 6), None) == OK
 
 
 def test_status_strings_and_error_state():

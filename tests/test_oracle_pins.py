@@ -488,3 +488,40 @@ def test_landmark_backward_chains_with_gca_backward():
     dlq, dlk = O.landmark_backward(x["lq"], x["lk"], idx, ds)
     np.testing.assert_allclose(dlq, lq_t.grad.numpy(), rtol=1e-9, atol=1e-11)
     np.testing.assert_allclose(dlk, lk_t.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+# ------------------------------------------------------------------ fetch of retrieved chunks
+def test_fetch_chunks_preserves_attention():
+    """Attending over the fetched tiles with the remapped index is attending over the history."""
+    shp, x, idx, sc = _small_case(seed=7, n=9, K=3)
+    o, lse = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=1)
+    k_c, v_c, idx_c = O.fetch_chunks(idx, x["k"], x["v"])
+    o2, lse2 = O.forward(x["q"], k_c, v_c, idx_c, sc, shift=1)
+    assert np.array_equal(o2, o)
+    assert np.array_equal(lse2, lse)
+
+
+def test_fetch_chunks_tiles_and_codes():
+    rng = np.random.default_rng(3)
+    G, B, H, n_q, K, n_kv, d = 2, 2, 3, 4, 3, 6, 8
+    k = rng.standard_normal((B, H, n_kv * 64, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, n_kv * 64, d)).astype(np.float32)
+    idx = rng.integers(-2, n_kv + 2, size=(G, B, n_q, K)).astype(np.int32)  # some out of range
+    idx[0, 0, 0, :] = [2, 2, 5]  # the same chunk in two slots
+    k_c, v_c, idx_c = O.fetch_chunks(idx, k, v)
+    assert k_c.shape == (B, H, G * n_q * K * 64, d) and k_c.dtype == k.dtype
+    valid = (idx >= 0) & (idx < n_kv)
+    assert np.array_equal(idx_c >= 0, valid)
+    codes = idx_c[valid]
+    assert codes.min() >= 0 and codes.max() < G * n_q * K
+    for g, b in np.ndindex(G, B):
+        assert len(set(idx_c[g, b][valid[g, b]].tolist())) == int(valid[g, b].sum())
+    for g, b, r, s in np.ndindex(G, B, n_q, K):
+        c = (g * n_q + r) * K + s
+        tk, tv = k_c[b, :, 64 * c:64 * c + 64], v_c[b, :, 64 * c:64 * c + 64]
+        if valid[g, b, r, s]:
+            j = idx[g, b, r, s]
+            assert idx_c[g, b, r, s] == c
+            assert np.array_equal(tk, k[b, :, 64 * j:64 * j + 64]) and np.array_equal(tv, v[b, :, 64 * j:64 * j + 64])
+        else:
+            assert not tk.any() and not tv.any()
