@@ -260,6 +260,107 @@ def inference_latency(shape, iters=50):
     return res
 
 
+def offload_latency(shape, iters=50):
+    """Per-chunk latency with the K/V history in pinned host memory (the pages' memory-offload
+    inference): retrieve over the device-resident landmarks, fetch the retrieved tiles over the
+    host link (gca_fetch_chunks), attend to the fetched tiles."""
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    cfg = gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                     dtype="bf16", q_chunk_base=shape.q_chunk_base, shift=shape.shift)
+    fcfg = gca.fetched_config(cfg)
+    host = I.make_inputs(shape, "bf16", seed=0, names=("lq", "lk", "q"))
+    lq, lk, q = (host[n].cuda() for n in ("lq", "lk", "q"))
+    # K/V history in pinned host memory (hipHostMalloc of the exact size: torch's caching pinned
+    # allocator rounds a 25.8 GB request up to 32 GiB and keeps it), filled by repeating a seeded
+    # 32 MiB random block
+    import ctypes
+
+    import numpy as np
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    blk = torch.randn(1 << 24, generator=torch.Generator().manual_seed(1234)).to(torch.bfloat16)
+    kv, ptrs = [], []
+    numel = 1
+    for dim in shape.tensor_shape("k"):
+        numel *= dim
+    for _ in range(2):
+        ptr = ctypes.c_void_p()
+        if hip.hipHostMalloc(ctypes.byref(ptr), ctypes.c_size_t(2 * numel), ctypes.c_uint(0)) != 0:
+            raise RuntimeError(f"hipHostMalloc of {2 * numel} bytes failed")
+        ptrs.append(ptr)
+        raw = np.ctypeslib.as_array((ctypes.c_int16 * numel).from_address(ptr.value))
+        t = torch.from_numpy(raw).view(torch.bfloat16).view(shape.tensor_shape("k"))
+        flat = t.view(-1)
+        for i in range(0, flat.numel(), blk.numel()):
+            n = min(blk.numel(), flat.numel() - i)
+            flat[i:i + n].copy_(blk[:n])
+        kv.append(t)
+    k, v = kv
+    idx = torch.empty((shape.G, shape.B, shape.n_q, shape.topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty_like(idx, dtype=torch.float32)
+    n_c = fcfg.n_kv
+    k_c = torch.empty((shape.B, shape.H, n_c * 64, 64), dtype=torch.bfloat16, device="cuda")
+    v_c = torch.empty_like(k_c)
+    idx_c = torch.empty_like(idx)
+    o = torch.empty_like(q)
+    nws = gca.workspace_size(gca.OP_RETRIEVE, cfg)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device="cuda")
+
+    def one():
+        gca.retrieve(cfg, lq, lk, idx, sc, ws=ws if nws else None)
+        gca.fetch_chunks(cfg, idx, k, v, out=(k_c, v_c, idx_c))
+        gca.forward(fcfg, q, k_c, v_c, idx_c, sc, need_lse=False, o=o)
+
+    for _ in range(5):
+        one()
+    torch.cuda.synchronize()
+    res = {}
+    gca.profile_collect()
+    gca.profile_enable(True)
+    for _ in range(iters):
+        one()
+    torch.cuda.synchronize()
+    gca.profile_enable(False)
+    res["kernels_us"] = {kk: vv[0] / vv[1] * 1e3 for kk, vv in gca.profile_collect().items()}
+    for mode in ("warm", "cold"):
+        times = []
+        for _ in range(iters):
+            if mode == "cold":
+                flush.max()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            one()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        times.sort()
+        res[mode] = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
+                     "p90_us": times[(9 * len(times)) // 10]}
+    # the host link's rate for a plain 1 GiB DMA copy out of the same pinned history
+    dst = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(k.view(-1)[: 1 << 29], non_blocking=True)
+    a.record()
+    dst.copy_(k.view(-1)[: 1 << 29], non_blocking=True)
+    b.record()
+    b.synchronize()
+    res["host_link_copy_gbs"] = (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+    res["host_link_bytes"] = shape.G * shape.B * shape.n_q * shape.topk * shape.H * 2 * 64 * 64 * 2
+    res["host_link_bound_us"] = res["host_link_bytes"] / (res["host_link_copy_gbs"] * 1e9) * 1e6
+    res["hbm_bytes"] = shape.G * shape.B * shape.n_kv * 64 * 2 + 2 * res["host_link_bytes"]
+    torch.cuda.synchronize()
+    del k, v, kv, t, flat, raw, flush, dst
+    for ptr in ptrs:
+        hip.hipHostFree(ptr)
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +452,13 @@ def main():
             log(f"  {label}: warm {infer[label]['warm']['median_us']:.1f} us, "
                 f"cold {infer[label]['cold']['median_us']:.1f} us; graph replay warm "
                 f"{infer[label]['graph_warm']['median_us']:.1f} us, cold {infer[label]['graph_cold']['median_us']:.1f} us")
+        for label, shp in (("1M_host_kv", I.INFER_1M), ("16M_host_kv", I.INFER_16M)):
+            log("inference latency, K/V history in pinned host memory", label)
+            r = offload_latency(shp)
+            infer[label] = r
+            log(f"  {label}: warm {r['warm']['median_us']:.1f} us, cold {r['cold']['median_us']:.1f} us; fetch "
+                f"{r['kernels_us'].get('fetch_chunks', 0):.1f} us for {r['host_link_bytes'] / 2**20:.1f} MiB "
+                f"(host-link copy rate {r['host_link_copy_gbs']:.1f} GB/s -> bound {r['host_link_bound_us']:.1f} us)")
 
     out = {
         "metric": METRIC,

@@ -29,7 +29,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/attend.hip", "csrc/retrieve.hip", "csrc/gca_device.hpp", "csrc/gca_internal.hpp"]
 SHORT = ["score_topk", "topk_merge", "attend_fwd", "inverse_index", "bwd_query", "bwd_key", "score_grad",
-         "lmk_query_grad", "lmk_key_grad"]
+         "lmk_query_grad", "lmk_key_grad", "fetch_chunks"]
 COPY_BYTES = 1 << 30
 
 
@@ -109,7 +109,7 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
     groups = {}
     for r in _rows(directory, "kernel_trace.csv"):
         s = short_name(r["Kernel_Name"])
-        if s not in ("score_topk", "topk_merge", "attend_fwd"):
+        if s not in ("score_topk", "topk_merge", "attend_fwd", "fetch_chunks"):
             continue
         wg = int(r["Workgroup_Size_X"])
         blocks = int(r["Grid_Size_X"]) // wg
@@ -119,7 +119,8 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
     inf = res.get("inference_latency") or {}
     # launch shapes of the decode steps (G = 2 rows of one batch row, H = 12, K = 8)
     shapes = {("score_topk", 128, 256): "1M scan (2 rows x 64 blocks)", ("topk_merge", 2, 1024): "1M / 16M merge",
-              ("score_topk", 1024, 256): "16M scan (2 rows x 512 blocks)", ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)"}
+              ("score_topk", 1024, 256): "16M scan (2 rows x 512 blocks)", ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)",
+              ("fetch_chunks", 192, 256): "host-memory K/V fetch (2 groups x 8 slots x 12 heads, 3 MiB)"}
     lines = [
         "# Kernel durations: one decode step over a 1M- / 16M-token history (retrieve + attend)",
         "",
@@ -144,9 +145,12 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
               "line carries the reported latencies):", "",
               "| history | warm median (us) | cold median (us) | graph replay warm (us) | graph replay cold (us) |",
               "|---|---|---|---|---|"]
+    def cell(v, mode):
+        return f"{v[mode]['median_us']:.1f}" if mode in v else "-"
+
     for label, v in inf.items():
-        lines.append(f"| {label} | {v['warm']['median_us']:.1f} | {v['cold']['median_us']:.1f} | "
-                     f"{v['graph_warm']['median_us']:.1f} | {v['graph_cold']['median_us']:.1f} |")
+        lines.append(f"| {label} | {cell(v, 'warm')} | {cell(v, 'cold')} | {cell(v, 'graph_warm')} | "
+                     f"{cell(v, 'graph_cold')} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
