@@ -154,6 +154,24 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
                         size_t ws_bytes, void* stream);
 
 /*
+ * Token-level decode [Notes, Key designs: GCA; Key designs: memory-offload inference]: while the
+ * tokens of a query chunk are generated one at a time, every new token attends to the chunks
+ * retrieved once for the chunk (one retrieval serves its S tokens).  For the call's single query
+ * chunk (n_q_chunks must be 1; it uses retrieval row 0 - shift, so shift = 1 gives zeros) and its
+ * first n_tokens tokens (1 <= n_tokens <= 64), o equals the first n_tokens rows of gca_forward's
+ * output for that chunk:
+ *   o[g,b,h,u,:] = sum_k w_k softmax_j(attn_scale q[g,b,h,u,:] . k_jk[j,:]) v_jk
+ * with w the softmax over the valid slots of score[g,b,0,:].
+ * q, o [G,B,H,n_tokens,64] (problem->dtype); k, v [B,H,n_kv,64,64]; idx, score [G,B,1,K]; all
+ * device memory (k, v may also be the compact buffers of gca_fetch_chunks, with n_kv = G * K).
+ * Arithmetic in fp32; no workspace.  Errors: GCA_ERR_INVALID_ARGUMENT if n_q_chunks != 1 or
+ * n_tokens is out of range.
+ */
+gca_status gca_decode_tokens(const gca_problem* problem, int32_t n_tokens, const void* q,
+                             const void* k, const void* v, const int32_t* idx, const float* score,
+                             void* o, void* stream);
+
+/*
  * Fetch of retrieved chunks [Notes, Key designs: memory-offload inference]: the K/V of past
  * chunks may be kept in host memory, and the chunks a retrieval selects are loaded back to the
  * device before the next chunk attends to them.  For every retrieval slot (g, b, r, k) whose

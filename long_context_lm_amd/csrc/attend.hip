@@ -651,6 +651,97 @@ __global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(Atte
   }
 }
 
+// ------------------------------------------------------------- token-level decode
+// While the tokens of a query chunk are generated one at a time, each new token attends to the
+// chunks retrieved once for the chunk's row: one retrieval serves all S tokens of the chunk.  For
+// one to a few query tokens the products are matrix-vector sized, so they run on the vector units:
+// one workgroup per (group, batch row, head), one wave per retrieval slot (slots k, k + 8, ...),
+// lane u holding key u's row for the scores and lane d holding column d of V for P V.  Each slot's
+// output, already scaled by w_k / l_k, goes to LDS; the fused output sums the valid slots in slot
+// order.  Tokens are processed kDecodeBatch at a time.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeBatch = 4;
+
+template <typename T>
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_tokens_kernel(AttendParams p, int32_t n_tok) {
+  __shared__ float q_s[kDecodeBatch][kDim];
+  __shared__ float p_s[kDecodeWaves][kChunk];
+  __shared__ float o_s[kMaxTopk][kDecodeBatch][kDim];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t gbh = blockIdx.x;  // (g B + b) H + h
+  const int h = static_cast<int>(gbh % p.H);
+  const int64_t gb = gbh / p.H;
+  const int b = static_cast<int>(gb % p.B);
+  const int64_t row = -static_cast<int64_t>(p.shift);  // the call's single query chunk is chunk 0
+  const bool has_row = row >= 0;
+  const int64_t rowbase = (gb * p.n_q + (has_row ? row : 0)) * p.K;
+  const T* q = static_cast<const T*>(p.q) + gbh * static_cast<int64_t>(n_tok) * kDim;
+  T* o = static_cast<T*>(p.o) + gbh * static_cast<int64_t>(n_tok) * kDim;
+  const int rounds = (p.K + kDecodeWaves - 1) / kDecodeWaves;
+  uint32_t vmask = 0;  // valid slots of the row (wave-uniform, the same in every wave)
+  if (has_row) {
+    bool v0;
+    int32_t j0;
+    (void)wave_slot_weight(p, rowbase, lane, 0, v0, j0, vmask);
+  }
+
+  for (int t0 = 0; t0 < n_tok; t0 += kDecodeBatch) {  // uniform over the workgroup
+    const int nb = n_tok - t0 < kDecodeBatch ? n_tok - t0 : kDecodeBatch;
+    if (tid < kDecodeBatch * kDim) {
+      const int t = tid / kDim, d = tid % kDim;
+      q_s[t][d] = t < nb ? to_f32(q[(t0 + t) * kDim + d]) : 0.f;
+    }
+    __syncthreads();
+    for (int rd = 0; rd < rounds; ++rd) {  // uniform
+      const int k = rd * kDecodeWaves + wave;
+      bool valid = false;
+      int32_t j = -1;
+      uint32_t vm_k = 0;
+      float w = 0.f;
+      if (has_row && k < p.K) w = wave_slot_weight(p, rowbase, lane, k, valid, j, vm_k);
+      if (!valid) continue;  // wave-uniform
+      const T* kt = kv_tile<T>(p.k, p, b, h, j);
+      const T* vt = kv_tile<T>(p.v, p, b, h, j);
+      float krow[kDim], vcol[kChunk];
+#pragma unroll
+      for (int d = 0; d < kDim; ++d) krow[d] = to_f32(kt[lane * kDim + d]);
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) vcol[u] = to_f32(vt[u * kDim + lane]);
+      for (int t = 0; t < nb; ++t) {
+        float z = 0.f;
+#pragma unroll
+        for (int d = 0; d < kDim; ++d) z = __builtin_fmaf(q_s[t][d], krow[d], z);
+        z *= p.attn_scale;
+        float mx = z;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const float e = expf(z - mx);
+        float l = e;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+        p_s[wave][lane] = e * (w / l);
+        __builtin_amdgcn_wave_barrier();
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) acc = __builtin_fmaf(p_s[wave][u], vcol[u], acc);
+        o_s[k][t][lane] = acc;
+        __builtin_amdgcn_wave_barrier();  // p_s is rewritten for the next token
+      }
+    }
+    __syncthreads();
+    if (tid < kDecodeBatch * kDim) {
+      const int t = tid / kDim, d = tid % kDim;
+      if (t < nb) {
+        float acc = 0.f;
+        for (int k = 0; k < p.K; ++k)
+          if ((vmask >> k) & 1u) acc += o_s[k][t][d];
+        from_f32(o + (t0 + t) * kDim + d, acc);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------- backward, query-major (dQ)
 // Sum over the 32 queries of a wave of a per-query value (lanes l and l ^ 32 hold the same
 // query): DPP steps within each 16-lane row, then the row pair.  Fixed order: deterministic.
@@ -1093,6 +1184,13 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
     if (p.lse) hipLaunchKernelGGL((attend_fwd_wave_kernel<true>), grid, dim3(64), 0, s, p);
     else hipLaunchKernelGGL((attend_fwd_wave_kernel<false>), grid, dim3(64), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.H)), block(64 * kDecodeWaves);
+  if (f32) hipLaunchKernelGGL(decode_tokens_kernel<float>, grid, block, 0, s, p, n_tok);
+  else hipLaunchKernelGGL(decode_tokens_kernel<bf16_t>, grid, block, 0, s, p, n_tok);
   return hipGetLastError();
 }
 

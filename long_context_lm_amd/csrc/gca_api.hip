@@ -14,7 +14,7 @@ namespace gca {
 const char* kernel_name(int id) {
   static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
-                                           "lmk_key_grad", "fetch_chunks"};
+                                           "lmk_key_grad", "fetch_chunks", "decode_tokens"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -399,6 +399,30 @@ gca_status gca_landmark_backward(const gca_problem* problem, const void* lq, con
   if (any) GCA_TRY(launch(kLmkQueryGrad, s, [&] { return launch_lmk_query_grad(m, f32, s); }));
   if (kv) GCA_TRY(launch(kLmkKeyGrad, s, [&] { return launch_lmk_key_grad(m, f32, s); }));
   return GCA_OK;
+}
+
+gca_status gca_decode_tokens(const gca_problem* problem, int32_t n_tokens, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const float* score, void* o, void* stream) {
+  GCA_TRY(validate_problem(problem));
+  const gca_problem* p = problem;
+  if (p->n_q_chunks != 1 || n_tokens < 1 || n_tokens > p->S) return GCA_ERR_INVALID_ARGUMENT;
+  const bool kv = p->n_kv_chunks > 0;
+  GCA_TRY(check_tensor(q, true, 16));
+  GCA_TRY(check_tensor(k, kv, 16));
+  GCA_TRY(check_tensor(v, kv, 16));
+  GCA_TRY(check_tensor(idx, true, 4));
+  GCA_TRY(check_tensor(score, true, 4));
+  GCA_TRY(check_tensor(o, true, 16));
+  AttendParams a = attend_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.score = score;
+  a.o = o;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = p->dtype == GCA_F32;
+  return launch(kDecodeTokens, s, [&] { return launch_decode_tokens(a, n_tokens, f32, s); });
 }
 
 // The device address of a K/V source: device memory as it is; pinned host memory (hipHostMalloc)

@@ -18,6 +18,7 @@ enum KernelId {
   kLmkQueryGrad,
   kLmkKeyGrad,
   kFetchChunks,
+  kDecodeTokens,
   kNumKernels
 };
 const char* kernel_name(int id);
@@ -103,5 +104,6 @@ hipError_t launch_score_grad(const AttendParams& p, hipStream_t s);
 hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_fetch_chunks(const FetchParams& p, bool f32, hipStream_t s);
+hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, hipStream_t s);
 
 }  // namespace gca

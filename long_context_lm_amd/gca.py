@@ -85,6 +85,7 @@ def load() -> ctypes.CDLL:
     lib.gca_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_landmark_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_fetch_chunks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.gca_decode_tokens.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
     for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
@@ -235,6 +236,17 @@ def landmark_backward(cfg: Config, lq, lk, idx, dscore, ws=None, out=None):
                                                                  _ptr(dscore), _ptr(dlq), _ptr(dlk), _ptr(ws), n,
                                                                  _stream()))
     return dlq, dlk
+
+
+def decode_tokens(cfg: Config, q, k, v, idx, score, o=None):
+    """gca_decode_tokens: q [G,B,H,n_tokens,64] of the call's single query chunk -> o like q."""
+    import torch
+
+    o = torch.empty_like(q) if o is None else o
+    prob = cfg.problem()
+    _check("gca_decode_tokens", load().gca_decode_tokens(ctypes.byref(prob), int(q.shape[-2]), _ptr(q), _ptr(k),
+                                                         _ptr(v), _ptr(idx), _ptr(score), _ptr(o), _stream()))
+    return o
 
 
 def fetched_config(cfg: Config) -> Config:

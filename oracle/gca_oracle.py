@@ -382,3 +382,20 @@ def fetch_chunks(idx, k, v, n_kv=None):
                     k_out[b, :, c * CHUNK:(c + 1) * CHUNK] = k[b, :, j * CHUNK:(j + 1) * CHUNK]
                     v_out[b, :, c * CHUNK:(c + 1) * CHUNK] = v[b, :, j * CHUNK:(j + 1) * CHUNK]
     return k_out, v_out, idx_out
+
+
+def decode_tokens(q_tok, k, v, idx, score, *, shift=0, attn_scale=0.125):
+    """Token-level decode: the first n tokens of a query chunk attend to its retrieved chunks.
+
+    While a chunk's tokens are generated one at a time, each new token attends to the chunks
+    retrieved once for the chunk [Notes, Key designs: GCA; Key designs: memory-offload
+    inference].  Attention is per query token, so these are the first n rows of the chunk forward
+    of a chunk whose first n tokens are q_tok: q_tok [G, B, H, n, d] (n <= 64) with
+    idx/score [G, B, 1, K] -> o [G, B, H, n, d] (float64).
+    """
+    q_tok = np.asarray(q_tok, dtype=np.float64)
+    G, B, H, n, d = q_tok.shape
+    q = np.zeros((G, B, H, CHUNK, d))
+    q[:, :, :, :n] = q_tok
+    o, _ = forward(q, k, v, idx, score, shift=shift, attn_scale=attn_scale)
+    return o[:, :, :, :n]

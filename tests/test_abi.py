@@ -91,6 +91,7 @@ def test_problem_validation(field, value, status):
     assert lib.gca_backward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, None, 0, None) == status
     assert lib.gca_landmark_backward(ctypes.byref(p), z, z, z, z, z, z, None, 0, None) == status
     assert lib.gca_fetch_chunks(ctypes.byref(p), z, z, z, z, z, z, None) == status
+    assert lib.gca_decode_tokens(ctypes.byref(p), 1, z, z, z, z, z, z, None) == status
 
 
 def test_null_problem_and_bad_op():
@@ -164,6 +165,15 @@ def test_pointer_checks():
     assert lib.gca_fetch_chunks(ctypes.byref(p), z, mis, z, z, z, z, None) == MISALIGNED
     assert lib.gca_fetch_chunks(ctypes.byref(p), z, z, z, z, mis, z, None) == MISALIGNED
     assert lib.gca_fetch_chunks(ctypes.byref(p), ctypes.c_void_p(FAKE + 2), z, z, z, z, z, None) == MISALIGNED
+    # token-level decode: one query chunk, 1..64 tokens, then the tensors
+    one = good(n_q_chunks=1)
+    assert lib.gca_decode_tokens(ctypes.byref(p), 1, z, z, z, z, z, z, None) == INVALID  # n_q_chunks = 8
+    for n_tok in (0, -1, 65):
+        assert lib.gca_decode_tokens(ctypes.byref(one), n_tok, z, z, z, z, z, z, None) == INVALID
+    assert lib.gca_decode_tokens(ctypes.byref(one), 1, None, z, z, z, z, z, None) == INVALID
+    assert lib.gca_decode_tokens(ctypes.byref(one), 1, z, z, z, z, z, None, None) == INVALID
+    assert lib.gca_decode_tokens(ctypes.byref(one), 1, mis, z, z, z, z, z, None) == MISALIGNED
+    assert lib.gca_decode_tokens(ctypes.byref(one), 1, z, z, z, ctypes.c_void_p(FAKE + 2), z, z, None) == MISALIGNED
     # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
     big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED

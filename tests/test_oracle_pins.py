@@ -525,3 +525,30 @@ def test_fetch_chunks_tiles_and_codes():
             assert np.array_equal(tk, k[b, :, 64 * j:64 * j + 64]) and np.array_equal(tv, v[b, :, 64 * j:64 * j + 64])
         else:
             assert not tk.any() and not tv.any()
+
+
+# ------------------------------------------------------------------------ token-level decode
+def test_decode_tokens_rows_are_independent():
+    """A token's output depends on its own query row only (every token has its own softmax per
+    retrieved chunk), so decoding n tokens gives the chunk forward's first n rows whatever the
+    chunk's later tokens are."""
+    rng = np.random.default_rng(9)
+    G, B, H, n_kv, K, d = 2, 1, 3, 7, 3, 64
+    k = rng.standard_normal((B, H, n_kv * 64, d))
+    v = rng.standard_normal((B, H, n_kv * 64, d))
+    idx = np.array([[[[4, 0, 6]]], [[[2, -1, 5]]]], dtype=np.int32)
+    score = rng.standard_normal((G, B, 1, K)).astype(np.float32)
+    score[idx < 0] = -np.inf
+    q_full = rng.standard_normal((G, B, H, 64, d))
+    o_full, _ = O.forward(q_full, k, v, idx, score, shift=0)
+    for n in (1, 5, 64):
+        o_tok = O.decode_tokens(q_full[:, :, :, :n], k, v, idx, score, shift=0)
+        np.testing.assert_allclose(o_tok, o_full[:, :, :, :n], rtol=1e-13, atol=1e-13)
+    # one token against a single valid slot: plain softmax attention over that chunk (sdpa)
+    one = np.array([[[[3, -1, -1]]]], dtype=np.int32)
+    sc1 = np.array([[[[0.5, -np.inf, -np.inf]]]], dtype=np.float32)
+    qt = rng.standard_normal((1, B, H, 1, d))
+    got = O.decode_tokens(qt, k, v, one, sc1, shift=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qt[0]), torch.from_numpy(k[:, :, 192:256]), torch.from_numpy(v[:, :, 192:256]), scale=0.125)
+    np.testing.assert_allclose(got[0], ref.numpy(), rtol=1e-12, atol=1e-12)
