@@ -260,6 +260,63 @@ def inference_latency(shape, iters=50):
     return res
 
 
+def token_decode_latency(shape, iters=100):
+    """Per-token latency of autoregressive decode over a long history held in HBM: one new token
+    attends (gca_decode_tokens) to the chunks retrieved once for its chunk; the retrieval itself
+    runs once per 64 tokens, so its cost per token is a 64th of the chunk step's."""
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    cfg = gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                     dtype="bf16", q_chunk_base=shape.q_chunk_base, shift=shape.shift)
+    host = I.make_inputs(shape, "bf16", seed=0, names=("lq", "lk", "q"))
+    lq, lk = host["lq"].cuda(), host["lk"].cuda()
+    q1 = host["q"][:, :, :, :1].contiguous().cuda()
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    k = torch.randn(shape.tensor_shape("k"), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(shape.tensor_shape("v"), generator=gen, device="cuda", dtype=torch.bfloat16)
+    nws = gca.workspace_size(gca.OP_RETRIEVE, cfg)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    idx, sc = gca.retrieve(cfg, lq, lk, ws=ws if nws else None)
+    o1 = torch.empty_like(q1)
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device="cuda")
+    for _ in range(5):
+        gca.decode_tokens(cfg, q1, k, v, idx, sc, o=o1)
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("warm", "cold"):
+        times = []
+        for _ in range(iters):
+            if mode == "cold":
+                flush.max()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gca.decode_tokens(cfg, q1, k, v, idx, sc, o=o1)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        times.sort()
+        res[mode] = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
+                     "p90_us": times[(9 * len(times)) // 10]}
+    # GPU time per call with the launches queued back to back (a single call on an idle GPU also
+    # waits for the host to submit it)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush.max()
+    a.record()
+    for _ in range(iters):
+        gca.decode_tokens(cfg, q1, k, v, idx, sc, o=o1)
+    b.record()
+    b.synchronize()
+    res["back_to_back_us"] = a.elapsed_time(b) * 1e3 / iters
+    res["hbm_bytes"] = shape.G * shape.B * shape.topk * shape.H * 2 * 64 * 64 * 2
+    res["hbm_bound_us"] = res["hbm_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
+    del k, v, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def offload_latency(shape, iters=50):
     """Per-chunk latency with the K/V history in pinned host memory (the pages' memory-offload
     inference): retrieve over the device-resident landmarks, fetch the retrieved tiles over the
@@ -452,6 +509,14 @@ def main():
             log(f"  {label}: warm {infer[label]['warm']['median_us']:.1f} us, "
                 f"cold {infer[label]['cold']['median_us']:.1f} us; graph replay warm "
                 f"{infer[label]['graph_warm']['median_us']:.1f} us, cold {infer[label]['graph_cold']['median_us']:.1f} us")
+        log("per-token decode over the 16M history (one token, retrieval reused for the chunk)")
+        r = token_decode_latency(I.INFER_16M)
+        infer["16M_token"] = r
+        tok = r["warm"]["median_us"] + infer["16M"]["warm"]["median_us"] / 64
+        r["per_token_with_amortised_chunk_step_us"] = tok
+        log(f"  16M_token: warm {r['warm']['median_us']:.1f} us, cold {r['cold']['median_us']:.1f} us, "
+            f"back to back {r['back_to_back_us']:.1f} us per call; "
+            f"with the chunk step amortised over 64 tokens {tok:.1f} us per token")
         for label, shp in (("1M_host_kv", I.INFER_1M), ("16M_host_kv", I.INFER_16M)):
             log("inference latency, K/V history in pinned host memory", label)
             r = offload_latency(shp)

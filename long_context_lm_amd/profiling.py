@@ -110,7 +110,7 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
     groups = {}
     for r in _rows(directory, "kernel_trace.csv"):
         s = short_name(r["Kernel_Name"])
-        if s not in ("score_topk", "topk_merge", "attend_fwd", "fetch_chunks"):
+        if s not in ("score_topk", "topk_merge", "attend_fwd", "fetch_chunks", "decode_tokens"):
             continue
         wg = int(r["Workgroup_Size_X"])
         blocks = int(r["Grid_Size_X"]) // wg
@@ -121,7 +121,8 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
     # launch shapes of the decode steps (G = 2 rows of one batch row, H = 12, K = 8)
     shapes = {("score_topk", 128, 256): "1M scan (2 rows x 64 blocks)", ("topk_merge", 2, 1024): "1M / 16M merge",
               ("score_topk", 1024, 256): "16M scan (2 rows x 512 blocks)", ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)",
-              ("fetch_chunks", 192, 256): "host-memory K/V fetch (2 groups x 8 slots x 12 heads, 3 MiB)"}
+              ("fetch_chunks", 192, 256): "host-memory K/V fetch (2 groups x 8 slots x 12 heads, 3 MiB)",
+              ("decode_tokens", 24, 512): "one-token decode, 16M history (2 groups x 12 heads)"}
     lines = [
         "# Kernel durations: one decode step over a 1M- / 16M-token history (retrieve + attend)",
         "",
