@@ -154,6 +154,21 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
                         size_t ws_bytes, void* stream);
 
 /*
+ * Sliding-window self-attention [Notes, Loss / training strategy: sliding-window self-attention
+ * with W = 512 beside the top-k retrieval]: the local attention of the layers that also run GCA.
+ * Token i of a sequence of L = 64 n_q_chunks tokens attends to tokens max(0, i - W + 1) .. i
+ * (itself included) under one softmax:
+ *   o[b,h,i,:] = sum_j softmax_j(attn_scale q[b,h,i,:] . k[b,h,j,:]) v[b,h,j,:]
+ *   lse[b,h,i] = log sum_j exp(attn_scale q[b,h,i,:] . k[b,h,j,:])   (natural log)
+ * window = W: a positive multiple of 64 (a window longer than the sequence is causal attention).
+ * q, k, v, o [B,H,L,64] bf16 (GCA_F32 is GCA_ERR_UNSUPPORTED here); lse [B,H,L] fp32, may be NULL
+ * (the backward needs it).  Requires G = 1 and n_kv_chunks = n_q_chunks; uses B, H, n_q_chunks,
+ * attn_scale of problem.  No workspace.
+ */
+gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* stream);
+
+/*
  * Token-level decode [Notes, Key designs: GCA; Key designs: memory-offload inference]: while the
  * tokens of a query chunk are generated one at a time, every new token attends to the chunks
  * retrieved once for the chunk (one retrieval serves its S tokens).  For the call's single query

@@ -651,6 +651,155 @@ __global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(Atte
   }
 }
 
+// ------------------------------------------------------------- sliding-window attention
+// Local causal attention beside GCA [Notes, Loss / training strategy: sliding-window
+// self-attention with W = 512]: token i attends to tokens max(0, i - W + 1) .. i under one softmax.
+// With W = 64 m, query tile t meets key tiles t - m .. t: in tile t - m only keys above the query's
+// position inside the tile are in the window (its lower edge), in tile t only keys at or below it
+// (causality), the tiles between are whole.  In the S^T accumulators lane (li, hl) holds
+// sacc[qh][tt][r] = S[query 32 qh + li][key 32 tt + 16 hl + r], so the masks are per-register
+// comparisons.  Masked scores are -inf; a query whose keys in a tile are all masked keeps its
+// running maximum (the guards below avoid -inf - -inf).
+__device__ __forceinline__ void sw_mask(f32x16_t (&sacc)[2][2], bool lower_edge, bool diagonal) {
+  const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * tt + 16 * hl + r, query = 32 * qh + li;
+        const bool out = (lower_edge && key <= query) || (diagonal && key > query);
+        sacc[qh][tt][r] = out ? -__builtin_inff() : sacc[qh][tt][r];
+      }
+}
+
+// One wave per query tile, as the bf16 GCA forward: K and V tiles stream through single LDS
+// buffers with the same counted-copy pipeline, and the softmax is online (running maximum and sum
+// per query; the output accumulators are rescaled when the maximum grows).
+__global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
+  using T = bf16_t;
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, 1>;
+  constexpr int kC = Off::kCopies;
+  __shared__ __align__(1024) char Ks[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+
+  const int lane = threadIdx.x, li = lane & 31, hl = lane >> 5;
+  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t t = lid % p.n_c;
+  const int64_t bh = lid / p.n_c;
+  const int64_t row0 = bh * p.n_c * kChunk;  // first token of this (batch row, head)
+  const int64_t qrow0 = row0 + t * kChunk;
+
+  Frag<T> qf[2][4];
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const T* q = static_cast<const T*>(p.q) + (qrow0 + 32 * qh + li) * kDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qh][s].load(q + 16 * s + 8 * hl);
+  }
+  Off off;
+  off.init(0);
+  const int64_t kt0 = t - p.m > 0 ? t - p.m : 0;
+  auto tile = [&](const void* base, int64_t kt) {
+    return static_cast<const T*>(base) + (row0 + kt * kChunk) * kDim;
+  };
+  off.copy(tile(p.k, kt0), Ks, 0);
+  off.copy(tile(p.v, kt0), Vs, 0);
+
+  f32x16_t oacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+  float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
+  const float c2 = p.attn_scale * kLog2e;
+  for (int64_t kt = kt0; kt <= t; ++kt) {  // wave-uniform
+    const bool more = kt < t;
+    wait_vm_outstanding<kC>();  // K(kt) landed: only V(kt) may be in flight
+    Frag<T> kf[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[tt][s] = off.kfrag(Ks, tt, s);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K(kt) in registers: the buffer is free
+    if (more) off.copy(tile(p.k, kt + 1), Ks, 0);
+
+    f32x16_t sacc[2][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sacc[qh][tt] = zero16();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[qh][tt] = mma(kf[tt][s], qf[qh][s], sacc[qh][tt]);
+      }
+    const bool lower_edge = kt == t - p.m, diagonal = kt == t;
+    if (lower_edge || diagonal) sw_mask(sacc, lower_edge, diagonal);
+    Frag<T> pf[2][4];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qh][tt][r]);
+      mx = xor32_max(mx) * c2;  // log2 units
+      const float m_new = fmaxf(m_run[qh], mx);
+      const bool none = m_new == -__builtin_inff();  // no key of the window seen yet
+      const float alpha = none ? 1.f : fast_exp2(m_run[qh] - m_new);
+      const float bias = none ? 0.f : -m_new;
+      float l = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[qh][tt][r] = fast_exp2(__builtin_fmaf(sacc[qh][tt][r], c2, bias));
+          l += sacc[qh][tt][r];
+        }
+      l_run[qh] = l_run[qh] * alpha + xor32_sum(l);
+      m_run[qh] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[qh][dt][r] *= alpha;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sacc[qh][s >> 1][8 * (s & 1) + e];
+        pf[qh][s].set(x);
+      }
+    }
+    if (more) wait_vm_outstanding<kC>();  // V(kt) landed: K(kt + 1) may not have
+    else wait_vm_outstanding<0>();
+    Frag<T> vf[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) vf[s][dt] = off.vfrag(Vs, s, dt);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V(kt) in registers: the buffer is free
+    if (more) off.copy(tile(p.v, kt + 1), Vs, 0);
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) oacc[qh][dt] = mma(vf[s][dt], pf[qh][s], oacc[qh][dt]);
+  }
+
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const float f = __builtin_amdgcn_rcpf(l_run[qh]);
+    T* o = static_cast<T*>(p.o) + (qrow0 + 32 * qh + li) * kDim;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        store4(o + 32 * dt + 8 * a + 4 * hl, f * oacc[qh][dt][4 * a], f * oacc[qh][dt][4 * a + 1],
+               f * oacc[qh][dt][4 * a + 2], f * oacc[qh][dt][4 * a + 3]);
+    if (p.lse && hl == qh)  // lane (li, hl) writes query 32 hl + li
+      p.lse[qrow0 + 32 * qh + li] = m_run[qh] * kLn2f + __builtin_amdgcn_logf(l_run[qh]) * kLn2f;
+  }
+}
+
 // ------------------------------------------------------------- token-level decode
 // While the tokens of a query chunk are generated one at a time, each new token attends to the
 // chunks retrieved once for the chunk's row: one retrieval serves all S tokens of the chunk.  For
@@ -1191,6 +1340,11 @@ hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, 
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.H)), block(64 * kDecodeWaves);
   if (f32) hipLaunchKernelGGL(decode_tokens_kernel<float>, grid, block, 0, s, p, n_tok);
   else hipLaunchKernelGGL(decode_tokens_kernel<bf16_t>, grid, block, 0, s, p, n_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_sw_fwd(const SwParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(sw_fwd_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ namespace gca {
 const char* kernel_name(int id) {
   static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
-                                           "lmk_key_grad", "fetch_chunks", "decode_tokens"};
+                                           "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd",
+                                           "sw_bwd_query", "sw_bwd_key"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -423,6 +424,45 @@ gca_status gca_decode_tokens(const gca_problem* problem, int32_t n_tokens, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool f32 = p->dtype == GCA_F32;
   return launch(kDecodeTokens, s, [&] { return launch_decode_tokens(a, n_tokens, f32, s); });
+}
+
+// Sliding-window attention problems: one sequence of n_q_chunks chunks per (batch row, head).
+static gca_status sw_check(const gca_problem* p, int32_t window) {
+  GCA_TRY(validate_problem(p));
+  if (p->G != 1 || p->n_kv_chunks != p->n_q_chunks) return GCA_ERR_INVALID_ARGUMENT;
+  if (window < 64 || window % 64 != 0) return GCA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != GCA_BF16) return GCA_ERR_UNSUPPORTED;
+  return GCA_OK;
+}
+
+static SwParams sw_params(const gca_problem* p, int32_t window) {
+  SwParams w{};
+  w.n_c = p->n_q_chunks;
+  w.B = p->B;
+  w.H = p->H;
+  w.m = window / 64;
+  w.attn_scale = p->attn_scale;
+  return w;
+}
+
+gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void* q, const void* k, const void* v,
+                          void* o, float* lse, void* stream) {
+  GCA_TRY(sw_check(problem, window));
+  const bool any = problem->n_q_chunks > 0;
+  GCA_TRY(check_tensor(q, any, 16));
+  GCA_TRY(check_tensor(k, any, 16));
+  GCA_TRY(check_tensor(v, any, 16));
+  GCA_TRY(check_tensor(o, any, 16));
+  if (lse != nullptr) GCA_TRY(check_tensor(lse, any, 4));
+  if (!any) return GCA_OK;
+  SwParams w = sw_params(problem, window);
+  w.q = q;
+  w.k = k;
+  w.v = v;
+  w.o = o;
+  w.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch(kSwFwd, s, [&] { return launch_sw_fwd(w, s); });
 }
 
 // The device address of a K/V source: device memory as it is; pinned host memory (hipHostMalloc)

@@ -19,6 +19,9 @@ enum KernelId {
   kLmkKeyGrad,
   kFetchChunks,
   kDecodeTokens,
+  kSwFwd,
+  kSwBwdQuery,
+  kSwBwdKey,
   kNumKernels
 };
 const char* kernel_name(int id);
@@ -93,6 +96,28 @@ struct FetchParams {
   int32_t G, B, H, K;
 };
 
+// Sliding-window attention over one sequence of n_c chunks: q, k, v, o, dout, dq, dk, dv are
+// [B, H, n_c * 64, 64]; lse [B, H, n_c * 64] (natural log-sum-exp of attn_scale q.k over the window);
+// stats [B, H, n_c * 64, 2] {-lse log2 e, D = <dout, o>} for the key-major pass.
+struct SwParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o_in;
+  const float* lse_in;
+  const void* dout;
+  void* o;
+  float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* stats;
+  int64_t n_c;
+  int32_t B, H;
+  int32_t m;            // window in chunks: W = 64 m keys per token, itself included
+  float attn_scale;
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_score_topk(const RetrieveParams& p, bool f32, hipStream_t s);
 hipError_t launch_topk_merge(const RetrieveParams& p, hipStream_t s);
@@ -105,5 +130,8 @@ hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t 
 hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_fetch_chunks(const FetchParams& p, bool f32, hipStream_t s);
 hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, hipStream_t s);
+hipError_t launch_sw_fwd(const SwParams& p, hipStream_t s);
+hipError_t launch_sw_bwd_query(const SwParams& p, hipStream_t s);
+hipError_t launch_sw_bwd_key(const SwParams& p, hipStream_t s);
 
 }  // namespace gca

@@ -86,6 +86,7 @@ def load() -> ctypes.CDLL:
     lib.gca_landmark_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_fetch_chunks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.gca_decode_tokens.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
+    lib.gca_sw_forward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
@@ -247,6 +248,24 @@ def decode_tokens(cfg: Config, q, k, v, idx, score, o=None):
     _check("gca_decode_tokens", load().gca_decode_tokens(ctypes.byref(prob), int(q.shape[-2]), _ptr(q), _ptr(k),
                                                          _ptr(v), _ptr(idx), _ptr(score), _ptr(o), _stream()))
     return o
+
+
+def sw_config(B: int, H: int, n_chunks: int, attn_scale: float = 1.0 / math.sqrt(64)) -> Config:
+    """The problem of a sliding-window attention call over one sequence of n_chunks chunks."""
+    return Config(B=B, G=1, H=H, n_q=n_chunks, n_kv=n_chunks, topk=1, dtype="bf16", attn_scale=attn_scale)
+
+
+def sw_forward(cfg: Config, q, k, v, window: int = 512, need_lse: bool = True, o=None, lse=None):
+    """gca_sw_forward: q, k, v [B,H,L,64] bf16 -> (o like q, lse fp32 [B,H,L] or None)."""
+    import torch
+
+    o = torch.empty_like(q) if o is None else o
+    if need_lse and lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    prob = cfg.problem()
+    _check("gca_sw_forward", load().gca_sw_forward(ctypes.byref(prob), int(window), _ptr(q), _ptr(k), _ptr(v),
+                                                   _ptr(o), _ptr(lse) if need_lse else None, _stream()))
+    return o, (lse if need_lse else None)
 
 
 def fetched_config(cfg: Config) -> Config:

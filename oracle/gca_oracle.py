@@ -399,3 +399,28 @@ def decode_tokens(q_tok, k, v, idx, score, *, shift=0, attn_scale=0.125):
     q[:, :, :, :n] = q_tok
     o, _ = forward(q, k, v, idx, score, shift=shift, attn_scale=attn_scale)
     return o[:, :, :, :n]
+
+
+def sw_attention(q, k, v, window, *, attn_scale=0.125):
+    """Sliding-window causal self-attention, the local attention beside GCA.
+
+    [Notes, Loss / training strategy]: sliding-window self-attention with W = 512 beside the top-k
+    retrieval.  Token i attends to tokens max(0, i - W + 1) .. i under one softmax of
+    z = attn_scale <q_i, k_j>.  q, k, v [B, H, L, d] -> o [B, H, L, d] and the natural
+    log-sum-exp lse [B, H, L], both float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, L, d = q.shape
+    o = np.zeros((B, H, L, d))
+    lse = np.zeros((B, H, L))
+    for i in range(L):
+        lo = max(0, i - window + 1)
+        z = attn_scale * np.einsum("bhd,bhjd->bhj", q[:, :, i], k[:, :, lo:i + 1])
+        m = z.max(axis=-1, keepdims=True)
+        e = np.exp(z - m)
+        s = e.sum(axis=-1, keepdims=True)
+        o[:, :, i] = np.einsum("bhj,bhjd->bhd", e / s, v[:, :, lo:i + 1])
+        lse[:, :, i] = (m + np.log(s))[..., 0]
+    return o, lse

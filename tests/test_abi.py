@@ -174,6 +174,19 @@ def test_pointer_checks():
     assert lib.gca_decode_tokens(ctypes.byref(one), 1, z, z, z, z, z, None, None) == INVALID
     assert lib.gca_decode_tokens(ctypes.byref(one), 1, mis, z, z, z, z, z, None) == MISALIGNED
     assert lib.gca_decode_tokens(ctypes.byref(one), 1, z, z, z, ctypes.c_void_p(FAKE + 2), z, z, None) == MISALIGNED
+    # sliding-window attention: one group, a query sequence that is its own key sequence, a
+    # window that is a positive multiple of 64, bf16
+    sw = gca.sw_config(2, 3, 8).problem()
+    assert lib.gca_sw_forward(ctypes.byref(sw), 512, None, z, z, z, None, None) == INVALID
+    assert lib.gca_sw_forward(ctypes.byref(sw), 512, mis, z, z, z, None, None) == MISALIGNED
+    for window in (0, -64, 100):
+        assert lib.gca_sw_forward(ctypes.byref(sw), window, z, z, z, z, None, None) == INVALID
+    for field, value, status in (("G", 2, INVALID), ("n_kv_chunks", 9, INVALID), ("dtype", 1, UNSUPPORTED)):
+        bad = gca.sw_config(2, 3, 8).problem()
+        setattr(bad, field, value)
+        assert lib.gca_sw_forward(ctypes.byref(bad), 512, z, z, z, z, None, None) == status
+    empty = gca.sw_config(2, 3, 0).problem()
+    assert lib.gca_sw_forward(ctypes.byref(empty), 512, None, None, None, None, None, None) == OK
     # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
     big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED

@@ -552,3 +552,40 @@ def test_decode_tokens_rows_are_independent():
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(qt[0]), torch.from_numpy(k[:, :, 192:256]), torch.from_numpy(v[:, :, 192:256]), scale=0.125)
     np.testing.assert_allclose(got[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------- sliding-window attention
+def _band_sdpa(q, k, v, window, scale):
+    L = q.shape[-2]
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    allowed = (j <= i) & (j > i - window)
+    t = [torch.from_numpy(np.asarray(x, dtype=np.float64)) for x in (q, k, v)]
+    o = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=allowed, scale=scale)
+    z = scale * t[0] @ t[1].transpose(-1, -2)
+    lse = torch.logsumexp(z.masked_fill(~allowed, float("-inf")), dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("window", [1, 64, 100, 192, 10_000])
+def test_sw_attention_matches_band_masked_sdpa(window):
+    rng = np.random.default_rng(window)
+    B, H, L, d = 2, 2, 300, 16
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    o, lse = O.sw_attention(q, k, v, window, attn_scale=0.3)
+    ro, rl = _band_sdpa(q, k, v, window, 0.3)
+    np.testing.assert_allclose(o, ro, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def test_sw_attention_special_cases():
+    rng = np.random.default_rng(2)
+    B, H, L, d = 1, 3, 130, 8
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    o1, lse1 = O.sw_attention(q, k, v, 1)  # a window of one token: the token's own value
+    assert np.array_equal(o1, v)
+    np.testing.assert_allclose(lse1, 0.125 * np.einsum("bhld,bhld->bhl", q, k), rtol=1e-14, atol=0)
+    oc, _ = O.sw_attention(q, k, v, L)  # the whole sequence: causal attention
+    ref = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)), is_causal=True,
+                                                           scale=0.125)
+    np.testing.assert_allclose(oc, ref.numpy(), rtol=1e-10, atol=1e-12)
