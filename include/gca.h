@@ -68,7 +68,8 @@ typedef enum {
   GCA_OP_RETRIEVE = 0,
   GCA_OP_FORWARD = 1,
   GCA_OP_BACKWARD = 2,
-  GCA_OP_LANDMARK_BACKWARD = 3
+  GCA_OP_LANDMARK_BACKWARD = 3,
+  GCA_OP_SW_BACKWARD = 4
 } gca_op;
 
 /* Sizes and options of one problem.  Fields are read, never written. */
@@ -167,6 +168,19 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
  */
 gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void* q, const void* k,
                           const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Backward of gca_sw_forward: with P the window softmax, dP = dout v^T and D = <dout, o> per
+ * token,
+ *   dS = P (dP - D),  dq = attn_scale dS k,  dk = attn_scale dS^T q,  dv = P^T dout,
+ * in fp32 over fixed orders without atomics (bit-identical from run to run), rounded once to bf16.
+ * q, k, v, o and lse (from gca_sw_forward), dout: inputs [B,H,L,64] bf16 (lse [B,H,L] fp32); dq,
+ * dk, dv: outputs like q.  ws: >= gca_workspace_size(SW_BACKWARD) = B*H*L*8 bytes (per-token
+ * {-lse log2 e, D}; contents need no setup).  Same problem rules as gca_sw_forward.
+ */
+gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Token-level decode [Notes, Key designs: GCA; Key designs: memory-offload inference]: while the

@@ -1042,6 +1042,252 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
   }
 }
 
+// ------------------------------------------------------------- sliding-window backward
+// dS = P (dP - D) with P = exp(z - lse) and D = <dO, O> per query (one softmax over the window),
+// then dQ = scale dS K query-major and dK = scale dS^T Q, dV = P^T dO key-major, without atomics.
+// The query-major pass walks key tiles t - m .. t exactly as the GCA query-major pass walks its
+// slots (double-buffered K, single V, two waves of 32 queries); it first computes D from the
+// stored output and writes {-lse log2 e, D} per query, which the key-major pass reads as the GCA
+// key-major pass reads its {bias, e} vectors.  Masked scores become -inf before the exp, so their
+// P and dS are exactly 0.
+__device__ __forceinline__ void sw_mask_keys_major(f32x16_t (&sacc)[2], int query_base, bool lower_edge,
+                                                   bool diagonal) {
+  // query-major accumulators: sacc[tt][r] = S[query query_base + li][key 32 tt + 16 hl + r]
+  const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * tt + 16 * hl + r, query = query_base + li;
+      const bool out = (lower_edge && key <= query) || (diagonal && key > query);
+      sacc[tt][r] = out ? -__builtin_inff() : sacc[tt][r];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
+  using T = bf16_t;
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, kWaves>;
+  __shared__ __align__(1024) char Ka[TL::kBytes];
+  __shared__ __align__(1024) char Kb[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hl = lane >> 5;
+  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t t = lid % p.n_c;
+  const int64_t bh = lid / p.n_c;
+  const int64_t row0 = bh * p.n_c * kChunk;
+  const int64_t qrow0 = row0 + t * kChunk;
+  const int my_q = 32 * wave + li;
+
+  Frag<T> qf[4], df[4], of[4];
+  const int64_t my_row = qrow0 + my_q;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qf[s].load(static_cast<const T*>(p.q) + my_row * kDim + 16 * s + 8 * hl);
+    df[s].load(static_cast<const T*>(p.dout) + my_row * kDim + 16 * s + 8 * hl);
+    of[s].load(static_cast<const T*>(p.o_in) + my_row * kDim + 16 * s + 8 * hl);
+  }
+  // D = <dO, O> of this lane's query (lanes l and l ^ 32 hold its two halves of the dimensions)
+  float dd = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = df[s].v[w], c = of[s].v[w];
+      dd = __builtin_fmaf(__uint_as_float(a << 16), __uint_as_float(c << 16), dd);
+      dd = __builtin_fmaf(__uint_as_float(a & 0xffff0000u), __uint_as_float(c & 0xffff0000u), dd);
+    }
+  const float D = xor32_sum(dd);
+  const float bias = -p.lse_in[my_row] * kLog2e;
+  if (hl == 0) reinterpret_cast<f32x2_t*>(p.stats)[my_row] = f32x2_t{bias, D};
+  Off off;
+  off.init(wave);
+
+  const int64_t kt0 = t - p.m > 0 ? t - p.m : 0;
+  const int nt = static_cast<int>(t - kt0 + 1);
+  auto tile = [&](const void* base, int64_t kt) {
+    return static_cast<const T*>(base) + (row0 + kt * kChunk) * kDim;
+  };
+  off.copy(tile(p.k, kt0), Ka, wave);
+  off.copy(tile(p.v, kt0), Vs, wave);
+  barrier_copies_landed<0>();
+
+  f32x16_t dqacc[2] = {zero16(), zero16()};
+  const float c2 = p.attn_scale * kLog2e;
+  auto step = [&](int n, char* const Kc, char* const Kn) {
+    const int64_t kt = kt0 + n;
+    const bool more = n + 1 < nt;
+    if (more) off.copy(tile(p.k, kt + 1), Kn, wave);  // the other K buffer is free
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = zero16();
+      pacc[tt] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sacc[tt] = mma(off.kfrag(Kc, tt, s), qf[s], sacc[tt]);
+        pacc[tt] = mma(off.kfrag(Vs, tt, s), df[s], pacc[tt]);
+      }
+    }
+    barrier_lds_reads_done();  // every wave has read V(kt)
+    if (more) off.copy(tile(p.v, kt + 1), Vs, wave);
+    const bool lower_edge = kt == t - p.m, diagonal = kt == t;
+    if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+    Frag<T> zf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tt = s >> 1, r = 8 * (s & 1) + e;
+        const float pw = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
+        x[e] = pw * (pacc[tt][r] - D);
+      }
+      zf[s].set(x);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dqacc[dt] = mma(off.vfrag(Kc, s, dt), zf[s], dqacc[dt]);
+    // K(kt + 1) and V(kt + 1) landed, and every wave has read K(kt), whose buffer the next step
+    // refills
+    if (more) barrier_copies_landed_reads_done<0>();
+  };
+  for (int n = 0; n < nt; n += 2) {
+    step(n, Ka, Kb);
+    if (n + 1 < nt) step(n + 1, Kb, Ka);
+  }
+
+  T* dq = static_cast<T*>(p.dq) + my_row * kDim;
+  const float sc = p.attn_scale;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4(dq + 32 * dt + 8 * a + 4 * hl, sc * dqacc[dt][4 * a], sc * dqacc[dt][4 * a + 1],
+             sc * dqacc[dt][4 * a + 2], sc * dqacc[dt][4 * a + 3]);
+}
+
+// Key-major pass: one workgroup of two waves (32 keys each) per key tile kt walks the query tiles
+// kt .. kt + m whose windows reach it, double-buffered like the GCA key-major pass (Q tile, dO
+// tile and the 64 {bias, D} pairs of the next query tile copied in at the start of the current).
+__global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
+  using T = bf16_t;
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, kWaves>;
+  constexpr int kVecBytes = kChunk * 8;
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];
+  __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hl = lane >> 5;
+  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t kt = lid % p.n_c;
+  const int64_t bh = lid / p.n_c;
+  const int64_t row0 = bh * p.n_c * kChunk;
+  const int my_u = 32 * wave + li;
+  const int64_t krow = row0 + kt * kChunk + my_u;
+
+  Frag<T> kf[4], vf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    kf[s].load(static_cast<const T*>(p.k) + krow * kDim + 16 * s + 8 * hl);
+    vf[s].load(static_cast<const T*>(p.v) + krow * kDim + 16 * s + 8 * hl);
+  }
+  Off off;
+  off.init(wave);
+  f32x16_t dkacc[2] = {zero16(), zero16()};
+  f32x16_t dvacc[2] = {zero16(), zero16()};
+  const float c2 = p.attn_scale * kLog2e;
+  const int64_t qt_last = kt + p.m < p.n_c - 1 ? kt + p.m : p.n_c - 1;
+  const int count = static_cast<int>(qt_last - kt + 1);
+
+  auto fill = [&](int64_t qt, char* buf) {
+    const int64_t qrow0 = row0 + qt * kChunk;
+    off.copy(static_cast<const T*>(p.q) + qrow0 * kDim, buf, wave);
+    off.copy(static_cast<const T*>(p.dout) + qrow0 * kDim, buf + TL::kBytes, wave);
+    // wave w copies the pairs of queries 32 w .. 32 w + 31 (16 bytes per lane, lanes < 16)
+    const float* src = p.stats + 2 * (qrow0 + 32 * wave);
+    if (lane < 16) copy16_async_untracked(src, 16u * lane, buf + 2 * TL::kBytes + 256 * wave);
+  };
+  auto body = [&](int n, const char* cur, char* nxt) {
+    const int64_t qt = kt + n;
+    if (n + 1 < count) fill(qt + 1, nxt);
+    const char* Qs = cur;
+    const char* Ds = cur + TL::kBytes;
+    const f32x4_t* vec = reinterpret_cast<const f32x4_t*>(cur + 2 * TL::kBytes);  // {b, D, b, D}
+    const bool diagonal = qt == kt, lower_edge = qt == kt + p.m;
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      sacc[qh] = zero16();
+      pacc[qh] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sacc[qh] = mma(off.kfrag(Qs, qh, s), kf[s], sacc[qh]);
+        pacc[qh] = mma(off.kfrag(Ds, qh, s), vf[s], pacc[qh]);
+      }
+    }
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      // lane holds queries 32 qh + 16 hl + r of key my_u
+      Frag<T> pf[2], zf[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int q0 = 32 * qh + 16 * hl + 8 * half;
+        f32x4_t be[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) be[i] = vec[q0 / 2 + i];
+        float xp[8], xz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e, query = q0 + e;
+          const bool out = (lower_edge && my_u <= query) || (diagonal && my_u > query);
+          const float z = out ? -__builtin_inff() : sacc[qh][r];
+          const float bias_q = be[e >> 1][2 * (e & 1)], d_q = be[e >> 1][2 * (e & 1) + 1];
+          const float pw = fast_exp2(__builtin_fmaf(z, c2, bias_q));
+          xp[e] = pw;
+          xz[e] = pw * (pacc[qh][r] - d_q);
+        }
+        pf[half].set(xp);
+        zf[half].set(xz);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          dvacc[dt] = mma(off.vfrag(Ds, 2 * qh + half, dt), pf[half], dvacc[dt]);
+          dkacc[dt] = mma(off.vfrag(Qs, 2 * qh + half, dt), zf[half], dkacc[dt]);
+        }
+    }
+    // the next query tile's copies landed, and every wave is done with this buffer
+    barrier_copies_landed_reads_done<0>();
+  };
+  fill(kt, buf0);
+  barrier_copies_landed_reads_done<0>();
+  for (int n = 0; n < count; n += 2) {
+    body(n, buf0, buf1);
+    if (n + 1 < count) body(n + 1, buf1, buf0);
+  }
+
+  T* dk = static_cast<T*>(p.dk) + krow * kDim;
+  T* dv = static_cast<T*>(p.dv) + krow * kDim;
+  const float sc = p.attn_scale;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hl;
+      store4(dk + d0, sc * dkacc[dt][4 * a], sc * dkacc[dt][4 * a + 1], sc * dkacc[dt][4 * a + 2],
+             sc * dkacc[dt][4 * a + 3]);
+      store4(dv + d0, dvacc[dt][4 * a], dvacc[dt][4 * a + 1], dvacc[dt][4 * a + 2], dvacc[dt][4 * a + 3]);
+    }
+}
+
 // ------------------------------------------------------------- backward, key-major (dK, dV)
 struct PairRef {
   int g, slot;
@@ -1345,6 +1591,18 @@ hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, 
 
 hipError_t launch_sw_fwd(const SwParams& p, hipStream_t s) {
   hipLaunchKernelGGL(sw_fwd_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sw_bwd_query(const SwParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(sw_bwd_query_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)),
+                     dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sw_bwd_key(const SwParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(sw_bwd_key_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -221,6 +221,9 @@ gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes)
       *bytes = plan_backward(problem).total;
       return GCA_OK;
     case GCA_OP_LANDMARK_BACKWARD: *bytes = plan_landmark(problem).total; return GCA_OK;
+    case GCA_OP_SW_BACKWARD:
+      *bytes = align_up(static_cast<size_t>(problem->B) * problem->H * problem->n_q_chunks * 64 * 8);
+      return GCA_OK;
     default: return GCA_ERR_INVALID_ARGUMENT;
   }
 }
@@ -463,6 +466,35 @@ gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void
   w.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launch(kSwFwd, s, [&] { return launch_sw_fwd(w, s); });
+}
+
+gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                           size_t ws_bytes, void* stream) {
+  GCA_TRY(sw_check(problem, window));
+  const bool any = problem->n_q_chunks > 0;
+  for (const void* t : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    GCA_TRY(check_tensor(t, any, 16));
+  GCA_TRY(check_tensor(lse, any, 4));
+  size_t need = 0;
+  GCA_TRY(gca_workspace_size(GCA_OP_SW_BACKWARD, problem, &need));
+  GCA_TRY(check_ws(need, ws, ws_bytes));
+  if (!any) return GCA_OK;
+  SwParams w = sw_params(problem, window);
+  w.q = q;
+  w.k = k;
+  w.v = v;
+  w.o_in = o;
+  w.lse_in = lse;
+  w.dout = dout;
+  w.dq = dq;
+  w.dk = dk;
+  w.dv = dv;
+  w.stats = static_cast<float*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GCA_TRY(launch(kSwBwdQuery, s, [&] { return launch_sw_bwd_query(w, s); }));
+  return launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(w, s); });
 }
 
 // The device address of a K/V source: device memory as it is; pinned host memory (hipHostMalloc)

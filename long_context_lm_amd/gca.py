@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgca.so")
 
 GCA_OK = 0
-OP_RETRIEVE, OP_FORWARD, OP_BACKWARD, OP_LANDMARK_BACKWARD = 0, 1, 2, 3
+OP_RETRIEVE, OP_FORWARD, OP_BACKWARD, OP_LANDMARK_BACKWARD, OP_SW_BACKWARD = 0, 1, 2, 3, 4
 DTYPES = {"bf16": 0, "f32": 1}
 
 
@@ -87,6 +87,7 @@ def load() -> ctypes.CDLL:
     lib.gca_fetch_chunks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.gca_decode_tokens.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
     lib.gca_sw_forward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+    lib.gca_sw_backward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
@@ -266,6 +267,22 @@ def sw_forward(cfg: Config, q, k, v, window: int = 512, need_lse: bool = True, o
     _check("gca_sw_forward", load().gca_sw_forward(ctypes.byref(prob), int(window), _ptr(q), _ptr(k), _ptr(v),
                                                    _ptr(o), _ptr(lse) if need_lse else None, _stream()))
     return o, (lse if need_lse else None)
+
+
+def sw_backward(cfg: Config, q, k, v, o, lse, dout, window: int = 512, ws=None, out=None):
+    """gca_sw_backward: returns (dq, dk, dv) like q."""
+    import torch
+
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None else out
+    if ws is None:
+        ws, n = _workspace(OP_SW_BACKWARD, cfg, q.device)
+    else:
+        n = ws.numel()
+    prob = cfg.problem()
+    _check("gca_sw_backward", load().gca_sw_backward(ctypes.byref(prob), int(window), _ptr(q), _ptr(k), _ptr(v),
+                                                     _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                     _ptr(ws), n, _stream()))
+    return dq, dk, dv
 
 
 def fetched_config(cfg: Config) -> Config:

@@ -424,3 +424,31 @@ def sw_attention(q, k, v, window, *, attn_scale=0.125):
         o[:, :, i] = np.einsum("bhj,bhjd->bhd", e / s, v[:, :, lo:i + 1])
         lse[:, :, i] = (m + np.log(s))[..., 0]
     return o, lse
+
+
+def sw_attention_backward(q, k, v, dout, window, *, attn_scale=0.125):
+    """Gradients of sw_attention: with P the window softmax of token i, dP_ij = <dout_i, v_j> and
+    D_i = sum_j P_ij dP_ij = <dout_i, o_i>,
+      dS_ij = P_ij (dP_ij - D_i),  dq_i = attn_scale sum_j dS_ij k_j,
+      dk_j = attn_scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i.
+    All float64; returns (dq, dk, dv) shaped like q."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, L, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for i in range(L):
+        lo = max(0, i - window + 1)
+        z = attn_scale * np.einsum("bhd,bhjd->bhj", q[:, :, i], k[:, :, lo:i + 1])
+        e = np.exp(z - z.max(axis=-1, keepdims=True))
+        P = e / e.sum(axis=-1, keepdims=True)
+        dP = np.einsum("bhd,bhjd->bhj", dout[:, :, i], v[:, :, lo:i + 1])
+        D = (P * dP).sum(axis=-1, keepdims=True)
+        dS = P * (dP - D)
+        dq[:, :, i] = attn_scale * np.einsum("bhj,bhjd->bhd", dS, k[:, :, lo:i + 1])
+        dk[:, :, lo:i + 1] += attn_scale * dS[..., None] * q[:, :, i][:, :, None, :]
+        dv[:, :, lo:i + 1] += P[..., None] * dout[:, :, i][:, :, None, :]
+    return dq, dk, dv

@@ -83,7 +83,7 @@ def ws_size(p, op):
 def test_problem_validation(field, value, status):
     p = good(**{field: value})
     lib = gca.load()
-    for op in (0, 1, 2, 3):
+    for op in (0, 1, 2, 3, 4):
         assert ws_size(p, op)[0] == status
     z = ctypes.c_void_p(FAKE)
     assert lib.gca_retrieve(ctypes.byref(p), z, z, z, z, None, 0, None) == status
@@ -99,7 +99,7 @@ def test_null_problem_and_bad_op():
     n = ctypes.c_size_t(0)
     assert lib.gca_workspace_size(0, None, ctypes.byref(n)) == INVALID
     p = good()
-    assert lib.gca_workspace_size(4, ctypes.byref(p), ctypes.byref(n)) == INVALID
+    assert lib.gca_workspace_size(5, ctypes.byref(p), ctypes.byref(n)) == INVALID
     assert lib.gca_workspace_size(-1, ctypes.byref(p), ctypes.byref(n)) == INVALID
     assert lib.gca_workspace_size(0, ctypes.byref(p), None) == INVALID
     assert lib.gca_retrieve(None, None, None, None, None, None, 0, None) == INVALID
@@ -187,6 +187,16 @@ def test_pointer_checks():
         assert lib.gca_sw_forward(ctypes.byref(bad), 512, z, z, z, z, None, None) == status
     empty = gca.sw_config(2, 3, 0).problem()
     assert lib.gca_sw_forward(ctypes.byref(empty), 512, None, None, None, None, None, None) == OK
+    assert lib.gca_sw_backward(ctypes.byref(empty), 512, *([None] * 9), None, 0, None) == OK
+    st, need = ws_size(sw, 4)
+    assert st == OK and need == 2 * 3 * 8 * 64 * 8
+    args = [z] * 9
+    assert lib.gca_sw_backward(ctypes.byref(sw), 512, *args, z, need - 1, None) == WS_SMALL
+    assert lib.gca_sw_backward(ctypes.byref(sw), 512, *args, None, need, None) == INVALID
+    assert lib.gca_sw_backward(ctypes.byref(sw), 512, *([z] * 5), ctypes.c_void_p(FAKE + 2), *([z] * 3), z, need,
+                               None) == MISALIGNED
+    assert lib.gca_sw_backward(ctypes.byref(sw), 512, *([z] * 6), None, z, z, z, need, None) == INVALID
+    assert lib.gca_sw_backward(ctypes.byref(sw), 96, *args, z, need, None) == INVALID
     # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
     big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED

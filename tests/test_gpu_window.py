@@ -68,3 +68,49 @@ def test_sw_forward_training_shape_sampled():
         ref.append(ro[0, 0, -1])
         assert abs(float(lse[b, h, i]) - rl[0, 0, -1]) < 2e-3
     assert_close("o sampled", np.array(got), np.array(ref), "bf16")
+
+
+def _sw_grads(B, H, n_c, window, seed):
+    q, k, v, do = _inputs(B, H, n_c, seed=seed)
+    dev = [t.cuda() for t in (q, k, v, do)]
+    cfg = gca.sw_config(B, H, n_c)
+    o, lse = gca.sw_forward(cfg, *dev[:3], window)
+    dq, dk, dv = gca.sw_backward(cfg, *dev[:3], o, lse, dev[3], window)
+    torch.cuda.synchronize()
+    return (q, k, v, do), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("n_c", [1, 3, 11])
+@pytest.mark.parametrize("window", [64, 128, 512, 4096])
+def test_sw_backward_matches_oracle(n_c, window):
+    say("case sw backward", n_c, window)
+    (q, k, v, do), got = _sw_grads(2, 3, n_c, window, seed=n_c * 5 + window)
+    ref = O.sw_attention_backward(_f64(q), _f64(k), _f64(v), _f64(do), window)
+    errs = [assert_close(name, _f64(g), r, "bf16") for name, g, r in zip(("dq", "dk", "dv"), got, ref)]
+    say("  errors", " ".join(f"{e:.2e}" for e in errs))
+
+
+def test_sw_backward_is_deterministic():
+    _, a = _sw_grads(2, 2, 12, 512, seed=1)
+    _, b = _sw_grads(2, 2, 12, 512, seed=1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_sw_backward_training_shape_sampled():
+    B, H, n_c, W = 8, 12, 256, 512
+    say("case sw backward 16K", B, H, n_c, W)
+    (q, k, v, do), (dq, dk, dv) = _sw_grads(B, H, n_c, W, seed=4)
+    rng = np.random.default_rng(1)
+    L = 64 * n_c
+    got, ref = {n: [] for n in ("dq", "dk", "dv")}, {n: [] for n in ("dq", "dk", "dv")}
+    for pos in np.concatenate([[0, 63, 64, 511, 512, L - 1], rng.integers(0, L, 6)]):
+        b, h = rng.integers(0, B), rng.integers(0, H)
+        lo, hi = max(0, pos - W + 1), min(L, pos + W)  # every query and key that reaches pos
+        sl = (slice(b, b + 1), slice(h, h + 1), slice(lo, hi))
+        r = O.sw_attention_backward(_f64(q[sl]), _f64(k[sl]), _f64(v[sl]), _f64(do[sl]), W)
+        for n, g, rr in zip(("dq", "dk", "dv"), (dq, dk, dv), r):
+            got[n].append(_f64(g[b, h, pos]))
+            ref[n].append(rr[0, 0, pos - lo])
+    for n in got:
+        assert_close(n + " sampled", np.array(got[n]), np.array(ref[n]), "bf16")

@@ -589,3 +589,36 @@ def test_sw_attention_special_cases():
     ref = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)), is_causal=True,
                                                            scale=0.125)
     np.testing.assert_allclose(oc, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 64, 150])
+def test_sw_attention_backward_matches_autograd(window):
+    rng = np.random.default_rng(window + 1)
+    B, H, L, d = 1, 2, 200, 16
+    q, k, v, do = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+    dq, dk, dv = O.sw_attention_backward(q, k, v, do, window, attn_scale=0.3)
+    t = [torch.from_numpy(x).requires_grad_(True) for x in (q, k, v)]
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=(j <= i) & (j > i - window), scale=0.3)
+    o.backward(torch.from_numpy(do))
+    for name, got, ref in (("dq", dq, t[0].grad), ("dk", dk, t[1].grad), ("dv", dv, t[2].grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+def test_sw_attention_backward_finite_difference():
+    rng = np.random.default_rng(5)
+    B, H, L, d, W = 1, 1, 40, 4, 7
+    q, k, v, do = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+    dq, dk, dv = O.sw_attention_backward(q, k, v, do, W, attn_scale=0.5)
+    eps = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for _ in range(5):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + eps
+            up = (O.sw_attention(q, k, v, W, attn_scale=0.5)[0] * do).sum()
+            arr[idx] = old - eps
+            dn = (O.sw_attention(q, k, v, W, attn_scale=0.5)[0] * do).sum()
+            arr[idx] = old
+            assert abs((up - dn) / (2 * eps) - grad[idx]) < 1e-6
