@@ -186,6 +186,58 @@ def landmark_timing(shape, cfg, dev, bufs, iters=50):
             "hbm_bound_us": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6}
 
 
+def window_timing(B=8, H=12, n_c=256, window=512, iters=10):
+    """Sliding-window self-attention beside GCA (W = 512) at the training shape: gca_sw_forward +
+    gca_sw_backward on synthetic bf16 inputs, timed apart from the GCA step."""
+    import torch
+
+    from long_context_lm_amd import gca
+
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    q, k, v, do = (torch.randn((B, H, 64 * n_c, 64), generator=gen, device="cuda", dtype=torch.bfloat16)
+                   for _ in range(4))
+    cfg = gca.sw_config(B, H, n_c)
+    ws = torch.empty(gca.workspace_size(gca.OP_SW_BACKWARD, cfg), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+
+    def one():
+        gca.sw_forward(cfg, q, k, v, window, o=o, lse=lse)
+        gca.sw_backward(cfg, q, k, v, o, lse, do, window, ws=ws, out=grads)
+
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    gca.profile_collect()
+    gca.profile_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    gca.profile_enable(False)
+    kern = {kk: vv[0] / vv[1] * 1e3 for kk, vv in gca.profile_collect().items()}
+    us = a.elapsed_time(b) / iters * 1e3
+    L = 64 * n_c
+    pairs = sum(min(i + 1, window) for i in range(L))  # (query, key) pairs per (batch row, head)
+    fwd_flops = 4 * 64 * pairs * B * H      # q.k and p.v
+    bwd_flops = 8 * 64 * pairs * B * H      # dp, dq, dk, dv
+    res = {"workload": f"B={B} L={L} H={H} d=64 W={window} bf16", "us_per_step": us, "kernels_us": kern,
+           "tokens_per_s": B * L / (us * 1e-6), "algorithmic_flops_fwd": fwd_flops, "algorithmic_flops_bwd": bwd_flops}
+    fwd_us = kern.get("sw_fwd", 0.0)
+    bwd_us = kern.get("sw_bwd_query", 0.0) + kern.get("sw_bwd_key", 0.0)
+    if fwd_us > 0:
+        res["fwd_tflops"] = fwd_flops / (fwd_us * 1e-6) / 1e12
+    if bwd_us > 0:
+        res["bwd_tflops"] = bwd_flops / (bwd_us * 1e-6) / 1e12
+    res["mfma_frac"] = (fwd_flops + bwd_flops) / (us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12)
+    del q, k, v, do, o, lse, grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def inference_latency(shape, iters=50):
     """Per-chunk retrieve + attend latency over a long history held in HBM (warm and cold)."""
     import torch
@@ -501,6 +553,12 @@ def main():
     infer = None
     del dev, bufs
     torch.cuda.empty_cache()
+    log("sliding-window attention beside GCA (W = 512), forward + backward at the training shape")
+    sw = window_timing()
+    log(f"  {sw['us_per_step']:.1f} us per fwd+bwd ({sw['tokens_per_s'] / 1e6:.1f} M tokens/s); "
+        + ", ".join(f"{k} {v:.1f}" for k, v in sw["kernels_us"].items())
+        + f"; fwd {sw.get('fwd_tflops', 0):.0f} TFLOP/s, bwd {sw.get('bwd_tflops', 0):.0f} TFLOP/s, "
+        f"matrix-core fraction {sw['mfma_frac']:.3f}")
     if not args.no_inference:
         infer = {}
         for label, shp in (("1M", I.INFER_1M), ("16M", I.INFER_16M)):
@@ -546,6 +604,7 @@ def main():
         "kernels": kernels,
         "inference_latency": infer,
         "landmark_backward": lmk,
+        "sliding_window": sw,
     }
     print(json.dumps(out), flush=True)
 

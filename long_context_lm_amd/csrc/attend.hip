@@ -1232,6 +1232,16 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
         pacc[qh] = mma(off.kfrag(Ds, qh, s), vf[s], pacc[qh]);
       }
     }
+    if (lower_edge || diagonal) {  // wave-uniform: only the two edge query tiles are masked
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int query = 32 * qh + 16 * hl + r;  // sacc[qh][r] = S[query][key my_u]
+          const bool out = (lower_edge && my_u <= query) || (diagonal && my_u > query);
+          sacc[qh][r] = out ? -__builtin_inff() : sacc[qh][r];
+        }
+    }
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       // lane holds queries 32 qh + 16 hl + r of key my_u
@@ -1245,11 +1255,9 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
         float xp[8], xz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int r = 8 * half + e, query = q0 + e;
-          const bool out = (lower_edge && my_u <= query) || (diagonal && my_u > query);
-          const float z = out ? -__builtin_inff() : sacc[qh][r];
+          const int r = 8 * half + e;
           const float bias_q = be[e >> 1][2 * (e & 1)], d_q = be[e >> 1][2 * (e & 1) + 1];
-          const float pw = fast_exp2(__builtin_fmaf(z, c2, bias_q));
+          const float pw = fast_exp2(__builtin_fmaf(sacc[qh][r], c2, bias_q));
           xp[e] = pw;
           xz[e] = pw * (pacc[qh][r] - d_q);
         }
