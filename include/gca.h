@@ -15,7 +15,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major (last index fastest), in device memory, owned by the
- *     caller.  The library never allocates, frees or synchronises, keeps no state between
+ *     caller (the one exception: gca_fetch_chunks also reads its K/V sources from pinned host
+ *     memory).  The library never allocates, frees or synchronises, keeps no state between
  *     calls, and enqueues all work on `stream` (a hipStream_t; NULL = the null stream).
  *     Calls that share a workspace must be ordered on one stream.
  *   - Floating tensors q, k, v, o, dout, dq, dk, dv, lq, lk use `problem->dtype`
@@ -27,6 +28,9 @@
  *       k, v, dk, dv    [B, H, n_kv*S, d]      shared by all G groups
  *       idx, score, dscore [G, B, n_q, topk]
  *       lse    [G, B, H, n_q, topk, S]   (per query chunk and slot, the chunk's S tokens)
+ *     Token-level decode: q, o [G, B, H, n_tokens, d].  Fetched chunks: k_out, v_out
+ *     [B, H, G*n_q*topk*S, d].  Sliding-window attention (one sequence of L = n_q*S tokens per
+ *     batch row and head): q, k, v, o, dout, dq, dk, dv [B, H, L, d] and lse [B, H, L].
  *   - Row r of a retrieval is global chunk i = q_chunk_base + r; its candidates are the
  *     chunks j < min(i, n_kv).  Query chunk t uses row t - shift (shift = 1 in training, where
  *     the landmark of chunk t-1 retrieves for chunk t; shift = 0 when the caller passes the
@@ -38,8 +42,9 @@
  *     nothing when it returns an error.  A launch failure returns GCA_ERR_HIP; the HIP code
  *     is then available from gca_last_hip_error() (per calling thread).  Faults inside
  *     kernels surface at the caller's next synchronisation.
- *   - Outputs are fully overwritten; inputs are read only.  Results are bit-identical from
- *     run to run (no floating-point atomics anywhere).
+ *   - Outputs are fully overwritten (gca_fetch_chunks writes only the tiles of slots in range);
+ *     inputs are read only.  Results are bit-identical from run to run (no floating-point
+ *     atomics anywhere).
  *   - gca_retrieve and gca_forward with n_q_chunks = 0 validate and return GCA_OK without
  *     launching anything; gca_backward with n_q_chunks = 0 still writes zero dk and dv.
  */
