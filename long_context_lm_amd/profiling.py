@@ -24,6 +24,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,8 +44,10 @@ def source_hash() -> str:
 
 
 def short_name(kernel: str):
+    # whole kernel names (with an optional variant suffix, e.g. attend_fwd_wave_kernel) only:
+    # "bwd_query" must not match sw_bwd_query_kernel
     for s in SHORT:
-        if s in kernel:
+        if re.search(r"(?<![A-Za-z0-9_])" + s + r"(_[a-z]+)?_kernel\b", kernel):
             return s
     if "copy" in kernel.lower() or "elementwise" in kernel.lower():
         return "copy"
