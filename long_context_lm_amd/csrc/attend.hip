@@ -742,7 +742,12 @@ __global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qh][tt][r]);
       mx = xor32_max(mx) * c2;  // log2 units
-      const float m_new = fmaxf(m_run[qh], mx);
+      // The running maximum moves only when a new score exceeds it by more than kLazy (or on the
+      // first keys): otherwise the exps run against the stale maximum, stay below 2^kLazy, and the
+      // rescale of the accumulators is skipped (a wave-uniform decision).
+      constexpr float kLazy = 8.f;
+      const bool grow = __ballot(mx > m_run[qh] + kLazy) != 0;
+      const float m_new = grow ? fmaxf(m_run[qh], mx) : m_run[qh];
       const bool none = m_new == -__builtin_inff();  // no key of the window seen yet
       const float alpha = none ? 1.f : fast_exp2(m_run[qh] - m_new);
       const float bias = none ? 0.f : -m_new;
@@ -756,10 +761,12 @@ __global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
         }
       l_run[qh] = l_run[qh] * alpha + xor32_sum(l);
       m_run[qh] = m_new;
+      if (grow) {
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qh][dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[qh][dt][r] *= alpha;
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float x[8];
