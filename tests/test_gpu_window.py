@@ -114,3 +114,43 @@ def test_sw_backward_training_shape_sampled():
             ref[n].append(rr[0, 0, pos - lo])
     for n in got:
         assert_close(n + " sampled", np.array(got[n]), np.array(ref[n]), "bf16")
+
+
+def _membership_inputs(B, H, n_c):
+    """k = 0 makes every score 0, so P is uniform over each token's window; v[j] = one-hot of
+    j mod 64 then makes o[i] the histogram (by residue) of the keys in token i's window."""
+    L = 64 * n_c
+    q = torch.randn((B, H, L, 64), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    k = torch.zeros((B, H, L, 64), dtype=torch.bfloat16)
+    v = torch.zeros((B, H, L, 64), dtype=torch.bfloat16)
+    v[:, :, torch.arange(L), torch.arange(L) % 64] = 1.0
+    return q, k, v
+
+
+@pytest.mark.parametrize("window", [64, 128, 512])
+def test_sw_window_membership_is_exact(window):
+    """Which keys every token attends to, checked bit for bit: for tokens with a full window,
+    P = 1/W is exact in bf16 and o[i, d] = #{j in (i - W, i] : j = d mod 64} / W; in the backward
+    with dO one-hot, dq is exactly 0 (k = 0) and dv[j, d] = #{i in [j, j + W) : i = d mod 64,
+    i < L} / W for keys whose covering queries all have full windows."""
+    B, H, n_c = 1, 2, 11
+    L = 64 * n_c
+    say("case window membership", window)
+    q, k, v = _membership_inputs(B, H, n_c)
+    cfg = gca.sw_config(B, H, n_c)
+    o, lse = gca.sw_forward(cfg, q.cuda(), k.cuda(), v.cuda(), window)
+    dout = torch.zeros((B, H, L, 64), dtype=torch.bfloat16)
+    dout[:, :, torch.arange(L), torch.arange(L) % 64] = float(window)
+    dq, dk, dv = gca.sw_backward(cfg, q.cuda(), k.cuda(), v.cuda(), o, lse, dout.cuda(), window)
+    torch.cuda.synchronize()
+    o, dq, dv = _f64(o), _f64(dq), _f64(dv)
+    i = np.arange(L)
+    for tok in range(window - 1, L):
+        keys = np.arange(tok - window + 1, tok + 1)
+        expect = np.bincount(keys % 64, minlength=64) / window
+        assert np.array_equal(o[0, 0, tok], expect) and np.array_equal(o[0, 1, tok], expect), f"o, token {tok}"
+    assert not dq.any(), "dq must be exactly zero when k = 0"
+    for j in range(window - 1, L):
+        qs = i[(i >= j) & (i < j + window)]
+        expect = np.bincount(qs % 64, minlength=64).astype(np.float64)
+        assert np.array_equal(dv[0, 0, j], expect), f"dv, key {j}"
