@@ -167,8 +167,7 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
  *   o[b,h,i,:] = sum_j softmax_j(attn_scale q[b,h,i,:] . k[b,h,j,:]) v[b,h,j,:]
  *   lse[b,h,i] = log sum_j exp(attn_scale q[b,h,i,:] . k[b,h,j,:])   (natural log)
  * window = W: a positive multiple of 64 (a window longer than the sequence is causal attention).
- * q, k, v, o [B,H,L,64] bf16 (GCA_F32 is GCA_ERR_UNSUPPORTED here); lse [B,H,L] fp32, may be NULL
- * (the backward needs it).  Requires G = 1 and n_kv_chunks = n_q_chunks; uses B, H, n_q_chunks,
+ * q, k, v, o [B,H,L,64] (problem->dtype); lse [B,H,L] fp32, may be NULL (the backward needs it).  Requires G = 1 and n_kv_chunks = n_q_chunks; uses B, H, n_q_chunks,
  * attn_scale of problem.  No workspace.
  */
 gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void* q, const void* k,
@@ -178,9 +177,9 @@ gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void
  * Backward of gca_sw_forward: with P the window softmax, dP = dout v^T and D = <dout, o> per
  * token,
  *   dS = P (dP - D),  dq = attn_scale dS k,  dk = attn_scale dS^T q,  dv = P^T dout,
- * in fp32 over fixed orders without atomics (bit-identical from run to run), rounded once to bf16.
- * q, k, v, o and lse (from gca_sw_forward), dout: inputs [B,H,L,64] bf16 (lse [B,H,L] fp32); dq,
- * dk, dv: outputs like q.  ws: >= gca_workspace_size(SW_BACKWARD) = B*H*L*8 bytes (per-token
+ * in fp32 over fixed orders without atomics (bit-identical from run to run), rounded once to dtype.
+ * q, k, v, o and lse (from gca_sw_forward), dout: inputs [B,H,L,64] (lse [B,H,L] fp32); dq, dk, dv:
+ * outputs like q.  ws: >= gca_workspace_size(SW_BACKWARD) = B*H*L*8 bytes (per-token
  * {-lse log2 e, D}; contents need no setup).  Same problem rules as gca_sw_forward.
  */
 gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const void* q, const void* k,

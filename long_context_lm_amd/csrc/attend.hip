@@ -674,6 +674,20 @@ __device__ __forceinline__ void sw_mask(f32x16_t (&sacc)[2][2], bool lower_edge,
       }
 }
 
+__device__ __forceinline__ void sw_mask_keys_major(f32x16_t (&sacc)[2], int query_base, bool lower_edge,
+                                                   bool diagonal) {
+  // query-major accumulators: sacc[tt][r] = S[query query_base + li][key 32 tt + 16 hl + r]
+  const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * tt + 16 * hl + r, query = query_base + li;
+      const bool out = (lower_edge && key <= query) || (diagonal && key > query);
+      sacc[tt][r] = out ? -__builtin_inff() : sacc[tt][r];
+    }
+}
+
 // One wave per query tile, as the bf16 GCA forward: K and V tiles stream through single LDS
 // buffers with the same counted-copy pipeline, and the softmax is online (running maximum and sum
 // per query; the output accumulators are rescaled when the maximum grows).
@@ -805,6 +819,111 @@ __global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
     if (p.lse && hl == qh)  // lane (li, hl) writes query 32 hl + li
       p.lse[qrow0 + 32 * qh + li] = m_run[qh] * kLn2f + __builtin_amdgcn_logf(l_run[qh]) * kLn2f;
   }
+}
+
+// Two waves of 32 queries per query tile, for fp32 tiles (the one-wave forward's registers hold
+// bf16 fragments only): the pipeline of the two-wave GCA forward, single K and V buffers
+// published by barriers, with the same online softmax and edge masks.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sw_fwd2_kernel(SwParams p) {
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, kWaves>;
+  constexpr int kC = Off::kCopies;
+  __shared__ __align__(1024) char Ks[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hl = lane >> 5;
+  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t t = lid % p.n_c;
+  const int64_t bh = lid / p.n_c;
+  const int64_t row0 = bh * p.n_c * kChunk;
+  const int64_t qrow0 = row0 + t * kChunk;
+  const int my_q = 32 * wave + li;
+
+  Frag<T> qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s].load(static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim + 16 * s + 8 * hl);
+  Off off;
+  off.init(wave);
+  const int64_t kt0 = t - p.m > 0 ? t - p.m : 0;
+  auto tile = [&](const void* base, int64_t kt) {
+    return static_cast<const T*>(base) + (row0 + kt * kChunk) * kDim;
+  };
+  off.copy(tile(p.k, kt0), Ks, wave);
+  off.copy(tile(p.v, kt0), Vs, wave);
+  barrier_copies_landed<kC>();  // K(kt0) landed and visible; V(kt0) may still be in flight
+
+  f32x16_t oacc[2] = {zero16(), zero16()};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  const float c2 = p.attn_scale * kLog2e;
+  for (int64_t kt = kt0; kt <= t; ++kt) {
+    const bool more = kt < t;
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sacc[tt] = mma(off.kfrag(Ks, tt, s), qf[s], sacc[tt]);
+    }
+    barrier_lds_reads_done();  // every wave has read K(kt)
+    if (more) off.copy(tile(p.k, kt + 1), Ks, wave);
+    const bool lower_edge = kt == t - p.m, diagonal = kt == t;
+    if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[tt][r]);
+    mx = xor32_max(mx) * c2;
+    constexpr float kLazy = 8.f;
+    const bool grow = __ballot(mx > m_run + kLazy) != 0;
+    const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+    const bool none = m_new == -__builtin_inff();
+    const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+    const float bias = none ? 0.f : -m_new;
+    float l = 0.f;
+    Frag<T> pf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + e], c2, bias));
+        l += x[e];
+      }
+      pf[s].set(x);
+    }
+    l_run = l_run * alpha + xor32_sum(l);
+    m_run = m_new;
+    if (grow) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    if (more) barrier_copies_landed<kC>();  // V(kt) landed and visible (K(kt + 1) may be in flight)
+    else barrier_copies_landed<0>();
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) oacc[dt] = mma(off.vfrag(Vs, s, dt), pf[s], oacc[dt]);
+    if (more) {
+      barrier_lds_reads_done();  // every wave has read V(kt)
+      off.copy(tile(p.v, kt + 1), Vs, wave);
+      barrier_copies_landed<kC>();  // K(kt + 1) landed (V(kt + 1) may not)
+    }
+  }
+  const float f = __builtin_amdgcn_rcpf(l_run);
+  T* o = static_cast<T*>(p.o) + (qrow0 + my_q) * kDim;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4(o + 32 * dt + 8 * a + 4 * hl, f * oacc[dt][4 * a], f * oacc[dt][4 * a + 1], f * oacc[dt][4 * a + 2],
+             f * oacc[dt][4 * a + 3]);
+  if (p.lse && hl == 0) p.lse[qrow0 + my_q] = m_run * kLn2f + __builtin_amdgcn_logf(l_run) * kLn2f;
 }
 
 // ------------------------------------------------------------- token-level decode
@@ -1057,22 +1176,30 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 // stored output and writes {-lse log2 e, D} per query, which the key-major pass reads as the GCA
 // key-major pass reads its {bias, e} vectors.  Masked scores become -inf before the exp, so their
 // P and dS are exactly 0.
-__device__ __forceinline__ void sw_mask_keys_major(f32x16_t (&sacc)[2], int query_base, bool lower_edge,
-                                                   bool diagonal) {
-  // query-major accumulators: sacc[tt][r] = S[query query_base + li][key 32 tt + 16 hl + r]
-  const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
+
+// <a, b> over one lane's eight fragment elements
+__device__ __forceinline__ float frag_dot(const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  float acc = 0.f;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = a.v[w], y = b.v[w];
+    acc = __builtin_fmaf(__uint_as_float(x << 16), __uint_as_float(y << 16), acc);
+    acc = __builtin_fmaf(__uint_as_float(x & 0xffff0000u), __uint_as_float(y & 0xffff0000u), acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_dot(const Frag<float>& a, const Frag<float>& b) {
+  float acc = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * tt + 16 * hl + r, query = query_base + li;
-      const bool out = (lower_edge && key <= query) || (diagonal && key > query);
-      sacc[tt][r] = out ? -__builtin_inff() : sacc[tt][r];
-    }
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_fmaf(a.v0[i], b.v0[i], acc);
+    acc = __builtin_fmaf(a.v1[i], b.v1[i], acc);
+  }
+  return acc;
 }
 
+template <typename T>
 __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
-  using T = bf16_t;
   using TL = Tile<T>;
   using Off = TileOffsets<T, kWaves>;
   __shared__ __align__(1024) char Ka[TL::kBytes];
@@ -1100,13 +1227,7 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
   // D = <dO, O> of this lane's query (lanes l and l ^ 32 hold its two halves of the dimensions)
   float dd = 0.f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a = df[s].v[w], c = of[s].v[w];
-      dd = __builtin_fmaf(__uint_as_float(a << 16), __uint_as_float(c << 16), dd);
-      dd = __builtin_fmaf(__uint_as_float(a & 0xffff0000u), __uint_as_float(c & 0xffff0000u), dd);
-    }
+  for (int s = 0; s < 4; ++s) dd += frag_dot(df[s], of[s]);
   const float D = xor32_sum(dd);
   const float bias = -p.lse_in[my_row] * kLog2e;
   if (hl == 0) reinterpret_cast<f32x2_t*>(p.stats)[my_row] = f32x2_t{bias, D};
@@ -1181,8 +1302,8 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
 // Key-major pass: one workgroup of two waves (32 keys each) per key tile kt walks the query tiles
 // kt .. kt + m whose windows reach it, double-buffered like the GCA key-major pass (Q tile, dO
 // tile and the 64 {bias, D} pairs of the next query tile copied in at the start of the current).
+template <typename T>
 __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
-  using T = bf16_t;
   using TL = Tile<T>;
   using Off = TileOffsets<T, kWaves>;
   constexpr int kVecBytes = kChunk * 8;
@@ -1604,20 +1725,24 @@ hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, 
   return hipGetLastError();
 }
 
-hipError_t launch_sw_fwd(const SwParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(sw_fwd_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)), dim3(64), 0, s, p);
+hipError_t launch_sw_fwd(const SwParams& p, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c));
+  if (f32) hipLaunchKernelGGL(sw_fwd2_kernel<float>, grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(sw_fwd_kernel, grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_sw_bwd_query(const SwParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(sw_bwd_query_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)),
-                     dim3(kThreads), 0, s, p);
+hipError_t launch_sw_bwd_query(const SwParams& p, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c));
+  if (f32) hipLaunchKernelGGL(sw_bwd_query_kernel<float>, grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(sw_bwd_query_kernel<bf16_t>, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_sw_bwd_key(const SwParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(sw_bwd_key_kernel, dim3(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c)),
-                     dim3(kThreads), 0, s, p);
+hipError_t launch_sw_bwd_key(const SwParams& p, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.B) * p.H * p.n_c));
+  if (f32) hipLaunchKernelGGL(sw_bwd_key_kernel<float>, grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(sw_bwd_key_kernel<bf16_t>, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -434,7 +434,6 @@ static gca_status sw_check(const gca_problem* p, int32_t window) {
   GCA_TRY(validate_problem(p));
   if (p->G != 1 || p->n_kv_chunks != p->n_q_chunks) return GCA_ERR_INVALID_ARGUMENT;
   if (window < 64 || window % 64 != 0) return GCA_ERR_INVALID_ARGUMENT;
-  if (p->dtype != GCA_BF16) return GCA_ERR_UNSUPPORTED;
   return GCA_OK;
 }
 
@@ -465,7 +464,8 @@ gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void
   w.o = o;
   w.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return launch(kSwFwd, s, [&] { return launch_sw_fwd(w, s); });
+  const bool f32 = problem->dtype == GCA_F32;
+  return launch(kSwFwd, s, [&] { return launch_sw_fwd(w, f32, s); });
 }
 
 gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const void* q, const void* k, const void* v,
@@ -493,8 +493,9 @@ gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const voi
   w.dv = dv;
   w.stats = static_cast<float*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  GCA_TRY(launch(kSwBwdQuery, s, [&] { return launch_sw_bwd_query(w, s); }));
-  return launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(w, s); });
+  const bool f32 = problem->dtype == GCA_F32;
+  GCA_TRY(launch(kSwBwdQuery, s, [&] { return launch_sw_bwd_query(w, f32, s); }));
+  return launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(w, f32, s); });
 }
 
 // The device address of a K/V source: device memory as it is; pinned host memory (hipHostMalloc)

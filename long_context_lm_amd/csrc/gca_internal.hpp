@@ -130,8 +130,8 @@ hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t 
 hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_fetch_chunks(const FetchParams& p, bool f32, hipStream_t s);
 hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, hipStream_t s);
-hipError_t launch_sw_fwd(const SwParams& p, hipStream_t s);
-hipError_t launch_sw_bwd_query(const SwParams& p, hipStream_t s);
-hipError_t launch_sw_bwd_key(const SwParams& p, hipStream_t s);
+hipError_t launch_sw_fwd(const SwParams& p, bool f32, hipStream_t s);
+hipError_t launch_sw_bwd_query(const SwParams& p, bool f32, hipStream_t s);
+hipError_t launch_sw_bwd_key(const SwParams& p, bool f32, hipStream_t s);
 
 }  // namespace gca

@@ -181,7 +181,7 @@ def test_pointer_checks():
     assert lib.gca_sw_forward(ctypes.byref(sw), 512, mis, z, z, z, None, None) == MISALIGNED
     for window in (0, -64, 100):
         assert lib.gca_sw_forward(ctypes.byref(sw), window, z, z, z, z, None, None) == INVALID
-    for field, value, status in (("G", 2, INVALID), ("n_kv_chunks", 9, INVALID), ("dtype", 1, UNSUPPORTED)):
+    for field, value, status in (("G", 2, INVALID), ("n_kv_chunks", 9, INVALID), ("dtype", 2, INVALID)):
         bad = gca.sw_config(2, 3, 8).problem()
         setattr(bad, field, value)
         assert lib.gca_sw_forward(ctypes.byref(bad), 512, z, z, z, z, None, None) == status
