@@ -55,6 +55,11 @@ EXPORTS = (
     "gca_last_hip_error",
     "gca_profile_enable",
     "gca_profile_collect",
+    "gca_landmark_backward",
+    "gca_fetch_chunks",
+    "gca_decode_tokens",
+    "gca_sw_forward",
+    "gca_sw_backward",
 )
 
 _lib = None

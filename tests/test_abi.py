@@ -35,7 +35,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = gca.load()
     names = declared_functions()
-    assert set(gca.EXPORTS) <= set(names)
+    assert set(gca.EXPORTS) == set(names)  # the binding knows every declared entry point
     for n in names:
         assert hasattr(lib, n), f"libgca.so does not export {n}"
 
