@@ -38,9 +38,11 @@ thread_local ProfState t_prof;
 // step) take four, so that a long history still gives enough waves.  cpt starts at 1 and doubles
 // while the grid would exceed kRetrieveMaxWaves waves and a row still spans several blocks; rows
 // spanning several blocks are merged by a second kernel.  The 16M-token history (262,144
-// candidates per row, two rows) runs as 1,024 workgroups of four waves, two candidates per lane,
-// whose loads are all in flight at once; the 16K training step as 4,096 single waves of four.
-constexpr int64_t kRetrieveMaxWaves = 4096;
+// candidates per row, two rows) runs as 512 workgroups of four waves, four candidates per lane
+// (two resident per CU, all loads in flight at once): half the partial lists of a 4,096-wave
+// grid, which the merge pays for, at the same scan time.  The 16K training step runs as 4,096
+// single waves of four candidates per lane (one block per row, whatever the cap).
+constexpr int64_t kRetrieveMaxWaves = 2048;
 constexpr int64_t kRetrieveManyRows = 1024;
 constexpr size_t kAlign = 256;
 

@@ -16,7 +16,7 @@
 // waves); each lane keeps a sorted list of its best keys, each wave extracts its top K with K
 // rounds of a wave-wide maximum, and the wave lists are merged through LDS.  Rows with more candidates
 // than one block are split over several workgroups whose partial top-K lists a second kernel
-// merges (the 16M-token history: 262,144 candidates per row, 512 blocks of 512).
+// merges (the 16M-token history: 262,144 candidates per row, 256 blocks of 1,024).
 #include "gca_device.hpp"
 #include "gca_internal.hpp"
 

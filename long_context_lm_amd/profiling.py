@@ -123,7 +123,7 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
     inf = res.get("inference_latency") or {}
     # launch shapes of the decode steps (G = 2 rows of one batch row, H = 12, K = 8)
     shapes = {("score_topk", 128, 256): "1M scan (2 rows x 64 blocks)", ("topk_merge", 2, 1024): "1M / 16M merge",
-              ("score_topk", 1024, 256): "16M scan (2 rows x 512 blocks)", ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)",
+              ("score_topk", 512, 256): "16M scan (2 rows x 256 blocks)", ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)",
               ("fetch_chunks", 192, 256): "host-memory K/V fetch (2 groups x 8 slots x 12 heads, 3 MiB)",
               ("decode_tokens", 24, 512): "one-token decode, 16M history (2 groups x 12 heads)"}
     lines = [

@@ -112,12 +112,12 @@ def test_workspace_sizes():
     assert gca.workspace_size(gca.OP_FORWARD, c) == 0
     bw = gca.workspace_size(gca.OP_BACKWARD, c)
     assert bw >= 2 * 8 * 12 * 256 * 64 * 8 * 4  # per-(token, slot) e values
-    # 16M-token history: 512 blocks of 512 candidates per row and group, 8 partial keys each
+    # 16M-token history: 256 blocks of 1024 candidates per row and group, 8 partial keys each
     c = gca.Config(B=1, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
-    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 2 * 512 * 8 * 8 + 2 * 512 * 8 * 4
-    # more rows: blocks grow (cpt doubles) until the grid is at most 1024 workgroups
+    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 2 * 256 * 8 * 8 + 2 * 256 * 8 * 4
+    # more rows: blocks grow (cpt doubles) until the grid is at most 2048 waves
     c = gca.Config(B=8, G=2, H=12, n_q=1, n_kv=262144, topk=8, q_chunk_base=262144, shift=0)
-    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 16 * 64 * 8 * 8 + 16 * 64 * 8 * 4
+    assert gca.workspace_size(gca.OP_RETRIEVE, c) == 16 * 32 * 8 * 8 + 16 * 32 * 8 * 4
     # landmark gradients: the inverse index over every row ({code, value} pairs) and its counts
     c = gca.Config(B=8, G=2, H=12, n_q=256, n_kv=256, topk=8)
     assert gca.workspace_size(gca.OP_LANDMARK_BACKWARD, c) == 8 * 256 * 2 * 256 * 2 * 4 + 8 * 256 * 4
