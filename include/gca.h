@@ -32,7 +32,9 @@
  *     [B, H, G*n_q*topk*S, d].  Sliding-window attention (one sequence of L = n_q*S tokens per
  *     batch row and head): q, k, v, o, dout, dq, dk, dv [B, H, L, d] and lse [B, H, L].
  *   - Row r of a retrieval is global chunk i = q_chunk_base + r; its candidates are the
- *     chunks j < min(i, n_kv).  Query chunk t uses row t - shift (shift = 1 in training, where
+ *     chunks j < min(i, n_kv).  The valid slots of a row name distinct chunks (gca_retrieve
+ *     guarantees it); idx rows given to gca_backward or gca_landmark_backward must keep to that,
+ *     since their key-side sums count a row once per chunk.  Query chunk t uses row t - shift (shift = 1 in training, where
  *     the landmark of chunk t-1 retrieves for chunk t; shift = 0 when the caller passes the
  *     landmark of the chunk being generated).  Query chunks whose row is missing or has no
  *     valid slot get o = 0, lse = -inf, dq = 0.

@@ -1583,7 +1583,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
 // words.  Phase 1: one thread per row ORs the row's bit into the mask of every chunk of this
 // block the row names (integer OR: the result does not depend on the order).  Phase 2: a running
 // prefix of the masks' popcounts gives every (word, chunk) its first output position.  Phase 3:
-// each (chunk, word) writes its rows' entries there, in row order.  Only rows that feed a query
+// one thread per row writes each of its entries at that position plus the row's rank among the
+// word's rows naming the chunk, so each chunk's entries come out in row order.  Only rows that feed a query
 // chunk (row + shift < n_q) and can hold a chunk of this block (global chunk index q_base + row
 // above the block's first chunk) are marked.  Runs after the query-major pass, which writes the
 // fusion weights.
@@ -1597,7 +1598,7 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
   __shared__ uint32_t mask[kIdxWords][64];
   __shared__ int32_t first[kIdxWords][64];
   __shared__ int32_t total[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int32_t nblk = static_cast<int32_t>((p.n_kv + 63) / 64);
   const int b = static_cast<int>(blockIdx.x / nblk);
   const int32_t j0 = static_cast<int32_t>(blockIdx.x % nblk) * 64;
@@ -1609,7 +1610,7 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
   const int32_t n_rows = p.G * nq;
   const int K = p.K;
   if (tid < 64) total[tid] = 0;
-  i32x2_t* out = reinterpret_cast<i32x2_t*>(p.pairs) + (static_cast<int64_t>(b) * p.n_kv + j) * p.pair_cap;
+  i32x2_t* out_b = reinterpret_cast<i32x2_t*>(p.pairs) + static_cast<int64_t>(b) * p.n_kv * p.pair_cap;
 
   for (int32_t gr0 = 0; gr0 < n_rows; gr0 += kIdxRows) {
     const int32_t nr = n_rows - gr0 < kIdxRows ? n_rows - gr0 : kIdxRows;
@@ -1649,18 +1650,29 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
       total[tid] = run;
     }
     __syncthreads();
-    // phase 3: entries
-    if (j < p.n_kv) {
-      for (int wl = wave; wl < nw; wl += kIdxThreads / 64) {
-        uint32_t m = mask[wl][lane];
-        int32_t pos = first[wl][lane];
-        while (m) {
-          const int bit = __ffs(m) - 1;
-          m &= m - 1;
-          const int lr = wl * 32 + bit;
-          int k = 0;
-          while (idx_s[lr][k] != j) ++k;  // the first slot naming j; one exists (mask bit)
-          out[pos++] = i32x2_t{(gr0 + lr) * K + k, __float_as_int(wts_s[lr][k])};
+    // phase 3: one thread per row writes the entries of its slots that name chunks of this block,
+    // each at its chunk's count before the row's word plus the row's rank among the word's rows
+    // naming the chunk (the mask bits below it), so every chunk's entries come out in row order.
+    // A row counts once per chunk, with its first slot naming it.
+    for (int lr = tid; lr < nr; lr += kIdxThreads) {
+      const int32_t gr = gr0 + lr;
+      const int32_t row = gr - (gr / nq) * nq;
+      if (row < row_lo || row >= row_hi) continue;
+      const int w = lr >> 5;
+      const uint32_t below = (1u << (lr & 31)) - 1u;
+      int32_t jv[kMaxTopk];
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) jv[k] = k < K ? idx_s[lr][k] : -1;
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {
+        const int32_t jk = jv[k];  // -1 beyond K
+        bool first_slot = jk >= j0 && jk < j0 + 64 && jk < p.n_kv;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) first_slot = first_slot && jv[k2] != jk;
+        if (first_slot) {
+          const int jj = jk - j0;
+          const int32_t pos = first[w][jj] + __popc(mask[w][jj] & below);
+          out_b[static_cast<int64_t>(jk) * p.pair_cap + pos] = i32x2_t{gr * K + k, __float_as_int(wts_s[lr][k])};
         }
       }
     }
