@@ -23,6 +23,12 @@ What is computed (all arithmetic in IEEE float64 unless a step says float32):
     scores receive gradients                       [Notes, Key designs: GCA],
                                                    [Notes, Background: entry point]
   * K/V are shared by all retrieval groups         [Notes, Key designs: GCA, last item]
+  * the retrieved chunks' K/V may be kept in host memory and loaded back at retrieval
+    (fetch_chunks)                                 [Notes, Key designs: memory-offload inference]
+  * tokens generated one at a time attend to the chunks retrieved once for their chunk
+    (decode_tokens)                                same
+  * sliding-window self-attention, W = 512, beside the retrieval
+    (sw_attention, sw_attention_backward)          [Notes, Loss / training strategy]
 
 Readings taken where the pages leave a step open (each is listed in the design doc):
   R1  score s_ij = fl32(fl32(sum_d lq[i,d]*lk[j,d]) * score_scale) + 0.0f, the sum taken in
@@ -38,6 +44,10 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
       carry idx = -1 and score = -inf; a token with no valid slot gets output 0.
   R7  attention inside a retrieved chunk is full (non-causal) over its 64 tokens, with
       z = attn_scale * <q, k>, no positional bias.
+  R8  the fetched chunks form a compact buffer, slot (g, b, r, s) -> chunk (g n_q + r) K + s.
+  R9  decoding the first n tokens of a chunk gives the chunk forward's first n rows.
+  R10 the sliding window of token i is tokens max(0, i - W + 1) .. i (causal, itself included),
+      one softmax of attn_scale <q, k>, no positional bias.
 
 Parity pins: every function here is pinned in tests/test_oracle_pins.py against brute force,
 library routines, closed forms, invariants and finite differences.
