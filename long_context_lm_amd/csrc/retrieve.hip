@@ -287,23 +287,29 @@ __device__ __forceinline__ void workgroup_topk(int K, uint64_t key, float sv, ui
 }
 
 // One workgroup of NW waves per (row, block of 64 NW cpt candidates).  Pass n of wave w scores
-// the 64 consecutive candidates starting at block start + 64 (NW n + w), one per lane; the next
-// pass's rows are loaded while the current pass is scored.  NW = 4 for a few long rows (a decode
-// step over a long history: many blocks per row, their lists merged by the workgroup and then by
-// topk_merge); NW = 1 for many short rows (training: one wave per row).  At most 128 VGPRs for
-// bf16 landmarks and lists of 8 (four resident waves per SIMD, enough loads in flight to stream a
-// long history); fp32 rows and lists of 16 keep two.  Each lane's list holds LL = min(K, cpt)
-// entries (rounded up to a power of two).
+// the 64 consecutive candidates starting at block start + 64 (NW n + w), one per lane.  NW = 4
+// for a few long rows (a decode step over a long history: many blocks per row, their lists
+// merged by the workgroup and then by topk_merge); NW = 1 for many short rows (training: one wave
+// per row).  Short rows and fp32 rows load the next pass into registers while the current pass
+// is scored: at most 128 VGPRs for bf16 landmarks and lists of 8 (four resident waves per SIMD),
+// two waves otherwise.  Long bf16 rows keep two passes in flight per wave in an LDS ring (two
+// workgroups per CU, which is what their grid of at most about two waves per SIMD fills).  Each
+// lane's list holds LL = min(K, cpt) entries (rounded up to a power of two).
 template <typename T, int LL, int NW>
-__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && LL <= 8) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && LL <= 8 && NW == 1) ? 4 : 2) void score_topk_kernel(RetrieveParams p) {
   using Stage = RowStage<T>;
   constexpr int kBlockCand = 64 * NW;  // candidates of one block per pass (one per lane)
+  // bf16 rows of a few long rows (a decode step) are copied straight into a two-stage LDS ring,
+  // two passes in flight per wave (64 KiB per workgroup, two workgroups per CU); the others go
+  // through registers, one pass ahead
+  constexpr bool kRing = NW > 1 && sizeof(T) == 2;
+  constexpr int kStages = kRing ? 2 : 1;
   __shared__ double lq_s[kDim];
-  __shared__ u32x4_t rows_s[NW][64 * Stage::P];
+  __shared__ u32x4_t rows_s[NW][kStages][64 * Stage::P];
   __shared__ uint64_t lkey[NW * kMaxTopk];
   __shared__ float ls[NW * kMaxTopk];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) : 0;
   const int64_t item = blockIdx.x;
   const int blk = static_cast<int>(item % p.nblk);
   const int64_t rowid = item / p.nblk;  // (g * B + b) * n_q + r
@@ -323,23 +329,10 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && LL <= 8) ? 4 : 2) void 
     const int64_t m = (ncand - jw + kBlockCand - 1) / kBlockCand;
     passes = m < p.cpt ? static_cast<int>(m) : p.cpt;
   }
-  Stage st;
-  if (passes > 0) st.load(lk, jw, ncand, lane);  // in flight while the query landmark is staged
-  if (threadIdx.x < kDim) lq_s[threadIdx.x] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, threadIdx.x);
-  __syncthreads();
-
-  u32x4_t* area = rows_s[wave];
-  for (int n = 0; n < passes; ++n) {
-    const int64_t j0 = jw + static_cast<int64_t>(n) * kBlockCand;
-    st.store(area, lane);
-    if (n + 1 < passes) st.load(lk, j0 + kBlockCand, ncand, lane);
+  auto score = [&](const u32x4_t* area, int64_t j0, const double* lqv) {
     const int64_t j = j0 + lane;
     if (j < ncand) {
-      // an opaque zero offset keeps the query landmark in LDS (read per candidate) instead of in
-      // 128 registers hoisted out of the loop
-      int zero = 0;
-      asm volatile("" : "+v"(zero));
-      const double acc = row_dot(area, lane, lq_s + zero, static_cast<const T*>(nullptr));
+      const double acc = row_dot(area, lane, lqv, static_cast<const T*>(nullptr));
       const float s = canon_zero(static_cast<float>(acc) * p.score_scale);
       float rkey = s;
       if (p.use_gumbel) {
@@ -348,6 +341,64 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && LL <= 8) ? 4 : 2) void 
         rkey = canon_zero(s + noise);
       }
       L.insert(make_key(rkey, j), s);
+    }
+  };
+
+  if constexpr (kRing) {
+    // Pass n's 64 rows go to stage n % 2.  Lane l's copy k lands at byte 16 l of the stage's
+    // k-th KiB, which is slot l % P of row r = k R + l / P, so it fetches the piece that the
+    // swizzle keeps in that slot.  Rows at or past ncand re-read row ncand - 1 (always a
+    // candidate here); their scores are never used.
+    auto issue = [&](int n, int stage) {  // wave-uniform
+      const int64_t j0 = jw + static_cast<int64_t>(n) * kBlockCand;
+      const char* g0 = reinterpret_cast<const char*>(lk + j0 * kDim);
+      char* dst = reinterpret_cast<char*>(rows_s[wave][stage]);
+      const int64_t last = ncand - 1 - j0;  // >= 0: every issued pass starts below ncand
+#pragma unroll
+      for (int k = 0; k < Stage::P; ++k) {
+        const int r = k * Stage::R + lane / Stage::P;
+        const int64_t row = r < last ? r : last;
+        const uint32_t off = static_cast<uint32_t>(row * Stage::kRowBytes) + 16u * Stage::slot(r, lane % Stage::P);
+        copy16_async_untracked(g0, off, dst + 1024 * k);
+      }
+    };
+    if (passes > 0) issue(0, 0);
+    if (passes > 1) issue(1, 1);
+    if (threadIdx.x < kDim) lq_s[threadIdx.x] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, threadIdx.x);
+    __syncthreads();
+    // the query landmark stays in 128 registers (this variant runs two waves per SIMD), so a pass
+    // reads only its rows from LDS
+    double lqr[kDim];
+#pragma unroll
+    for (int d = 0; d < kDim; ++d) lqr[d] = lq_s[d];
+    for (int n0 = 0; n0 < passes; n0 += 2) {
+#pragma unroll
+      for (int stage = 0; stage < 2; ++stage) {
+        const int n = n0 + stage;
+        if (n >= passes) break;  // wave-uniform
+        // pass n landed (only pass n + 1, issued after it, may still be in flight)
+        if (n + 1 < passes) wait_vm_outstanding<Stage::P>();
+        else wait_vm_outstanding<0>();
+        score(rows_s[wave][stage], jw + static_cast<int64_t>(n) * kBlockCand, lqr);
+        // every read of this stage has returned (its values are used above): refill it
+        if (n + 2 < passes) issue(n + 2, stage);
+      }
+    }
+  } else {
+    Stage st;
+    if (passes > 0) st.load(lk, jw, ncand, lane);  // in flight while the query landmark is staged
+    if (threadIdx.x < kDim) lq_s[threadIdx.x] = lmk_to_f64(static_cast<const T*>(p.lq) + rowid * kDim, threadIdx.x);
+    __syncthreads();
+    u32x4_t* area = rows_s[wave][0];
+    for (int n = 0; n < passes; ++n) {
+      const int64_t j0 = jw + static_cast<int64_t>(n) * kBlockCand;
+      st.store(area, lane);
+      if (n + 1 < passes) st.load(lk, j0 + kBlockCand, ncand, lane);
+      // an opaque zero offset keeps the query landmark in LDS (read per candidate) instead of in
+      // 128 registers hoisted out of the loop
+      int zero = 0;
+      asm volatile("" : "+v"(zero));
+      score(area, j0, lq_s + zero);
     }
   }
 
