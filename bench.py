@@ -238,6 +238,39 @@ def window_timing(B=8, H=12, n_c=256, window=512, iters=10):
     return res
 
 
+# Cycles of the spin kernel that holds the GPU before a warm timed step (about 0.2 ms at the
+# shader clock): long enough for the host to submit every launch of the step behind it.
+QUEUE_AHEAD_CYCLES = 400_000
+
+
+def _latency(step, iters, before=None):
+    """Median, p10 and p90 (us) of `step` between two events on the current stream.  `before`
+    runs ahead of each repetition: the 1 GiB flush for cold runs, a short spin kernel for warm
+    runs (so the step is queued before the GPU reaches it and the span is GPU time), or nothing,
+    which times a step submitted to an idle GPU, host launch time included."""
+    import torch
+
+    times = []
+    for _ in range(iters):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    times.sort()
+    return {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
+            "p90_us": times[(9 * len(times)) // 10]}
+
+
+def _queue_ahead():
+    import torch
+
+    torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+
+
 def inference_latency(shape, iters=50):
     """Per-chunk retrieve + attend latency over a long history held in HBM (warm and cold)."""
     import torch
@@ -286,23 +319,11 @@ def inference_latency(shape, iters=50):
     with torch.cuda.graph(graph):
         one()
     torch.cuda.synchronize()
-    for mode in ("warm", "cold", "graph_warm", "graph_cold"):
-        times = []
-        for _ in range(iters):
-            if mode.endswith("cold"):
-                flush.max()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            if mode.startswith("graph"):
-                graph.replay()
-            else:
-                one()
-            b.record()
-            b.synchronize()
-            times.append(a.elapsed_time(b) * 1e3)
-        times.sort()
-        res[mode] = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
-                     "p90_us": times[(9 * len(times)) // 10]}
+    res["warm"] = _latency(one, iters, _queue_ahead)
+    res["cold"] = _latency(one, iters, lambda: flush.max())
+    res["warm_host_launch"] = _latency(one, iters)
+    res["graph_warm"] = _latency(graph.replay, iters, _queue_ahead)
+    res["graph_cold"] = _latency(graph.replay, iters, lambda: flush.max())
     lmk_bytes = shape.G * shape.B * shape.n_kv * 64 * 2
     gather = shape.G * shape.B * shape.topk * shape.H * 2 * 64 * 64 * 2
     res["hbm_bytes"] = lmk_bytes + gather
@@ -338,22 +359,13 @@ def token_decode_latency(shape, iters=100):
         gca.decode_tokens(cfg, q1, k, v, idx, sc, o=o1)
     torch.cuda.synchronize()
     res = {}
-    for mode in ("warm", "cold"):
-        times = []
-        for _ in range(iters):
-            if mode == "cold":
-                flush.max()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            gca.decode_tokens(cfg, q1, k, v, idx, sc, o=o1)
-            b.record()
-            b.synchronize()
-            times.append(a.elapsed_time(b) * 1e3)
-        times.sort()
-        res[mode] = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
-                     "p90_us": times[(9 * len(times)) // 10]}
-    # GPU time per call with the launches queued back to back (a single call on an idle GPU also
-    # waits for the host to submit it)
+    def tok():
+        gca.decode_tokens(cfg, q1, k, v, idx, sc, o=o1)
+
+    res["warm"] = _latency(tok, iters, _queue_ahead)
+    res["cold"] = _latency(tok, iters, lambda: flush.max())
+    res["warm_host_launch"] = _latency(tok, iters)
+    # GPU time per call with the launches queued back to back
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     flush.max()
     a.record()
@@ -436,20 +448,9 @@ def offload_latency(shape, iters=50):
     torch.cuda.synchronize()
     gca.profile_enable(False)
     res["kernels_us"] = {kk: vv[0] / vv[1] * 1e3 for kk, vv in gca.profile_collect().items()}
-    for mode in ("warm", "cold"):
-        times = []
-        for _ in range(iters):
-            if mode == "cold":
-                flush.max()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            one()
-            b.record()
-            b.synchronize()
-            times.append(a.elapsed_time(b) * 1e3)
-        times.sort()
-        res[mode] = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
-                     "p90_us": times[(9 * len(times)) // 10]}
+    res["warm"] = _latency(one, iters, _queue_ahead)
+    res["cold"] = _latency(one, iters, lambda: flush.max())
+    res["warm_host_launch"] = _latency(one, iters)
     # the host link's rate for a plain 1 GiB DMA copy out of the same pinned history
     dst = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -565,7 +566,8 @@ def main():
             log("inference latency", label)
             infer[label] = inference_latency(shp)
             log(f"  {label}: warm {infer[label]['warm']['median_us']:.1f} us, "
-                f"cold {infer[label]['cold']['median_us']:.1f} us; graph replay warm "
+                f"cold {infer[label]['cold']['median_us']:.1f} us (host launch included: "
+                f"{infer[label]['warm_host_launch']['median_us']:.1f} us); graph replay warm "
                 f"{infer[label]['graph_warm']['median_us']:.1f} us, cold {infer[label]['graph_cold']['median_us']:.1f} us")
         log("per-token decode over the 16M history (one token, retrieval reused for the chunk)")
         r = token_decode_latency(I.INFER_16M)
