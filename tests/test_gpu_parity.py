@@ -146,16 +146,18 @@ def test_ties_hub_and_passkey_retrieval():
     assert r_idx[1, 1, 40, 0] == 17
 
 
-def test_retrieval_gumbel_long_rows_two_stage():
-    """Rows with more candidates than one block (forces the split + merge kernels)."""
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_retrieval_gumbel_long_rows_two_stage(dtype):
+    """Rows with more candidates than one block (forces the split + merge kernels).  bf16 rows
+    stream through the scan's LDS ring, fp32 rows through registers."""
     n_kv = 5000
     shape = I.Shape(B=1, G=2, H=1, n_q=3, n_kv=n_kv, topk=8, q_chunk_base=n_kv - 1, shift=0)
-    host = I.make_inputs(shape, "bf16", seed=9, scale=0.125, names=("lq", "lk"))
+    host = I.make_inputs(shape, dtype, seed=9, scale=0.125, names=("lq", "lk"))
     # one workspace for every call (its contents need no setup)
-    ws = torch.empty(gca.workspace_size(gca.OP_RETRIEVE, config_for(shape, "bf16")), dtype=torch.uint8,
+    ws = torch.empty(gca.workspace_size(gca.OP_RETRIEVE, config_for(shape, dtype)), dtype=torch.uint8,
                      device="cuda")
     for gumbel in (False, True, False):
-        cfg = config_for(shape, "bf16", use_gumbel=gumbel, seed=77)
+        cfg = config_for(shape, dtype, use_gumbel=gumbel, seed=77)
         idx, sc = gca.retrieve(cfg, host["lq"].cuda(), host["lk"].cuda(), ws=ws)
         torch.cuda.synchronize()
         r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8, use_gumbel=gumbel,
@@ -169,7 +171,10 @@ def test_retrieval_several_candidates_per_lane():
     several candidates per lane (single stage); few rows with a very long history give several
     candidates per lane in each of many blocks (two stages)."""
     cases = [(I.Shape(B=2, G=2, H=1, n_q=600, n_kv=600, topk=8), True),   # 2400 rows, 4 per lane
-             (I.Shape(B=2, G=2, H=1, n_q=1, n_kv=300_000, topk=8, q_chunk_base=300_000, shift=0), False)]
+             (I.Shape(B=2, G=2, H=1, n_q=1, n_kv=300_000, topk=8, q_chunk_base=300_000, shift=0), False),
+             # one row of 598,716 candidates: blocks of 2,048 (8 per lane), the last holding 700, so
+             # its waves make 3, 3, 3 and 2 passes (an odd count leaves the ring's second stage idle)
+             (I.Shape(B=1, G=1, H=1, n_q=1, n_kv=598_716, topk=8, q_chunk_base=598_716, shift=0), True)]
     for shape, gumbel in cases:
         say("case", shape, "gumbel", gumbel)
         host = I.make_inputs(shape, "bf16", seed=4, scale=0.125, names=("lq", "lk"))
