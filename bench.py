@@ -238,6 +238,124 @@ def window_timing(B=8, H=12, n_c=256, window=512, iters=10):
     return res
 
 
+def _device_inputs(shape, seed, scale=0.125):
+    """Seeded N(0, scale^2) bf16 inputs drawn on the device (timing runs only: their values
+    change no launch shape, and host generation of several GiB would dominate the run)."""
+    import torch
+
+    from long_context_lm_amd import inputs as I
+
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    out = {}
+    for name in I.STREAMS:
+        x = torch.randn(shape.tensor_shape(name), generator=gen, device="cuda", dtype=torch.float32)
+        out[name] = x.mul_(scale).to(torch.bfloat16)
+        del x
+    return out
+
+
+def _timed(fn, iters, warmup=3):
+    """Average event time (ms) of fn over iters calls, and the per-kernel averages (us)."""
+    import torch
+
+    from long_context_lm_amd import gca
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    gca.profile_collect()
+    gca.profile_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    gca.profile_enable(False)
+    kern = {k: v[0] / v[1] * 1e3 for k, v in gca.profile_collect().items()}
+    return a.elapsed_time(b) / iters, kern
+
+
+def forward_timing(iters=20):
+    """The bf16 forward at the training shape with one retrieval group and no Gumbel noise
+    (B=8, L=16384, H=12, K=8, G=1, inputs N(0,1)/8): gca_retrieve + gca_forward without the
+    log-sum-exp output, as a forward-only layer call runs it."""
+    import numpy as np
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    shape = I.TRAIN_16K
+    cfg = gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                     dtype="bf16")
+    dev = _device_inputs(shape, seed=11)
+    G, B, H, nq, K = shape.G, shape.B, shape.H, shape.n_q, shape.topk
+    idx = torch.empty((G, B, nq, K), dtype=torch.int32, device="cuda")
+    score = torch.empty((G, B, nq, K), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(dev["q"])
+
+    def one():
+        gca.retrieve(cfg, dev["lq"], dev["lk"], idx, score)
+        gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, score, need_lse=False, o=o)
+
+    ms, kern = _timed(one, iters)
+    used = int((idx.cpu().numpy()[:, :, : nq - 1] >= 0).sum()) * H
+    tok = B * nq * 64
+    T = tok * H * 64 * 2
+    flops = 2 * UNIT_FLOPS * used + 2 * 64 * G * B * nq * (nq - 1) // 2
+    # Q, K, V read, O written; landmarks read; indices and scores written then read
+    nbytes = 4 * T + G * B * 2 * nq * 64 * 2 + 2 * G * B * nq * K * 8
+    floor = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+    res = {"workload": "GCA retrieve+fwd (no LSE), B=8 L=16384 H=12 d=64 K=8 G=1, no Gumbel, bf16, inputs N(0,1)/8",
+           "us_per_call": ms * 1e3, "tokens_per_s": tok / (ms * 1e-3), "kernels_us": kern,
+           "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "floor_us": floor * 1e6,
+           "frac": floor / (ms * 1e-3), "bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"}
+    del dev, idx, score, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def length_scaling(lengths=(4096, 16384, 65536), tokens=131072, iters=10):
+    """Tokens/s of the training step (retrieve + forward + backward, G=2, K=8, Gumbel, bf16) at
+    several context lengths with the tokens per batch fixed (B = tokens / L).  The attention work
+    per token is at most K chunks whatever L is; the landmark scores grow with the number of
+    earlier chunks.  [Notes, Loss / training strategy] states near-linear training cost in the
+    context length; this shows how far the step stays linear in L."""
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    out = {}
+    for L in lengths:
+        B, C = tokens // L, L // 64
+        shape = I.Shape(B=B, G=2, H=12, n_q=C, n_kv=C, topk=8)
+        cfg = gca.Config(B=B, G=2, H=12, n_q=C, n_kv=C, topk=8, dtype="bf16", use_gumbel=True, seed=1)
+        dev = _device_inputs(shape, seed=21)
+        G, H, K = 2, 12, 8
+        idx = torch.empty((G, B, C, K), dtype=torch.int32, device="cuda")
+        score = torch.empty((G, B, C, K), dtype=torch.float32, device="cuda")
+        o = torch.empty_like(dev["q"])
+        lse = torch.empty((G, B, H, C, K, 64), dtype=torch.float32, device="cuda")
+        grads = (torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"]),
+                 torch.empty((G, B, C, K), dtype=torch.float32, device="cuda"))
+        n_r = gca.workspace_size(gca.OP_RETRIEVE, cfg)
+        ws_r = torch.empty(n_r, dtype=torch.uint8, device="cuda") if n_r else None
+        ws_b = torch.empty(gca.workspace_size(gca.OP_BACKWARD, cfg), dtype=torch.uint8, device="cuda")
+
+        def step():
+            gca.retrieve(cfg, dev["lq"], dev["lk"], idx, score, ws=ws_r)
+            gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, score, o=o, lse=lse)
+            gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, score, lse, dev["dout"], ws=ws_b, out=grads)
+
+        ms, kern = _timed(step, iters)
+        out[str(L)] = {"B": B, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3), "kernels_us": kern}
+        del dev, idx, score, o, lse, grads, ws_r, ws_b
+        torch.cuda.empty_cache()
+    return out
+
+
 # Cycles of the spin kernel that holds the GPU before a warm timed step (about 0.2 ms at the
 # shader clock): long enough for the host to submit every launch of the step behind it.
 QUEUE_AHEAD_CYCLES = 400_000
@@ -478,6 +596,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-inference", action="store_true", help="skip the 1M/16M-history latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-scaling", action="store_true", help="skip the context-length scaling runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM traffic counters)")
     args = ap.parse_args()
@@ -560,6 +679,18 @@ def main():
         + ", ".join(f"{k} {v:.1f}" for k, v in sw["kernels_us"].items())
         + f"; fwd {sw.get('fwd_tflops', 0):.0f} TFLOP/s, bwd {sw.get('bwd_tflops', 0):.0f} TFLOP/s, "
         f"matrix-core fraction {sw['mfma_frac']:.3f}")
+    log("forward only at the training shape (G=1, no Gumbel, no LSE)")
+    fwd = forward_timing()
+    log(f"  {fwd['us_per_call']:.1f} us per call ({fwd['tokens_per_s'] / 1e6:.1f} M tokens/s), "
+        + ", ".join(f"{k} {v:.1f}" for k, v in fwd["kernels_us"].items())
+        + f"; floor {fwd['floor_us']:.1f} us ({fwd['bound']}), frac {fwd['frac']:.3f}")
+    scaling = None
+    if not args.no_scaling:
+        log("context-length scaling of the training step at 131,072 tokens per batch")
+        scaling = length_scaling()
+        for L, r in scaling.items():
+            log(f"  L={L:>6} B={r['B']:>2}: {r['ms_per_step']:.3f} ms, {r['tokens_per_s'] / 1e6:.2f} M tokens/s; "
+                + ", ".join(f"{k} {v:.0f}" for k, v in r["kernels_us"].items()))
     if not args.no_inference:
         infer = {}
         for label, shp in (("1M", I.INFER_1M), ("16M", I.INFER_16M)):
@@ -607,6 +738,8 @@ def main():
         "inference_latency": infer,
         "landmark_backward": lmk,
         "sliding_window": sw,
+        "forward_only": fwd,
+        "length_scaling": scaling,
     }
     print(json.dumps(out), flush=True)
 
