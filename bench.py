@@ -127,12 +127,13 @@ def roofline_for(name, fig, ms):
             "algorithmic_flops": fig["flops"], "algorithmic_bytes": fig["bytes"], "avg_launch_ms": ms}
 
 
-def cpu_baseline(shape, host):
-    """The oracle on a bounded sample: batch row 0 of the workload (both groups, all heads)."""
+def cpu_baseline(shape, host, rows=3):
+    """The oracle on a bounded sample: the first `rows` batch rows of the workload (both groups,
+    all heads), about 10-15 s of host work."""
     from long_context_lm_amd import inputs as I
     from oracle import gca_oracle as O
 
-    x = {k: I.as_f64(v[:, 0:1] if k in ("lq", "lk", "q", "dout") else v[0:1]) for k, v in host.items()}
+    x = {k: I.as_f64(v[:, 0:rows] if k in ("lq", "lk", "q", "dout") else v[0:rows]) for k, v in host.items()}
     threads = 1
     try:
         from threadpoolctl import threadpool_info
@@ -146,10 +147,19 @@ def cpu_baseline(shape, host):
     _o, _lse = O.forward(x["q"], x["k"], x["v"], idx, sc, shift=1)
     O.backward(x["q"], x["k"], x["v"], idx, sc, x["dout"], shift=1)
     dt = time.perf_counter() - t0
-    tokens = shape.n_q * 64
+    tokens = rows * shape.n_q * 64
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"batch row 0 of the workload ({tokens} tokens, G=2, H=12): retrieve+fwd+bwd, "
-                      f"{dt:.1f} s on {os.cpu_count()} host CPUs (BLAS threads {threads})"}
+            "sample": f"batch rows 0..{rows - 1} of the workload ({tokens} tokens, G=2, H=12): retrieve+fwd+bwd, "
+                      f"{dt:.1f} s on {os.cpu_count()} host CPUs (BLAS threads {threads})",
+            "host": {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity": affinity,
+                     "blas_threads": threads, "seconds": dt}}
 
 
 def landmark_timing(shape, cfg, dev, bufs, iters=50):
@@ -632,6 +642,20 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     tokens = shape.B * shape.n_q * 64
     log(f"step {ms:.3f} ms -> {tokens / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    # spread of single steps (after the timed region, one event pair per step)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in evs)
+    spread = None
+    if each:
+        spread = {"median_ms": statistics.median(each), "p10_ms": each[len(each) // 10],
+                  "p90_ms": each[(9 * len(each)) // 10], "steps": len(each)}
+        log(f"  single steps: median {spread['median_ms']:.3f} ms, p10 {spread['p10_ms']:.3f}, "
+            f"p90 {spread['p90_ms']:.3f}")
 
     figs = kernel_figures(shape, bufs["idx"].cpu().numpy())
     kernels = {}
@@ -724,6 +748,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_spread": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
