@@ -313,6 +313,44 @@ def test_full_16k_training_step_sampled():
         say(f"batch row {b} matches")
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("L,B,rows", [(4096, 32, (0, 31)), (65536, 2, (1,))], ids=["4K", "64K"])
+def test_training_step_other_lengths_sampled(L, B, rows):
+    """The training step at the other context lengths the benchmark runs with 131,072 tokens per
+    batch (G=2, K=8, Gumbel, bf16, N(0,1)/8): 64 chunks per sequence (most rows hold fewer than K
+    earlier chunks at the start) and 1,024 chunks (rows of up to 1,023 candidates, key chunks
+    named by many rows).  idx/score in full; o, dq and dscore for the sampled batch rows; dk, dv
+    for heads 0 and 11 of those rows."""
+    shape = I.Shape(B=B, G=2, H=12, n_q=L // 64, n_kv=L // 64, topk=8)
+    cfg = config_for(shape, "bf16", use_gumbel=True, seed=1)
+    say("case", shape)
+    host = I.make_inputs(shape, "bf16", seed=3, scale=0.125)
+    dev = upload(host)
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    dq, dk, dv, ds = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
+    torch.cuda.synchronize()
+    say("gpu step done")
+    r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8, use_gumbel=True, seed=1)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    say("retrieval bit-exact")
+    for b in rows:
+        qb, dob = I.as_f64(host["q"][:, b:b + 1]), I.as_f64(host["dout"][:, b:b + 1])
+        kb, vb = I.as_f64(host["k"][b:b + 1]), I.as_f64(host["v"][b:b + 1])
+        ib, sb = r_idx[:, b:b + 1], r_sc[:, b:b + 1]
+        r_o, r_lse = O.forward(qb, kb, vb, ib, sb, shift=1)
+        assert_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o, "bf16")
+        lse_compare(f"lse[b={b}]", lse[:, b:b + 1], r_lse, "bf16")
+        r_dq, r_dk, r_dv, r_ds = O.backward(qb, kb, vb, ib, sb, dob, shift=1)
+        assert_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq, "bf16")
+        for h in (0, 11):
+            assert_close(f"dk[b={b},h={h}]", I.as_f64(dk[b:b + 1, h]), r_dk[:, h], "bf16")
+            assert_close(f"dv[b={b},h={h}]", I.as_f64(dv[b:b + 1, h]), r_dv[:, h], "bf16")
+        assert_close(f"dscore[b={b}]", ds[:, b:b + 1].cpu().numpy(), r_ds, "bf16")
+        say(f"batch row {b} matches")
+
+
 # ------------------------------------------------------------------ long-history inference
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("shape", [I.INFER_1M, I.INFER_16M], ids=["1M", "16M"])
