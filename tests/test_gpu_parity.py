@@ -351,6 +351,38 @@ def test_training_step_other_lengths_sampled(L, B, rows):
         say(f"batch row {b} matches")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", ["small_f32", "small_bf16", "train16k_g1"])
+def test_forward_without_lse(case):
+    """A forward-only call (no log-sum-exp output) above the decode-size threshold: the output is
+    bit-identical to the training forward's and matches the oracle.  train16k_g1 is the bf16
+    forward workload at the training shape: B=8, L=16384, H=12, K=8, one group, no Gumbel,
+    inputs N(0,1)/8 (batch rows 0 and 7 against the oracle)."""
+    if case == "train16k_g1":
+        shape, dtype, scale, rows = I.TRAIN_16K, "bf16", 0.125, (0, 7)
+    else:
+        shape = I.Shape(B=2, G=1, H=4, n_q=40, n_kv=40, topk=8)  # 320 query tiles
+        dtype, scale, rows = ("f32" if case == "small_f32" else "bf16"), 1.0, (0, 1)
+    cfg = config_for(shape, dtype)
+    say("case", case, shape)
+    host = I.make_inputs(shape, dtype, seed=5, scale=scale, names=("lq", "lk", "q", "k", "v"))
+    dev = upload(host)
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o_inf, none = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, need_lse=False)
+    o_tr, _ = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o_inf, o_tr), "forward without LSE differs from the training forward"
+    r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    for b in rows:
+        r_o, _ = O.forward(I.as_f64(host["q"][:, b:b + 1]), I.as_f64(host["k"][b:b + 1]),
+                           I.as_f64(host["v"][b:b + 1]), r_idx[:, b:b + 1], r_sc[:, b:b + 1], shift=1)
+        assert_close(f"o[b={b}]", I.as_f64(o_inf[:, b:b + 1]), r_o, dtype)
+    say("  matches")
+
+
 # ------------------------------------------------------------------ long-history inference
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("shape", [I.INFER_1M, I.INFER_16M], ids=["1M", "16M"])
