@@ -352,7 +352,7 @@ def test_training_step_other_lengths_sampled(L, B, rows):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("case", ["small_f32", "small_bf16", "train16k_g1"])
+@pytest.mark.parametrize("case", ["small_f32", "small_bf16", "ragged_bf16", "train16k_g1"])
 def test_forward_without_lse(case):
     """A forward-only call (no log-sum-exp output) above the decode-size threshold: the output is
     bit-identical to the training forward's and matches the oracle.  train16k_g1 is the bf16
@@ -360,6 +360,8 @@ def test_forward_without_lse(case):
     inputs N(0,1)/8 (batch rows 0 and 7 against the oracle)."""
     if case == "train16k_g1":
         shape, dtype, scale, rows = I.TRAIN_16K, "bf16", 0.125, (0, 7)
+    elif case == "ragged_bf16":  # 261 query tiles: the last workgroup of eight tiles holds five
+        shape, dtype, scale, rows = I.Shape(B=1, G=1, H=3, n_q=87, n_kv=87, topk=8), "bf16", 1.0, (0,)
     else:
         shape = I.Shape(B=2, G=1, H=4, n_q=40, n_kv=40, topk=8)  # 320 query tiles
         dtype, scale, rows = ("f32" if case == "small_f32" else "bf16"), 1.0, (0, 1)
