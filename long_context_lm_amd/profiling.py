@@ -191,6 +191,82 @@ def traffic(dir_fetch: str, dir_write: str, out_json: str, commands) -> None:
         json.dump(out, fh, indent=1)
 
 
+def counters(directory: str, out_md: str, command: str, warmup: int = 1, steps: int = 2, n_xcc: int = 8,
+             n_simd: int = 1024) -> None:
+    """Issue counters of the training step's attention kernels (one rocprofv3 --pmc pass): how busy
+    the matrix cores were, how often a VALU instruction issued while they were busy, and the VALU
+    and LDS activity, per dispatch of the timed steps (dispatches [warmup, warmup + steps))."""
+    dur = {}  # dispatch id -> duration (us), from the kernel trace of the same run
+    try:
+        for r in _rows(directory, "kernel_trace.csv"):
+            dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    except FileNotFoundError:
+        pass
+    per = {}
+    for r in _rows(directory, "counter_collection.csv"):
+        k = short_name(r["Kernel_Name"])
+        if k not in ("attend_fwd", "bwd_query", "bwd_key"):
+            continue
+        did = int(r["Dispatch_Id"])
+        us = dur.get(did, 0.0)
+        if not us and "End_Timestamp" in r:
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        e = per.setdefault(k, {}).setdefault(did, {"us": us, "grid": int(r["Grid_Size"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [
+        "# Issue counters: attention kernels of the GCA training step (16K workload)",
+        "",
+        "Workload: B=8, L=16384 (256 chunks of 64), H=12, d=64, K=8, G=2, Gumbel top-k, bf16.",
+        "",
+        f"Command (repository root, on an MI355X): `{command}`",
+        "",
+        f"Kernel sources hash: `{source_hash()}`.  Dispatches {warmup}..{warmup + steps - 1} of each kernel "
+        "(the timed steps).  Cycles = GRBM_GUI_ACTIVE / 8 XCDs.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+        "(cycles x 1024 SIMDs).  Co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (share of "
+        "matrix-busy cycles in which a VALU instruction also issued).  VALU and MFMA instructions are per "
+        "SIMD per 1,000 cycles.  LDS active = SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs).",
+        "",
+        "| kernel | duration (us) | cycles | clock (GHz) | MFMA busy | co-issue | VALU instr. / kcycle / SIMD | "
+        "MFMA instr. / kcycle / SIMD | LDS active |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k in ("attend_fwd", "bwd_query", "bwd_key"):
+        if k not in per:
+            continue
+        disp = [per[k][key] for key in sorted(per[k])][warmup:warmup + steps]
+        if not disp:
+            continue
+        avg = {c: sum(x.get(c, 0.0) for x in disp) / len(disp) for c in disp[0] if c != "grid"}
+        cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / n_xcc
+        if cyc <= 0:
+            continue
+        busy = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        co = avg.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0)
+        lines.append(
+            f"| {k} | {avg['us']:.1f} | {cyc:.0f} | {cyc / (avg['us'] * 1e3):.2f} | {busy / (cyc * n_simd):.1%} | "
+            f"{(co / busy if busy else 0):.1%} | {1e3 * avg.get('SQ_INSTS_VALU', 0) / (cyc * n_simd):.0f} | "
+            f"{1e3 * avg.get('SQ_INSTS_MFMA', 0) / (cyc * n_simd):.1f} | "
+            f"{avg.get('SQ_LDS_IDX_ACTIVE', 0) / (cyc * (n_simd // 4)):.1%} |")
+    lines += ["", "Every dispatch of these kernels at the training shape in the run (warm-up, timed and "
+              "single-step runs): the cycle count stays nearly fixed while the duration follows the shader "
+              "clock.", "",
+              "| kernel | dispatch | duration (us) | cycles | clock (GHz) |", "|---|---|---|---|---|"]
+    for k in ("attend_fwd", "bwd_query", "bwd_key"):
+        ids = sorted(per.get(k, {}))
+        if not ids:
+            continue
+        grid = per[k][ids[0]]["grid"]
+        for did in ids:
+            e = per[k][did]
+            if e["grid"] != grid:
+                continue
+            cyc = e.get("GRBM_GUI_ACTIVE", 0.0) / n_xcc
+            if e["us"] > 0 and cyc > 0:
+                lines.append(f"| {k} | {did} | {e['us']:.1f} | {cyc:.0f} | {cyc / (e['us'] * 1e3):.2f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     what = sys.argv[1]
     if what == "stats":  # stats DIR OUT.md BENCH_LOG COMMAND...
@@ -198,6 +274,8 @@ if __name__ == "__main__":
               bench_log=sys.argv[4])
     elif what == "infer":  # infer DIR OUT.md BENCH_LOG COMMAND...
         infer_stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), sys.argv[4])
+    elif what == "counters":  # counters DIR OUT.md COMMAND...
+        counters(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif what == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     else:
