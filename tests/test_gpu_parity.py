@@ -82,6 +82,39 @@ def test_small_topk_variants_bf16(topk):
     _run_case(shape, "bf16", scale=0.125, seed=topk)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_logits(dtype):
+    """Every input x4 (attention logits with a standard deviation of 16, retrieval scores up to
+    about 45): nearly one-hot per-chunk softmaxes and fusion weights, the exponent range the
+    per-chunk maximum has to keep finite.  The outputs grow with the inputs (|dq| and |dscore|
+    reach a few hundred), so the float32 bar is the 1e-4 of unit-scale data taken relative to each
+    tensor's largest reference magnitude, tightened to 2e-5 (float32 sums of 512 products carry
+    about 1e-5 of relative rounding); bf16 keeps relative L2 1e-2.  idx and score stay bit-exact."""
+    shape = I.Shape(B=1, G=2, H=2, n_q=20, n_kv=20, topk=8)
+    cfg = config_for(shape, dtype, use_gumbel=True)
+    host = I.make_inputs(shape, dtype, seed=8, scale=4.0)
+    x = {k: I.as_f64(v) for k, v in host.items()}
+    dev = upload(host)
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    grads = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
+    torch.cuda.synchronize()
+    r_idx, r_sc, r_o, r_lse, r_grads = _oracle_all(shape, x, cfg, True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+    for name, got, ref in zip(("o", "dq", "dk", "dv", "dscore"), (o, *grads), (r_o, *r_grads)):
+        got = I.as_f64(got)
+        assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+        if dtype == "f32":
+            mag = max(1.0, float(np.max(np.abs(ref))))
+            err = float(np.max(np.abs(got - ref)))
+            say(f"  {name}: max-abs {err:.2e} at magnitude {mag:.1f}")
+            assert err <= 2e-5 * mag, f"{name}: max-abs {err:.3e} > 2e-5 x {mag:.1f}"
+        else:
+            assert_close(name, got, ref, dtype)
+    lse_compare("lse", lse, r_lse, dtype)
+
+
 def test_history_shorter_than_queries_and_offset_rows():
     # rows are global chunks 5..16; only 9 history chunks exist
     shape = I.Shape(B=2, G=1, H=2, n_q=12, n_kv=9, topk=4, q_chunk_base=5, shift=0)
