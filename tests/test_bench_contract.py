@@ -1,0 +1,42 @@
+"""The benchmark's command-line contract, checked on the CPU (no GPU needed).
+
+bench.py measures one GPU: asked for more it must exit with an explanation before touching a
+device, and its helpers that compute the reported algorithmic figures must count what the
+method does (valid slots of the causal retrieval, the 64x64x64 products per slot).
+"""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""  # no JSON line
+
+
+def test_kernel_figures_count_valid_slots():
+    sys.path.insert(0, ROOT)
+    import bench
+    from long_context_lm_amd import inputs as I
+
+    shape = I.Shape(B=2, G=2, H=3, n_q=16, n_kv=16, topk=4)
+    # row r has min(r, K) valid slots (strictly earlier chunks); rows feed query chunk r + 1
+    idx = np.full((2, 2, 16, 4), -1, dtype=np.int32)
+    for r in range(16):
+        idx[:, :, r, : min(r, 4)] = 0
+    figs = bench.kernel_figures(shape, idx)
+    per_row = sum(min(r, 4) for r in range(15))  # the last row feeds no query chunk
+    tiles = 2 * 2 * per_row * 3
+    assert figs["attend_fwd"]["tiles"] == tiles
+    assert figs["attend_fwd"]["flops"] == 2 * 2 * 64 ** 3 * tiles
+    assert figs["bwd_key"]["flops"] == figs["bwd_query"]["flops"] == figs["attend_fwd"]["flops"]
+    # causal landmark pairs: G * B * sum_i i
+    assert figs["score_topk"]["flops"] == 2 * 64 * 2 * 2 * (16 * 15 // 2)
