@@ -16,8 +16,9 @@
 // each retrieving chunk) are copied global -> LDS with direct 16-byte-per-lane copies into a
 // row-major, XOR-swizzled layout.  The backward passes double-buffer them (the copy of item n+1
 // is in flight while item n is computed; one barrier per item publishes the new buffer and
-// retires the old); the forward, whose registers allow four resident waves per SIMD, uses one
-// buffer and relies on the other resident workgroups to cover the copy latency.
+// retires the old); the forward keeps one K and one V buffer, refills each as soon as its
+// fragments are in registers, and relies on the other resident workgroups (two waves per SIMD)
+// to cover the rest of the copy latency.
 // Operands read along a tile row come from ds_read_b128; operands read down a tile column (V in
 // the forward, K in dQ, Q and dO in dK/dV) come from transposing LDS reads, so no tile is ever
 // stored transposed.
@@ -235,8 +236,9 @@ __device__ __forceinline__ float tile_softmax(f32x16_t (&sacc)[2], float c2, flo
   return mx;
 }
 
-// Slot loop, software-pipelined over one K and one V buffer (16 KiB of LDS for bf16, so four
-// waves per SIMD stay resident): once every wave has read K(n) for the scores, K(n+1) is copied
+// Two waves of 32 queries per query tile (the fp32 forward; bf16 uses the one-wave kernel below).
+// Slot loop, software-pipelined over one K and one V buffer (32 KiB of LDS for fp32 tiles; the
+// registers allow two waves per SIMD): once every wave has read K(n) for the scores, K(n+1) is copied
 // in behind the softmax and P V of slot n; once every wave has read V(n), V(n+1) is copied in
 // behind the scores and softmax of slot n+1.  Each wave waits only for its own copies (counted
 // with vmcnt, in issue order) and a barrier then publishes them to the other wave.  kLse: the

@@ -161,14 +161,22 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
 
 
 def _per_kernel(directory: str, counter: str):
-    per = {}
+    """Counter values per kernel, in dispatch order.  A kernel that also runs at other launch shapes
+    later in the run (the forward-only workload, the context-length sweep) keeps only the dispatches
+    with the grid of its first one: the training step, which bench.py runs first."""
+    rows = []
     for r in _rows(directory, "counter_collection.csv"):
         if r["Counter_Name"] != counter:
             continue
         s = short_name(r["Kernel_Name"])
         if s is None:
             continue
-        per.setdefault(s, []).append(float(r["Counter_Value"]))
+        rows.append((int(r["Dispatch_Id"]), s, int(r["Grid_Size"]), float(r["Counter_Value"])))
+    per, grid = {}, {}
+    for _did, s, g, v in sorted(rows):
+        grid.setdefault(s, g)
+        if s == "copy" or g == grid[s]:
+            per.setdefault(s, []).append(v)
     return per
 
 
