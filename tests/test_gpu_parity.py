@@ -156,6 +156,29 @@ def test_no_history():
 
 
 # ------------------------------------------------------------------ retrieval stress
+@pytest.mark.parametrize("tau,seed", [(0.0, 7), (0.5, 2**63 + 5), (3.0, 2**64 - 1)])
+def test_gumbel_temperatures_and_seeds(tau, seed):
+    """Gumbel top-k at other noise scales (tau = 0 leaves the clean order) and 64-bit seeds with
+    the top bit set: indices and clean scores bit-exact, on many rows (up to 299 candidates) and
+    on one 50,000-candidate decode row."""
+    cases = [I.Shape(B=2, G=2, H=1, n_q=300, n_kv=300, topk=8),
+             I.Shape(B=1, G=2, H=1, n_q=1, n_kv=50_000, topk=8, q_chunk_base=50_000, shift=0)]
+    for shape in cases:
+        say("case", shape, "tau", tau, "seed", seed)
+        host = I.make_inputs(shape, "bf16", seed=6, scale=0.125, names=("lq", "lk"))
+        cfg = config_for(shape, "bf16", use_gumbel=True, seed=seed, tau=tau)
+        idx, sc = gca.retrieve(cfg, host["lq"].cuda(), host["lk"].cuda())
+        torch.cuda.synchronize()
+        r_idx, r_sc = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8, use_gumbel=True, seed=seed,
+                                 tau=tau, q_chunk_base=shape.q_chunk_base, n_kv=shape.n_kv)
+        np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+        np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
+        if tau == 0.0:  # no noise: the same selection as plain top-k
+            p_idx, _ = O.retrieve(I.as_f64(host["lq"]), I.as_f64(host["lk"]), 8,
+                                  q_chunk_base=shape.q_chunk_base, n_kv=shape.n_kv)
+            np.testing.assert_array_equal(r_idx, p_idx)
+
+
 def test_ties_hub_and_passkey_retrieval():
     """Duplicate landmarks (ties toward lower j), a hub chunk every row prefers, a planted key."""
     n = 48
