@@ -71,6 +71,13 @@ def test_landmark_gradients_16k_training_shape():
     _run(I.Shape(B=8, G=2, H=12, n_q=256, n_kv=256, topk=8), "bf16", seed=3)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_landmark_gradients_64k_context(dtype):
+    """1,024 chunks per sequence (the 64K step of the context-length sweep, B=2, G=2): rows of up
+    to 1,023 candidates and early key chunks named by many rows (long inverse-index walks)."""
+    _run(I.Shape(B=2, G=2, H=12, n_q=1024, n_kv=1024, topk=8), dtype, seed=6)
+
+
 def test_landmark_gradients_decode_long_history():
     """One retrieval row over a 5,000-chunk history: nearly every key chunk gets zero."""
     _run(I.Shape(B=1, G=2, H=12, n_q=1, n_kv=5000, topk=8, q_chunk_base=5000, shift=0), "bf16", seed=4)
