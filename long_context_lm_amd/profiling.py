@@ -160,6 +160,85 @@ def infer_stats(directory: str, out_md: str, command: str, bench_log: str) -> No
         fh.write("\n".join(lines) + "\n")
 
 
+def _copy_calibration(directory: str, counter: str):
+    """Bytes per counter unit of the plain 1 GiB device copy bench.py --copy-calibration runs (the
+    runtime's copyBuffer blit kernel; other copy-like kernels of the run, such as random-number
+    fills of a long history, may move more data and must not be taken for it)."""
+    blit, other = [], []
+    for r in _rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        if "copyBuffer" in r["Kernel_Name"]:
+            blit.append(float(r["Counter_Value"]))
+        elif short_name(r["Kernel_Name"]) == "copy":
+            other.append(float(r["Counter_Value"]))
+    vals = blit or other
+    if not vals:
+        raise RuntimeError("the copy calibration kernel is missing from the counter runs")
+    return COPY_BYTES / max(vals)
+
+
+# Launch shapes of the decode-step kernels (G = 2 rows of one batch row, H = 12, K = 8).
+DECODE_SHAPES = {("score_topk", 128, 256): "1M scan (2 rows x 64 blocks)",
+                 ("score_topk", 512, 256): "16M scan (2 rows x 256 blocks)",
+                 ("topk_merge", 2, 1024): "1M / 16M merge",
+                 ("attend_fwd", 48, 512): "1M / 16M attend (24 tiles x 2 halves)",
+                 ("fetch_chunks", 192, 256): "host-memory K/V fetch (2 groups x 8 slots x 12 heads)",
+                 ("decode_tokens", 24, 512): "one-token decode, 16M history (2 groups x 12 heads)"}
+# Algorithmic bytes per dispatch: landmarks scanned (G rows x history x 64 x 2 B) plus the query
+# landmarks; the attend and fetch kernels read the retrieved K/V tiles (G x K x H x 2 x 8 KiB).
+DECODE_BYTES = {"1M scan (2 rows x 64 blocks)": 2 * 16384 * 128 + 2 * 128,
+                "16M scan (2 rows x 256 blocks)": 2 * 262144 * 128 + 2 * 128,
+                "1M / 16M attend (24 tiles x 2 halves)": 2 * 8 * 12 * 2 * 8192 + 2 * 2 * 12 * 64 * 128,
+                "host-memory K/V fetch (2 groups x 8 slots x 12 heads)": 2 * 8 * 12 * 2 * 8192,
+                "one-token decode, 16M history (2 groups x 12 heads)": 2 * 8 * 12 * 2 * 8192}
+
+
+def infer_traffic(dir_fetch: str, dir_write: str, out_md: str, commands) -> None:
+    """FETCH_SIZE / WRITE_SIZE of the decode-step kernels per launch shape, scaled by the plain
+    copy's readings, next to the algorithmic bytes of each launch."""
+    def shape_values(directory, counter):
+        per = {}
+        for r in _rows(directory, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_name(r["Kernel_Name"])
+            wg = int(r["Workgroup_Size"])
+            key = (k, int(r["Grid_Size"]) // wg, wg)
+            if key in DECODE_SHAPES:
+                per.setdefault(DECODE_SHAPES[key], []).append(float(r["Counter_Value"]))
+        return per, _copy_calibration(directory, counter)
+
+    fetch, f_scale = shape_values(dir_fetch, "FETCH_SIZE")
+    write, w_scale = shape_values(dir_write, "WRITE_SIZE")
+    lines = [
+        "# HBM traffic: decode-step kernels over 1M- and 16M-token histories",
+        "",
+        "Workload: B=1, G=2, H=12, d=64, K=8, one new 64-token chunk; bf16 K, V and landmarks in HBM "
+        "(the fetch reads pinned host memory).",
+        "",
+        "Commands (repository root, on an MI355X): " + "; ".join(f"`{c}`" for c in commands),
+        "",
+        f"Kernel sources hash: `{source_hash()}`.  Per launch shape, the average over its dispatches of "
+        f"FETCH_SIZE and WRITE_SIZE (KiB), scaled by what the counters read for a 1 GiB device copy "
+        f"({f_scale:.0f} and {w_scale:.0f} bytes per KiB).  Repeated dispatches find their data in "
+        "the caches, so the scans of a history that fits the MALL (1M) read less than once.",
+        "",
+        "| kernel launch | dispatches | fetched (MB) | written (MB) | algorithmic bytes read (MB) |",
+        "|---|---|---|---|---|",
+    ]
+    for name in DECODE_SHAPES.values():
+        if name not in fetch:
+            continue
+        f = sum(fetch[name]) / len(fetch[name]) * f_scale
+        w = sum(write.get(name, [0.0])) / max(len(write.get(name, [])), 1) * w_scale
+        alg = DECODE_BYTES.get(name)
+        lines.append(f"| {name} | {len(fetch[name])} | {f / 1e6:.2f} | {w / 1e6:.3f} | "
+                     + (f"{alg / 1e6:.2f}" if alg else "-") + " |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def _per_kernel(directory: str, counter: str):
     """Counter values per kernel, in dispatch order.  A kernel that also runs at other launch shapes
     later in the run (the forward-only workload, the context-length sweep) keeps only the dispatches
@@ -183,11 +262,9 @@ def _per_kernel(directory: str, counter: str):
 def traffic(dir_fetch: str, dir_write: str, out_json: str, commands) -> None:
     fetch = _per_kernel(dir_fetch, "FETCH_SIZE")
     write = _per_kernel(dir_write, "WRITE_SIZE")
-    if "copy" not in fetch or "copy" not in write:
-        raise RuntimeError("the copy calibration kernel is missing from the counter runs")
-    # the calibration copy reads and writes COPY_BYTES; use its largest dispatch
-    f_scale = COPY_BYTES / max(fetch["copy"])
-    w_scale = COPY_BYTES / max(write["copy"])
+    # the calibration copy reads and writes COPY_BYTES
+    f_scale = _copy_calibration(dir_fetch, "FETCH_SIZE")
+    w_scale = _copy_calibration(dir_write, "WRITE_SIZE")
     out = {"source_hash": source_hash(), "fetch_bytes_per_kib": f_scale, "write_bytes_per_kib": w_scale,
            "copy_bytes": COPY_BYTES, "commands": commands, "kernels": {}}
     for k in SHORT:
@@ -282,6 +359,8 @@ if __name__ == "__main__":
               bench_log=sys.argv[4])
     elif what == "infer":  # infer DIR OUT.md BENCH_LOG COMMAND...
         infer_stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), sys.argv[4])
+    elif what == "infer-traffic":  # infer-traffic DIR_F DIR_W OUT.md COMMAND_F COMMAND_W
+        infer_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     elif what == "counters":  # counters DIR OUT.md COMMAND...
         counters(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif what == "traffic":
