@@ -5,10 +5,13 @@ One step = causal retrieval (Gumbel top-k) + grouped cross-attention forward + b
 batch of the 16K-token training workload (B=8, L=16384 = 256 chunks of 64, H=12, d=64, K=8, G=2,
 bf16, synthetic N(0,1)/8 inputs).  Prints one JSON line: tokens/s with inputs resident in HBM,
 the roofline position of the dominant kernel (HIP events around each kernel launch inside the
-timed region), the CPU oracle timed on a bounded sample of the same workload, and the per-chunk
-retrieve+attend latency over 1M- and 16M-token histories held in HBM.
+timed region), the CPU oracle timed on a bounded sample of the same workload, the per-chunk
+retrieve+attend latency over 1M- and 16M-token histories held in HBM, and the rows beside the
+step: landmark gradients, sliding-window attention, the forward-only workload (one group, no
+Gumbel noise, no LSE) and the step at 4K/16K/64K contexts with the same tokens per batch.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-inference] [--no-cpu-baseline]
+                    [--no-scaling] [--copy-calibration]
 """
 
 from __future__ import annotations
