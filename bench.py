@@ -114,6 +114,81 @@ def measured_traffic(kernel):
     return t["kernels"][kernel]["hbm_bytes"]
 
 
+def step_roofline(shape, idx_cpu):
+    """The step's algorithmic floor: forward and backward each at the larger of their matrix-core
+    and HBM times.  Forward: two 64x64x64 products per (valid slot, head) tile; Q, K, V read, O
+    and the LSE written.  Backward: four products per tile (dP', dV, dQ, dK, no recompute); Q,
+    dO, K, V read, dQ, dK, dV written, LSE read.  At the 16K, G=2 shape (384,768 tiles) this is
+    163.7 us (forward, HBM) + 322.8 us (backward, matrix cores) = 486.5 us."""
+    import numpy as np
+
+    G, B, H, nq, K = shape.G, shape.B, shape.H, shape.n_q, shape.topk
+    tiles = int((np.asarray(idx_cpu)[:, :, : nq - 1] >= 0).sum()) * H
+    T = B * nq * 64 * H * 64 * 2
+    lse = G * B * nq * 64 * H * K * 4
+    sel = G * B * nq * K * 8
+    fwd = {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (2 * G + 2) * T + lse + sel}
+    bwd = {"flops": 4 * UNIT_FLOPS * tiles, "bytes": (3 * G + 4) * T + lse + sel}
+
+    def t(f, pf, pb):
+        return max(f["flops"] / pf, f["bytes"] / pb)
+
+    return {"tiles": tiles, "forward": fwd, "backward": bwd,
+            "floor_us": (t(fwd, PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9)
+                         + t(bwd, PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9)) * 1e6,
+            "t": t}
+
+
+def measured_peaks():
+    """Rates measured on this GPU in this run, beside the vendor peaks: a plain 1 GiB device copy
+    (bytes read + written per second) and a bf16 8192^3 matrix product through torch (hipBLASLt),
+    the rate a dense bf16 contraction reaches here."""
+    import torch
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    a.record()
+    for _ in range(n):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    copy_gbs = 2 * src.numel() * n / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    x = torch.randn((m, m), device="cuda", dtype=torch.bfloat16)
+    y = torch.randn((m, m), device="cuda", dtype=torch.bfloat16)
+    z = torch.empty((m, m), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(x, y, out=z)
+    a.record()
+    for _ in range(n):
+        torch.mm(x, y, out=z)
+    b.record()
+    b.synchronize()
+    gemm_tflops = 2 * m ** 3 * n / (a.elapsed_time(b) * 1e-3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+            "how": "1 GiB device copy (read + write bytes / time); torch.mm bf16 8192x8192x8192"}
+
+
+def both_ceilings(fig, ms, peaks):
+    """A kernel's position against both ceilings, vendor and measured."""
+    t = ms * 1e-3
+    tb = fig["bytes"] / t / 1e9
+    tf = fig["flops"] / t / 1e12
+    out = {"avg_ms": ms, "hbm_gbs": tb, "hbm_frac": tb / PEAK_HBM_GBS, "mfma_tflops": tf,
+           "mfma_frac": tf / PEAK_BF16_TFLOPS}
+    if peaks:
+        out["hbm_frac_measured_peak"] = tb / peaks["hbm_copy_gbs"]
+        out["mfma_frac_measured_peak"] = tf / peaks["bf16_gemm_tflops"]
+    return out
+
+
 def roofline_for(name, fig, ms):
     t = ms * 1e-3
     t_mfma = fig["flops"] / (PEAK_BF16_TFLOPS * 1e12)
@@ -459,6 +534,12 @@ def inference_latency(shape, iters=50):
     res["warm_host_launch"] = _latency(one, iters)
     res["graph_warm"] = _latency(graph.replay, iters, _queue_ahead)
     res["graph_cold"] = _latency(graph.replay, iters, lambda: flush.max())
+    # a plain streaming read of the same landmark bytes (torch's max over them as int32 words),
+    # warm and cold: what a one-pass read of this size takes on this GPU, launch and drain included
+    lk32 = lk.view(torch.int32)
+    res["plain_landmark_read"] = {"bytes": lk32.numel() * 4,
+                                  "warm": _latency(lambda: lk32.max(), iters, _queue_ahead),
+                                  "cold": _latency(lambda: lk32.max(), iters, lambda: flush.max())}
     lmk_bytes = shape.G * shape.B * shape.n_kv * 64 * 2
     gather = shape.G * shape.B * shape.topk * shape.H * 2 * 64 * 64 * 2
     res["hbm_bytes"] = lmk_bytes + gather
@@ -635,10 +716,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the headline: K steps between two events, no per-launch events inside
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tokens = shape.B * shape.n_q * 64
+    log(f"step {ms:.3f} ms -> {tokens / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    # per-kernel durations: the same K steps again, each launch between events on its stream
     gca.profile_collect()
     gca.profile_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
         step()
@@ -646,9 +736,8 @@ def main():
     torch.cuda.synchronize()
     gca.profile_enable(False)
     kern = gca.profile_collect()
-    ms = start.elapsed_time(end) / args.steps
-    tokens = shape.B * shape.n_q * 64
-    log(f"step {ms:.3f} ms -> {tokens / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    ms_bracketed = start.elapsed_time(end) / args.steps
+    log(f"  with per-launch events: {ms_bracketed:.3f} ms per step")
     # spread of single steps (after the timed region, one event pair per step)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in evs:
@@ -674,11 +763,6 @@ def main():
             kernels[name].update({"bound": r["bound"], "frac": r["frac"], "achieved": r["achieved"], "unit": r["unit"]})
     dominant = max(kern.items(), key=lambda kv: kv[1][0])[0]
     roof = roofline_for(dominant, figs[dominant], kern[dominant][0] / kern[dominant][1])
-    # whole-step position against the algorithmic roofline (max of the two ceilings per kernel)
-    step_floor_ms = sum(max(f["flops"] / (PEAK_BF16_TFLOPS * 1e12), f["bytes"] / (PEAK_HBM_GBS * 1e9))
-                        for f in figs.values()) * 1e3
-    roof["step_floor_ms"] = step_floor_ms
-    roof["step_frac"] = step_floor_ms / ms
     for k, v in kernels.items():
         log(f"  {k:12s} {v['avg_ms'] * 1e3:9.1f} us  x{v['launches']}"
             + (f"  {v['bound']} {v['frac'] * 100:5.1f}%" if "frac" in v else ""))
@@ -690,6 +774,34 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    log("measured peaks: plain device copy, bf16 matrix product")
+    peaks = measured_peaks()
+    log(f"  copy {peaks['hbm_copy_gbs']:.0f} GB/s, bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
+    # whole-step position: the forward's and the backward's algorithmic floors against the step
+    sr = step_roofline(shape, bufs["idx"].cpu().numpy())
+    fl = sr["t"]
+    step_floor_us = sr["floor_us"]
+    step_floor_measured_us = (fl(sr["forward"], peaks["bf16_gemm_tflops"] * 1e12, peaks["hbm_copy_gbs"] * 1e9)
+                              + fl(sr["backward"], peaks["bf16_gemm_tflops"] * 1e12, peaks["hbm_copy_gbs"] * 1e9)) * 1e6
+    roof["step_floor_us"] = step_floor_us
+    roof["step_frac"] = step_floor_us / (ms * 1e3)
+    roof["step_floor_measured_peaks_us"] = step_floor_measured_us
+    roof["step_frac_measured_peaks"] = step_floor_measured_us / (ms * 1e3)
+    roof["measured_peaks"] = peaks
+    if roof["unit"] == "GB/s":
+        roof["frac_measured_peak"] = roof["achieved"] / peaks["hbm_copy_gbs"]
+    else:
+        roof["frac_measured_peak"] = roof["achieved"] / peaks["bf16_gemm_tflops"]
+    log(f"  step floor {step_floor_us:.1f} us (vendor peaks) -> step_frac {roof['step_frac']:.3f}; "
+        f"{step_floor_measured_us:.1f} us (measured peaks) -> {roof['step_frac_measured_peaks']:.3f}")
+    backward_kernels = {}
+    for name in ("attend_fwd", "bwd_query", "bwd_key"):
+        if name in kern and name in figs:
+            backward_kernels[name] = both_ceilings(figs[name], kern[name][0] / kern[name][1], peaks)
+            c = backward_kernels[name]
+            log(f"  {name:12s} HBM {c['hbm_gbs']:.0f} GB/s ({c['hbm_frac']:.3f}), matrix cores "
+                f"{c['mfma_tflops']:.0f} TFLOP/s ({c['mfma_frac']:.3f})")
 
     log("landmark gradients (gca_landmark_backward) on the step's indices and d(score)")
     lmk = landmark_timing(shape, cfg, dev, bufs)
@@ -727,10 +839,15 @@ def main():
         for label, shp in (("1M", I.INFER_1M), ("16M", I.INFER_16M)):
             log("inference latency", label)
             infer[label] = inference_latency(shp)
-            log(f"  {label}: warm {infer[label]['warm']['median_us']:.1f} us, "
-                f"cold {infer[label]['cold']['median_us']:.1f} us (host launch included: "
-                f"{infer[label]['warm_host_launch']['median_us']:.1f} us); graph replay warm "
-                f"{infer[label]['graph_warm']['median_us']:.1f} us, cold {infer[label]['graph_cold']['median_us']:.1f} us")
+            r = infer[label]
+            log(f"  {label}: warm {r['warm']['median_us']:.1f} us, "
+                f"cold {r['cold']['median_us']:.1f} us (host launch included: "
+                f"{r['warm_host_launch']['median_us']:.1f} us); graph replay warm "
+                f"{r['graph_warm']['median_us']:.1f} us, cold {r['graph_cold']['median_us']:.1f} us; "
+                + ", ".join(f"{k} {v:.1f}" for k, v in r["kernels_us"].items())
+                + f"; plain read of the {r['plain_landmark_read']['bytes'] / 2**20:.0f} MiB of landmarks: warm "
+                f"{r['plain_landmark_read']['warm']['median_us']:.1f} us, cold "
+                f"{r['plain_landmark_read']['cold']['median_us']:.1f} us")
         log("per-token decode over the 16M history (one token, retrieval reused for the chunk)")
         r = token_decode_latency(I.INFER_16M)
         infer["16M_token"] = r
@@ -755,6 +872,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_with_launch_events": ms_bracketed,
         "step_spread": spread,
         "higher_is_better": True,
         "scaling": "weak",
@@ -767,6 +885,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "kernel_ceilings": backward_kernels,
         "inference_latency": infer,
         "landmark_backward": lmk,
         "sliding_window": sw,

@@ -38,8 +38,9 @@
  *     the landmark of chunk t-1 retrieves for chunk t; shift = 0 when the caller passes the
  *     landmark of the chunk being generated).  Query chunks whose row is missing or has no
  *     valid slot get o = 0, lse = -inf, dq = 0.
- *   - Pointers to the floating tensors, lq, lk and lse must be 16-byte aligned; idx, score,
- *     dscore 4-byte aligned.  Otherwise GCA_ERR_MISALIGNED.
+ *   - Pointers to the floating tensors, lq, lk and the lse of gca_forward / gca_backward must be
+ *     16-byte aligned; idx, score, dscore and the lse of gca_sw_forward / gca_sw_backward
+ *     ([B, H, L] fp32) 4-byte aligned.  Otherwise GCA_ERR_MISALIGNED.
  *   - Every call validates all arguments on the host before touching the GPU and enqueues
  *     nothing when it returns an error.  A launch failure returns GCA_ERR_HIP; the HIP code
  *     is then available from gca_last_hip_error() (per calling thread).  Faults inside
@@ -151,6 +152,9 @@ gca_status gca_forward(const gca_problem* problem, const void* q, const void* k,
  *   dq_t     = attn_scale sum_{k,u} dz_u K_u,
  *   dk_u     = attn_scale sum dz_u q_t,   dv_u = sum w_k a_u dout_t, both summed over all
  *              groups and every (token, slot) that retrieved the chunk of u (zero if none).
+ * Slots count exactly as in gca_forward: every slot with 0 <= idx < n_kv, whether or not
+ * idx < q_chunk_base + row (so idx built by the caller, e.g. the compact buffers of
+ * gca_fetch_chunks, is differentiated as the forward used it).
  * q, k, v, idx, score, lse (from gca_forward), dout: inputs; dq, dk, dv, dscore: outputs.
  * dk and dv are accumulated in fp32 in a fixed order and rounded once to dtype.
  * ws: >= gca_workspace_size(BACKWARD); it holds, among others, an inverse retrieval index of

@@ -1587,9 +1587,11 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
 // prefix of the masks' popcounts gives every (word, chunk) its first output position.  Phase 3:
 // one thread per row writes each of its entries at that position plus the row's rank among the
 // word's rows naming the chunk, so each chunk's entries come out in row order.  Only rows that feed a query
-// chunk (row + shift < n_q) and can hold a chunk of this block (global chunk index q_base + row
-// above the block's first chunk) are marked.  Runs after the query-major pass, which writes the
-// fusion weights.
+// chunk (row + shift < n_q) are marked; with causal_rows (the landmark gradients) also only rows
+// that can hold a chunk of this block (global chunk index q_base + row above the block's first
+// chunk), a coarse filter that the landmark key pass refines per entry.  The GCA backward lists
+// every row, so its key-major pass counts the same slots (0 <= j < n_kv) as its query-major pass.
+// Runs after the query-major pass, which writes the fusion weights.
 constexpr int kIdxThreads = 256;
 constexpr int kIdxWords = 16;
 constexpr int kIdxRows = kIdxWords * 32;
@@ -1607,7 +1609,8 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
   const int32_t j = j0 + lane;
   // chunk ids, row counts and (g, row) indices fit in int32 (checked on the host)
   const int32_t nq = static_cast<int32_t>(p.n_q);
-  const int32_t row_lo = static_cast<int32_t>(j0 - p.q_base + 1 > 0 ? j0 - p.q_base + 1 : 0);
+  const int32_t row_lo =
+      p.causal_rows ? static_cast<int32_t>(j0 - p.q_base + 1 > 0 ? j0 - p.q_base + 1 : 0) : 0;
   const int32_t row_hi = nq - p.shift;
   const int32_t n_rows = p.G * nq;
   const int K = p.K;

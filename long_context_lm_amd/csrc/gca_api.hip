@@ -398,6 +398,7 @@ gca_status gca_landmark_backward(const gca_problem* problem, const void* lq, con
     a.idx = idx;
     a.wts = const_cast<float*>(dscore);
     a.shift = 0;
+    a.causal_rows = 1;
     a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
     a.counts = reinterpret_cast<int32_t*>(w + L.counts);
     GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));

@@ -67,6 +67,9 @@ struct AttendParams {
   int64_t n_q, n_kv, q_base;
   int32_t G, B, H, K, shift;
   int32_t pair_cap;     // G * n_q: most retrievals one key chunk can receive
+  int32_t causal_rows;  // inverse index: 1 = list only rows whose global chunk lies after the key
+                        // chunk (the landmark gradients' rule j < q_base + row); 0 = every row
+                        // (the GCA backward, whose other passes count every 0 <= j < n_kv)
   float attn_scale;
 };
 

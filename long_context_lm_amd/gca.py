@@ -127,6 +127,15 @@ class Config:
     attn_scale: float = 1.0 / math.sqrt(64)
     score_scale: float = 1.0 / math.sqrt(64)
 
+    def shape(self, name: str):
+        """The tensor shape include/gca.h states for `name` under this problem."""
+        G, B, H, nq, nkv, K = self.G, self.B, self.H, self.n_q, self.n_kv, self.topk
+        return {
+            "lq": (G, B, nq, 64), "lk": (G, B, nkv, 64),
+            "q": (G, B, H, nq * 64, 64), "kv": (B, H, nkv * 64, 64),
+            "sel": (G, B, nq, K), "lse": (G, B, H, nq, K, 64),
+        }[name]
+
     def problem(self) -> Problem:
         return Problem(B=self.B, G=self.G, H=self.H, S=64, n_q_chunks=self.n_q,
                        q_chunk_base=self.q_chunk_base, n_kv_chunks=self.n_kv, d_head=64,
@@ -138,6 +147,32 @@ class Config:
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _expect(name: str, t, shape, dtype, device=None, host_ok: bool = False):
+    """Refuse a tensor the C ABI would misread: the library sees only a pointer, so the shape,
+    dtype, layout and device that include/gca.h states are checked here, before the call."""
+    import torch
+
+    if t is None:
+        raise ValueError(f"{name}: tensor required")
+    # any row-major view of the stated shape is the same memory (e.g. k as [B,H,n_kv*64,64] or
+    # [B,H,n_kv,64,64]); what the library would misread is a different element count
+    want = 1
+    for x in shape:
+        want *= int(x)
+    if t.numel() != want:
+        raise ValueError(f"{name}: shape {tuple(t.shape)} ({t.numel()} elements), expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (row-major)")
+    if t.device.type != "cuda":
+        # host sources of gca_fetch_chunks: the library itself tells pinned from pageable memory
+        if not host_ok:
+            raise ValueError(f"{name}: must be a GPU tensor")
+    elif device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
 
 
 def _stream():
@@ -156,6 +191,13 @@ def workspace_size(op: int, cfg: Config) -> int:
     prob = cfg.problem()
     _check("gca_workspace_size", load().gca_workspace_size(op, ctypes.byref(prob), ctypes.byref(n)))
     return n.value
+
+
+def _ws_bytes(ws, device) -> int:
+    """Byte size of a caller-provided workspace (a contiguous tensor on the call's device)."""
+    if not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace: must be a contiguous tensor on {device}")
+    return ws.numel() * ws.element_size()
 
 
 def _workspace(op: int, cfg: Config, device):
@@ -181,14 +223,30 @@ def retrieve(cfg: Config, lq, lk, idx=None, score=None, ws=None):
     shp = (cfg.G, cfg.B, cfg.n_q, cfg.topk)
     idx = torch.empty(shp, dtype=torch.int32, device=dev) if idx is None else idx
     score = torch.empty(shp, dtype=torch.float32, device=dev) if score is None else score
+    ft = _torch_dtype(cfg)
+    _expect("lq", lq, cfg.shape("lq"), ft, dev)
+    _expect("lk", lk, cfg.shape("lk"), ft, dev)
+    _expect("idx", idx, shp, torch.int32, dev)
+    _expect("score", score, shp, torch.float32, dev)
     if ws is None:
         ws, n = _workspace(OP_RETRIEVE, cfg, dev)
     else:
-        n = ws.numel()
+        n = _ws_bytes(ws, dev)
     prob = cfg.problem()
     _check("gca_retrieve", load().gca_retrieve(ctypes.byref(prob), _ptr(lq), _ptr(lk), _ptr(idx),
                                                _ptr(score), _ptr(ws), n, _stream()))
     return idx, score
+
+
+def _check_attend(cfg: Config, q, k, v, idx, score, dev):
+    import torch
+
+    ft = _torch_dtype(cfg)
+    _expect("q", q, cfg.shape("q"), ft, dev)
+    _expect("k", k, cfg.shape("kv"), ft, dev)
+    _expect("v", v, cfg.shape("kv"), ft, dev)
+    _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
+    _expect("score", score, cfg.shape("sel"), torch.float32, dev)
 
 
 def forward(cfg: Config, q, k, v, idx, score, need_lse: bool = True, o=None, lse=None):
@@ -199,6 +257,10 @@ def forward(cfg: Config, q, k, v, idx, score, need_lse: bool = True, o=None, lse
     o = torch.empty_like(q) if o is None else o
     if need_lse and lse is None:
         lse = torch.empty((cfg.G, cfg.B, cfg.H, cfg.n_q, cfg.topk, 64), dtype=torch.float32, device=dev)
+    _check_attend(cfg, q, k, v, idx, score, dev)
+    _expect("o", o, cfg.shape("q"), _torch_dtype(cfg), dev)
+    if need_lse:
+        _expect("lse", lse, cfg.shape("lse"), torch.float32, dev)
     prob = cfg.problem()
     _check("gca_forward", load().gca_forward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                              _ptr(score), _ptr(o), _ptr(lse) if need_lse else None,
@@ -218,10 +280,18 @@ def backward(cfg: Config, q, k, v, idx, score, lse, dout, ws=None, out=None):
         dscore = torch.empty(idx.shape, dtype=torch.float32, device=dev)
     else:
         dq, dk, dv, dscore = out
+    ft = _torch_dtype(cfg)
+    _check_attend(cfg, q, k, v, idx, score, dev)
+    _expect("lse", lse, cfg.shape("lse"), torch.float32, dev)
+    _expect("dout", dout, cfg.shape("q"), ft, dev)
+    _expect("dq", dq, cfg.shape("q"), ft, dev)
+    _expect("dk", dk, cfg.shape("kv"), ft, dev)
+    _expect("dv", dv, cfg.shape("kv"), ft, dev)
+    _expect("dscore", dscore, cfg.shape("sel"), torch.float32, dev)
     if ws is None:
         ws, n = _workspace(OP_BACKWARD, cfg, dev)
     else:
-        n = ws.numel()
+        n = _ws_bytes(ws, dev)
     prob = cfg.problem()
     _check("gca_backward", load().gca_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                                _ptr(score), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
@@ -234,10 +304,15 @@ def landmark_backward(cfg: Config, lq, lk, idx, dscore, ws=None, out=None):
     import torch
 
     dlq, dlk = (torch.empty_like(lq), torch.empty_like(lk)) if out is None else out
+    dev, ft = lq.device, _torch_dtype(cfg)
+    for name, t, shp in (("lq", lq, "lq"), ("lk", lk, "lk"), ("dlq", dlq, "lq"), ("dlk", dlk, "lk")):
+        _expect(name, t, cfg.shape(shp), ft, dev)
+    _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
+    _expect("dscore", dscore, cfg.shape("sel"), torch.float32, dev)
     if ws is None:
         ws, n = _workspace(OP_LANDMARK_BACKWARD, cfg, lq.device)
     else:
-        n = ws.numel()
+        n = _ws_bytes(ws, lq.device)
     prob = cfg.problem()
     _check("gca_landmark_backward", load().gca_landmark_backward(ctypes.byref(prob), _ptr(lq), _ptr(lk), _ptr(idx),
                                                                  _ptr(dscore), _ptr(dlq), _ptr(dlk), _ptr(ws), n,
@@ -250,6 +325,14 @@ def decode_tokens(cfg: Config, q, k, v, idx, score, o=None):
     import torch
 
     o = torch.empty_like(q) if o is None else o
+    dev, ft = q.device, _torch_dtype(cfg)
+    n_tok = int(q.shape[-2]) if q.dim() == 5 else 0
+    _expect("q", q, (cfg.G, cfg.B, cfg.H, n_tok, 64), ft, dev)
+    _expect("o", o, (cfg.G, cfg.B, cfg.H, n_tok, 64), ft, dev)
+    _expect("k", k, cfg.shape("kv"), ft, dev)
+    _expect("v", v, cfg.shape("kv"), ft, dev)
+    _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
+    _expect("score", score, cfg.shape("sel"), torch.float32, dev)
     prob = cfg.problem()
     _check("gca_decode_tokens", load().gca_decode_tokens(ctypes.byref(prob), int(q.shape[-2]), _ptr(q), _ptr(k),
                                                          _ptr(v), _ptr(idx), _ptr(score), _ptr(o), _stream()))
@@ -268,6 +351,11 @@ def sw_forward(cfg: Config, q, k, v, window: int = 512, need_lse: bool = True, o
     o = torch.empty_like(q) if o is None else o
     if need_lse and lse is None:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    seq = (cfg.B, cfg.H, cfg.n_q * 64, 64)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _expect(name, t, seq, _torch_dtype(cfg), q.device)
+    if need_lse:
+        _expect("lse", lse, seq[:-1], torch.float32, q.device)
     prob = cfg.problem()
     _check("gca_sw_forward", load().gca_sw_forward(ctypes.byref(prob), int(window), _ptr(q), _ptr(k), _ptr(v),
                                                    _ptr(o), _ptr(lse) if need_lse else None, _stream()))
@@ -279,10 +367,14 @@ def sw_backward(cfg: Config, q, k, v, o, lse, dout, window: int = 512, ws=None, 
     import torch
 
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None else out
+    seq = (cfg.B, cfg.H, cfg.n_q * 64, 64)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(name, t, seq, _torch_dtype(cfg), q.device)
+    _expect("lse", lse, seq[:-1], torch.float32, q.device)
     if ws is None:
         ws, n = _workspace(OP_SW_BACKWARD, cfg, q.device)
     else:
-        n = ws.numel()
+        n = _ws_bytes(ws, q.device)
     prob = cfg.problem()
     _check("gca_sw_backward", load().gca_sw_backward(ctypes.byref(prob), int(window), _ptr(q), _ptr(k), _ptr(v),
                                                      _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -308,6 +400,13 @@ def fetch_chunks(cfg: Config, idx, k, v, out=None):
         out = (torch.empty(shape, dtype=k.dtype, device=dev), torch.empty(shape, dtype=v.dtype, device=dev),
                torch.empty_like(idx))
     k_out, v_out, idx_out = out
+    ft = _torch_dtype(cfg)
+    _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
+    _expect("k", k, cfg.shape("kv"), ft, host_ok=True)
+    _expect("v", v, cfg.shape("kv"), ft, host_ok=True)
+    _expect("k_out", k_out, (cfg.B, cfg.H, n_c * 64, 64), ft, dev)
+    _expect("v_out", v_out, (cfg.B, cfg.H, n_c * 64, 64), ft, dev)
+    _expect("idx_out", idx_out, cfg.shape("sel"), torch.int32, dev)
     prob = cfg.problem()
     _check("gca_fetch_chunks", load().gca_fetch_chunks(ctypes.byref(prob), _ptr(idx), _ptr(k), _ptr(v), _ptr(k_out),
                                                        _ptr(v_out), _ptr(idx_out), _stream()))

@@ -61,3 +61,25 @@ def lse_compare(name: str, got, ref, dtype: str):
     inf_g, inf_r = np.isneginf(got), np.isneginf(ref)
     assert np.array_equal(inf_g, inf_r), f"{name}: -inf pattern differs"
     return assert_close(name, got[~inf_r], ref[~inf_r], dtype)
+
+
+def assert_tiles_close(name: str, got, ref, bar: float = 1e-2):
+    """bf16 parity per 64x64 tile: the last two axes are (tokens, 64) with tokens a multiple of 64;
+    every (leading index, chunk) tile must be within relative L2 `bar` of the reference, and a tile
+    whose reference is exactly zero (no retrieval reaches it) must be exactly zero.  One wrong slot
+    in one tile of a large tensor moves the whole-tensor norm by little; this catches it."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    L, d = ref.shape[-2:]
+    assert L % 64 == 0, (name, ref.shape)
+    g = got.reshape(-1, L // 64, 64, d)
+    r = ref.reshape(-1, L // 64, 64, d)
+    num = np.sqrt(((g - r) ** 2).sum(axis=(-1, -2)))
+    den = np.sqrt((r ** 2).sum(axis=(-1, -2)))
+    zero = den == 0
+    assert np.all(num[zero] == 0), f"{name}: {int((num[zero] != 0).sum())} tiles nonzero where the reference is 0"
+    rel = num[~zero] / den[~zero]
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= bar, f"{name}: worst tile rel-L2 {worst:.3e} > {bar} ({int((rel > bar).sum())} tiles)"
+    return worst

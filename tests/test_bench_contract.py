@@ -40,3 +40,27 @@ def test_kernel_figures_count_valid_slots():
     assert figs["bwd_key"]["flops"] == figs["bwd_query"]["flops"] == figs["attend_fwd"]["flops"]
     # causal landmark pairs: G * B * sum_i i
     assert figs["score_topk"]["flops"] == 2 * 64 * 2 * 2 * (16 * 15 // 2)
+
+
+def test_step_roofline_at_the_16k_training_shape():
+    """The step floor: forward at its HBM time (Q, K, V, O, LSE) plus backward at its matrix-core
+    time (four 64x64x64 products per tile) = 163.6 + 322.8 us at the 16K, G=2 shape, where every
+    (group, batch row) has sum_c min(c - 1, 8) = 2004 valid (chunk, slot) pairs."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from long_context_lm_amd import inputs as I
+
+    shape = I.TRAIN_16K_G2
+    idx = np.full((2, 8, 256, 8), -1, dtype=np.int32)
+    for r in range(256):
+        idx[:, :, r, : min(r, 8)] = 0
+    sr = bench.step_roofline(shape, idx)
+    assert sr["tiles"] == 2 * 8 * 2004 * 12 == 384_768
+    T = 8 * 16384 * 12 * 64 * 2
+    lse = 2 * 8 * 16384 * 12 * 8 * 4
+    assert sr["forward"]["bytes"] == 6 * T + lse + 2 * 8 * 256 * 8 * 8
+    assert sr["backward"]["flops"] == 4 * 2 * 64 ** 3 * 384_768
+    fwd_us = sr["forward"]["bytes"] / 8e12 * 1e6
+    bwd_us = sr["backward"]["flops"] / 2.5e15 * 1e6
+    assert abs(fwd_us - 163.6) < 0.1 and abs(bwd_us - 322.8) < 0.1
+    assert abs(sr["floor_us"] - (fwd_us + bwd_us)) < 1e-6

@@ -13,7 +13,7 @@ import torch
 from long_context_lm_amd import gca
 from long_context_lm_amd import inputs as I
 from oracle import gca_oracle as O
-from tests.gpu_util import assert_close, config_for, lse_compare, say, upload
+from tests.gpu_util import assert_close, assert_tiles_close, config_for, lse_compare, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +54,13 @@ def _run_case(shape, dtype, scale=1.0, seed=0, need_bwd=True, **cfgkw):
     np.testing.assert_array_equal(sc.cpu().numpy(), r_sc)
     errs = {"o": assert_close("o", I.as_f64(o), r_o, dtype),
             "lse": lse_compare("lse", lse, r_lse, dtype)}
+    if dtype == "bf16":
+        assert_tiles_close("o", I.as_f64(o), r_o)
     if need_bwd:
         for name, got, ref in zip(("dq", "dk", "dv", "dscore"), grads, r_grads):
             errs[name] = assert_close(name, I.as_f64(got), ref, dtype)
+            if dtype == "bf16" and name != "dscore":
+                assert_tiles_close(name, I.as_f64(got), ref)
     say("  errors", {k: f"{v:.2e}" for k, v in errs.items()})
     return cfg, dev, (idx, sc, o, lse, grads)
 
@@ -359,14 +363,18 @@ def test_full_16k_training_step_sampled():
         ib, sb = r_idx[:, b:b + 1], r_sc[:, b:b + 1]
         r_o, r_lse = O.forward(x["q"], kb, vb, ib, sb, shift=1)
         assert_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o, "bf16")
+        worst = {"o": assert_tiles_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o)}
         lse_compare(f"lse[b={b}]", lse[:, b:b + 1], r_lse, "bf16")
         r_dq, r_dk, r_dv, r_ds = O.backward(x["q"], kb, vb, ib, sb, x["dout"], shift=1)
         assert_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq, "bf16")
+        worst["dq"] = assert_tiles_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq)
         for h in (0, 11):
             assert_close(f"dk[b={b},h={h}]", I.as_f64(dk[b:b + 1, h]), r_dk[:, h], "bf16")
             assert_close(f"dv[b={b},h={h}]", I.as_f64(dv[b:b + 1, h]), r_dv[:, h], "bf16")
+            worst[f"dk{h}"] = assert_tiles_close(f"dk[b={b},h={h}]", I.as_f64(dk[b:b + 1, h]), r_dk[:, h])
+            worst[f"dv{h}"] = assert_tiles_close(f"dv[b={b},h={h}]", I.as_f64(dv[b:b + 1, h]), r_dv[:, h])
         assert_close(f"dscore[b={b}]", ds[:, b:b + 1].cpu().numpy(), r_ds, "bf16")
-        say(f"batch row {b} matches")
+        say(f"batch row {b} matches; worst tile rel-L2", {k: f"{v:.1e}" for k, v in worst.items()})
 
 
 @pytest.mark.timeout(900)
@@ -397,12 +405,16 @@ def test_training_step_other_lengths_sampled(L, B, rows):
         ib, sb = r_idx[:, b:b + 1], r_sc[:, b:b + 1]
         r_o, r_lse = O.forward(qb, kb, vb, ib, sb, shift=1)
         assert_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o, "bf16")
+        assert_tiles_close(f"o[b={b}]", I.as_f64(o[:, b:b + 1]), r_o)
         lse_compare(f"lse[b={b}]", lse[:, b:b + 1], r_lse, "bf16")
         r_dq, r_dk, r_dv, r_ds = O.backward(qb, kb, vb, ib, sb, dob, shift=1)
         assert_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq, "bf16")
+        assert_tiles_close(f"dq[b={b}]", I.as_f64(dq[:, b:b + 1]), r_dq)
         for h in (0, 11):
             assert_close(f"dk[b={b},h={h}]", I.as_f64(dk[b:b + 1, h]), r_dk[:, h], "bf16")
             assert_close(f"dv[b={b},h={h}]", I.as_f64(dv[b:b + 1, h]), r_dv[:, h], "bf16")
+            assert_tiles_close(f"dk[b={b},h={h}]", I.as_f64(dk[b:b + 1, h]), r_dk[:, h])
+            assert_tiles_close(f"dv[b={b},h={h}]", I.as_f64(dv[b:b + 1, h]), r_dv[:, h])
         assert_close(f"dscore[b={b}]", ds[:, b:b + 1].cpu().numpy(), r_ds, "bf16")
         say(f"batch row {b} matches")
 
@@ -438,6 +450,8 @@ def test_forward_without_lse(case):
         r_o, _ = O.forward(I.as_f64(host["q"][:, b:b + 1]), I.as_f64(host["k"][b:b + 1]),
                            I.as_f64(host["v"][b:b + 1]), r_idx[:, b:b + 1], r_sc[:, b:b + 1], shift=1)
         assert_close(f"o[b={b}]", I.as_f64(o_inf[:, b:b + 1]), r_o, dtype)
+        if dtype == "bf16":
+            assert_tiles_close(f"o[b={b}]", I.as_f64(o_inf[:, b:b + 1]), r_o)
     say("  matches")
 
 
