@@ -129,6 +129,22 @@ gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* 
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * gca_retrieve without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP stream capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid allocation.  Same arguments (minus ws), same results bit for bit, same validation.
+ * Rows longer than one scan block keep their partial top-k lists in a device array inside the
+ * library (512 KiB per GPU, one copy per GPU, resident until the process ends; located with
+ * hipGetSymbolAddress on the first call on each device) instead of a caller workspace.  Nothing
+ * in it needs setup.  Every call on one GPU shares that array: calls that overlap on one GPU
+ * (several streams or host threads) race and must be ordered on one stream.  Never allocates.
+ * Errors: those of gca_retrieve; GCA_ERR_UNSUPPORTED if the problem needs more scratch than the
+ * array holds (gca_workspace_size(RETRIEVE) > 512 KiB; the scan's grid cap keeps every problem
+ * within 384 KiB); GCA_ERR_HIP if the device or the array's address cannot be obtained.
+ */
+gca_status gca_retrieve_static(const gca_problem* problem, const void* lq, const void* lk,
+                               int32_t* idx, float* score, void* stream);
+
+/*
  * GCA forward [Notes, Key designs: GCA].  For query chunk t with row = t - shift, valid slots
  * k (0 <= idx[k] < n_kv; gca_retrieve only produces j < min(i, n_kv)), w = softmax over the
  * valid slots of score[g,b,row,:]:

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/gca.h"
@@ -230,18 +231,27 @@ gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes)
   }
 }
 
-gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* lk, int32_t* idx,
-                        float* score, void* ws, size_t ws_bytes, void* stream) {
-  GCA_TRY(validate_problem(problem));
-  const gca_problem* p = problem;
+}  // extern "C"
+
+namespace gca {
+namespace {
+
+gca_status retrieve_check(const gca_problem* p, const void* lq, const void* lk, const int32_t* idx,
+                          const float* score) {
+  GCA_TRY(validate_problem(p));
   const bool any = p->n_q_chunks > 0;
   GCA_TRY(check_tensor(lq, any, 16));
   GCA_TRY(check_tensor(lk, any && p->n_kv_chunks > 0, 16));
   GCA_TRY(check_tensor(idx, any, 4));
   GCA_TRY(check_tensor(score, any, 4));
-  const RetrievePlan plan = plan_retrieve(p);
-  GCA_TRY(check_ws(plan.ws, ws, ws_bytes));
-  if (!any) return GCA_OK;
+  return GCA_OK;
+}
+
+// The launches of a retrieval whose arguments passed retrieve_check, with a workspace of at least
+// plan.ws bytes at ws.
+gca_status retrieve_launch(const gca_problem* p, const RetrievePlan& plan, const void* lq, const void* lk,
+                           int32_t* idx, float* score, void* ws, void* stream) {
+  if (p->n_q_chunks == 0) return GCA_OK;
 
   RetrieveParams rp{};
   rp.lq = lq;
@@ -271,6 +281,64 @@ gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* 
   GCA_TRY(launch(kScoreTopk, s, [&] { return launch_score_topk(rp, f32, s); }));
   if (plan.nblk > 1) GCA_TRY(launch(kTopkMerge, s, [&] { return launch_topk_merge(rp, s); }));
   return GCA_OK;
+}
+
+// Scratch of gca_retrieve_static: the partial top-k lists of rows that span several scan blocks.
+// The scan grid is capped at kRetrieveMaxWaves waves, so a problem has at most that many
+// (row, block) lists of at most 16 {key, score} entries: 2048 * 16 * (8 + 4) bytes = 384 KiB.
+// One copy per GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the device address that hipGetSymbolAddress returns
+// for the current device, looked up once per device and kept in scratch_ptr.
+constexpr size_t kStaticScratchBytes = size_t{512} << 10;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+gca_status static_scratch(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    t_last_hip_error = static_cast<int>(e);
+    return GCA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return GCA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || ptr == nullptr) {
+      t_last_hip_error = static_cast<int>(r != hipSuccess ? r : hipErrorInvalidSymbol);
+      return GCA_ERR_HIP;
+    }
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return GCA_OK;
+}
+
+}  // namespace
+}  // namespace gca
+
+extern "C" {
+
+gca_status gca_retrieve(const gca_problem* problem, const void* lq, const void* lk, int32_t* idx,
+                        float* score, void* ws, size_t ws_bytes, void* stream) {
+  GCA_TRY(retrieve_check(problem, lq, lk, idx, score));
+  const RetrievePlan plan = plan_retrieve(problem);
+  GCA_TRY(check_ws(plan.ws, ws, ws_bytes));
+  return retrieve_launch(problem, plan, lq, lk, idx, score, ws, stream);
+}
+
+gca_status gca_retrieve_static(const gca_problem* problem, const void* lq, const void* lk, int32_t* idx,
+                               float* score, void* stream) {
+  GCA_TRY(retrieve_check(problem, lq, lk, idx, score));
+  const RetrievePlan plan = plan_retrieve(problem);
+  if (plan.ws > kStaticScratchBytes) return GCA_ERR_UNSUPPORTED;
+  if (problem->n_q_chunks == 0) return GCA_OK;
+  void* ws = nullptr;
+  if (plan.ws > 0) GCA_TRY(static_scratch(&ws));
+  return retrieve_launch(problem, plan, lq, lk, idx, score, ws, stream);
 }
 
 gca_status gca_forward(const gca_problem* problem, const void* q, const void* k, const void* v,

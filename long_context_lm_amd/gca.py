@@ -49,6 +49,7 @@ class Problem(ctypes.Structure):
 EXPORTS = (
     "gca_workspace_size",
     "gca_retrieve",
+    "gca_retrieve_static",
     "gca_forward",
     "gca_backward",
     "gca_status_string",
@@ -86,6 +87,7 @@ def load() -> ctypes.CDLL:
     P = ctypes.POINTER(Problem)
     lib.gca_workspace_size.argtypes = [ctypes.c_int, P, ctypes.POINTER(sz)]
     lib.gca_retrieve.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.gca_retrieve_static.argtypes = [P, vp, vp, vp, vp, vp]
     lib.gca_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gca_landmark_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -93,7 +95,7 @@ def load() -> ctypes.CDLL:
     lib.gca_decode_tokens.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
     lib.gca_sw_forward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     lib.gca_sw_backward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "gca_landmark_backward",
+    for f in ("gca_workspace_size", "gca_retrieve", "gca_retrieve_static", "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gca_status_string.argtypes = [ctypes.c_int]
@@ -247,6 +249,26 @@ def _check_attend(cfg: Config, q, k, v, idx, score, dev):
     _expect("v", v, cfg.shape("kv"), ft, dev)
     _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
     _expect("score", score, cfg.shape("sel"), torch.float32, dev)
+
+
+def retrieve_static(cfg: Config, lq, lk, idx=None, score=None):
+    """gca_retrieve_static (no workspace, no allocation inside the library):
+    returns (idx int32 [G,B,n_q,K], score fp32 [G,B,n_q,K])."""
+    import torch
+
+    dev = lq.device
+    shp = (cfg.G, cfg.B, cfg.n_q, cfg.topk)
+    idx = torch.empty(shp, dtype=torch.int32, device=dev) if idx is None else idx
+    score = torch.empty(shp, dtype=torch.float32, device=dev) if score is None else score
+    ft = _torch_dtype(cfg)
+    _expect("lq", lq, cfg.shape("lq"), ft, dev)
+    _expect("lk", lk, cfg.shape("lk"), ft, dev)
+    _expect("idx", idx, shp, torch.int32, dev)
+    _expect("score", score, shp, torch.float32, dev)
+    prob = cfg.problem()
+    _check("gca_retrieve_static", load().gca_retrieve_static(ctypes.byref(prob), _ptr(lq), _ptr(lk), _ptr(idx),
+                                                             _ptr(score), _stream()))
+    return idx, score
 
 
 def forward(cfg: Config, q, k, v, idx, score, need_lse: bool = True, o=None, lse=None):
