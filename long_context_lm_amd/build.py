@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -54,13 +55,80 @@ def _compile(src: str, obj: str) -> tuple[str, int, str]:
     return src, r.returncode, err
 
 
+# Files whose kernels copy tiles into LDS with copy16_async_untracked (gca_device.hpp) and wait
+# for those copies with counted vmcnt waits.  The counts assume that the only vector memory
+# operations in flight are the ones the kernel issued itself.  Compiler-issued ones would make a
+# counted wait release before the copy it guards: scratch spills and reloads, flat instructions
+# (LDS or global memory reached through generic pointers count in vmcnt too), or memory
+# instructions inside a called function.  guard_untracked_copies() fails the build if the device
+# code of these files contains any of them.
+UNTRACKED_COPY_SOURCES = ["csrc/attend.hip", "csrc/retrieve.hip"]
+_MEMORY_OPS = ("global_", "flat_", "scratch_", "buffer_", "ds_", "s_load", "s_buffer", "s_store")
+
+
+def _device_asm(src: str) -> str:
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(src, []), "--cuda-device-only", "-S",
+           os.path.join(HERE, src), "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"device assembly of {src} failed:\n{r.stderr}")
+    return r.stdout
+
+
+def untracked_copy_violations(asm: str) -> list[str]:
+    """Reasons the counted waits of this device assembly could be wrong (empty list: none)."""
+    bad = []
+    kernel = None
+    for line in asm.splitlines():
+        t = line.strip()
+        if t.startswith(".amdhsa_kernel "):
+            kernel = t.split()[1]
+        elif t.startswith(".end_amdhsa_kernel"):
+            kernel = None
+        elif kernel and t.startswith(".amdhsa_private_segment_fixed_size") and t.split()[1] != "0":
+            bad.append(f"{kernel}: uses scratch ({t.split()[1]} bytes per lane)")
+        elif kernel and t.startswith(".amdhsa_uses_dynamic_stack") and t.split()[1] != "0":
+            bad.append(f"{kernel}: dynamic stack")
+    # instructions, by function; functions other than kernels are callees
+    kernels = set()
+    for line in asm.splitlines():
+        t = line.strip()
+        if t.startswith(".amdhsa_kernel "):
+            kernels.add(t.split()[1])
+    fn = None
+    for line in asm.splitlines():
+        label = re.match(r"([A-Za-z_][\w$]*):", line)
+        if label:
+            fn = label.group(1)
+            continue
+        if fn is None or not line.startswith("\t") or line.lstrip().startswith((";", ".")):
+            continue
+        op = line.split()[0] if line.split() else ""
+        if op.startswith("flat_"):
+            bad.append(f"{fn}: flat instruction {op}")
+        elif fn not in kernels and op.startswith(_MEMORY_OPS):
+            bad.append(f"{fn} (called from a kernel): memory instruction {op}")
+    return sorted(set(bad))
+
+
+def guard_untracked_copies() -> None:
+    """Fail if a file using untracked LDS copies compiles to code that breaks their waits."""
+    bad = []
+    for src in UNTRACKED_COPY_SOURCES:
+        bad += [f"{src}: {b}" for b in untracked_copy_violations(_device_asm(src))]
+    if bad:
+        raise RuntimeError("untracked LDS copies with compiler-issued memory operations:\n  " + "\n  ".join(bad))
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link libgca.so; returns the library path."""
     bdir = os.path.join(ROOT, "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = [os.path.join(bdir, os.path.basename(s).replace(".hip", ".o")) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
+        guard = ex.submit(guard_untracked_copies)
         results = list(ex.map(_compile, SOURCES, objs))
+        guard.result()
     failed = False
     for src, rc, err in results:
         if err.strip() and (verbose or rc != 0):

@@ -1429,19 +1429,17 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
 // ------------------------------------------------------------- backward, key-major (dK, dV)
 struct PairRef {
   int g, slot;
-  int64_t row, t;
+  int64_t t;
 };
 
-// Entry codes are (g * n_q + row) * K + slot < 2^31; decoded in wave-uniform 32-bit arithmetic.
-__device__ __forceinline__ PairRef decode_pair(const AttendParams& p, int32_t code) {
-  const int32_t c = __builtin_amdgcn_readfirstlane(code);
-  const int32_t nq = static_cast<int32_t>(p.n_q);
+// The backward's inverse index stores each entry decoded: {query chunk t, g * 16 + slot}
+// (wave-uniform), so the walk needs no integer division per entry.
+__device__ __forceinline__ PairRef decode_pair(const i32x2_t ent) {
+  const int32_t gs = __builtin_amdgcn_readfirstlane(ent[1]);
   PairRef r;
-  r.slot = c % p.K;
-  const int32_t gr = c / p.K;
-  r.row = gr % nq;
-  r.g = gr / nq;
-  r.t = r.row + p.shift;
+  r.t = __builtin_amdgcn_readfirstlane(ent[0]);
+  r.g = gs >> 4;
+  r.slot = gs & 15;
   return r;
 }
 
@@ -1489,7 +1487,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   // The list is walked in rounds of up to kEntRound entries {code, weight}, staged in LDS.  Each
   // wave issues kCopies per tile plus one vector copy (lanes < 16) per entry.
   auto fill = [&](const i32x2_t ent, char* buf) {
-    const PairRef r = decode_pair(p, ent[0]);
+    const PairRef r = decode_pair(ent);
     const int64_t gbh = (static_cast<int64_t>(r.g) * p.B + b) * p.H + h;
     const int64_t qrow0 = gbh * Lq + r.t * kChunk;
     off.copy(static_cast<const T*>(p.q) + qrow0 * kDim, buf, wave);
@@ -1507,7 +1505,18 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     const f32x4_t* vec = reinterpret_cast<const f32x4_t*>(cur + 2 * TL::kBytes);  // {b, e, b, e}
     // Both 32-query tiles' scores first, then each tile's elementwise work beside the other
     // tile's matrix-core work (the second tile's S and dP' products run beside the first tile's
-    // exp and dz, the first tile's dK and dV products beside the second tile's).
+    // exp and dz, the first tile's dK and dV products beside the second tile's).  Every row
+    // fragment of the entry is read before the first product, so the products wait once for the
+    // LDS reads instead of once per product.
+    Frag<T> qr[2][4], dr[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        qr[qt][s] = off.kfrag(Qs, qt, s);
+        dr[qt][s] = off.kfrag(Ds, qt, s);
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -1515,8 +1524,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
       pacc[qt] = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sacc[qt] = mma(off.kfrag(Qs, qt, s), kf[s], sacc[qt]);
-        pacc[qt] = mma(off.kfrag(Ds, qt, s), vf[s], pacc[qt]);
+        sacc[qt] = mma(qr[qt][s], kf[s], sacc[qt]);
+        pacc[qt] = mma(dr[qt][s], vf[s], pacc[qt]);
       }
     }
 #pragma unroll
@@ -1580,7 +1589,9 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
 
 // ------------------------------------------------------------- inverse retrieval index
 // For one batch row and 64 consecutive key chunks (lane = chunk j), list the retrievals that
-// selected each chunk as entries {(group, row, slot) code, fusion weight}, in (group, row) order.
+// selected each chunk, in (group, row) order, as entries {(group, row, slot) code, entry value}
+// (the landmark gradients: the value is d(score)) or, with entry_decoded (the GCA backward's
+// key-major pass), {query chunk row + shift, group * 16 + slot}.
 // Retrieval rows, flattened as gr = g * n_q + row, are handled kIdxRows at a time as 32-row
 // words.  Phase 1: one thread per row ORs the row's bit into the mask of every chunk of this
 // block the row names (integer OR: the result does not depend on the order).  Phase 2: a running
@@ -1633,7 +1644,7 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k) {  // all of the row's loads in flight together
         jv[k] = k < K ? p.idx[rbase + k] : -1;
-        wv[k] = k < K ? p.wts[rbase + k] : 0.f;
+        wv[k] = k < K && !p.entry_decoded ? p.wts[rbase + k] : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k) {
@@ -1661,7 +1672,8 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
     // A row counts once per chunk, with its first slot naming it.
     for (int lr = tid; lr < nr; lr += kIdxThreads) {
       const int32_t gr = gr0 + lr;
-      const int32_t row = gr - (gr / nq) * nq;
+      const int32_t g = gr / nq;
+      const int32_t row = gr - g * nq;
       if (row < row_lo || row >= row_hi) continue;
       const int w = lr >> 5;
       const uint32_t below = (1u << (lr & 31)) - 1u;
@@ -1677,7 +1689,8 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
         if (first_slot) {
           const int jj = jk - j0;
           const int32_t pos = first[w][jj] + __popc(mask[w][jj] & below);
-          out_b[static_cast<int64_t>(jk) * p.pair_cap + pos] = i32x2_t{gr * K + k, __float_as_int(wts_s[lr][k])};
+          out_b[static_cast<int64_t>(jk) * p.pair_cap + pos] =
+              p.entry_decoded ? i32x2_t{row + p.shift, g * 16 + k} : i32x2_t{gr * K + k, __float_as_int(wts_s[lr][k])};
         }
       }
     }

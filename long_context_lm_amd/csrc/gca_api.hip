@@ -89,6 +89,7 @@ gca_status validate_problem(const gca_problem* p) {
   if (!std::isfinite(p->gumbel_tau) || p->gumbel_tau < 0.f) return GCA_ERR_INVALID_ARGUMENT;
   if (p->S != 64 || p->d_head != 64 || p->d_lmk != 64) return GCA_ERR_UNSUPPORTED;
   if (p->topk > 16) return GCA_ERR_UNSUPPORTED;
+  if (p->G > (1 << 26)) return GCA_ERR_UNSUPPORTED;  // (group, slot) travels as 16 g + slot in int32
   // index ranges: chunk ids travel as int32, grids as 32-bit block counts
   const int64_t big = (int64_t{1} << 31) - 1;
   if (p->n_kv_chunks > big || p->q_chunk_base + p->n_q_chunks > big) return GCA_ERR_UNSUPPORTED;
@@ -413,6 +414,7 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   a.wts = reinterpret_cast<float*>(w + L.wts);
   a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
   a.counts = reinterpret_cast<int32_t*>(w + L.counts);
+  a.entry_decoded = 1;
   const bool f32 = p->dtype == GCA_F32;
   // With no query chunk, only the inverse index (empty lists) and the key-major pass (which
   // writes zero dk, dv for chunks nobody retrieved) run.

@@ -180,7 +180,11 @@ __device__ __forceinline__ void copy16_async(const void* gsrc, char* lds_wave_ba
 // The same copy issued from inline assembly: the compiler does not see it as a write to LDS, so
 // it never makes later LDS reads wait for it.  The caller must order every read of the target
 // after the copy itself (wait_vm_outstanding / barrier_copies_landed, then a barrier).  Extra
-// vector memory operations the compiler does not count only make its own waits stricter.
+// vector memory operations the compiler does not count only make its own waits stricter; the
+// caller's counted waits, though, hold only while its own copies and stores are the only vector
+// memory operations in flight (no scratch, no flat access, no callee touching memory: the build
+// checks this for every file that uses the copy).  gbase must already be a wave-uniform scalar
+// (the "s" constraint); never force a vector value into it with readfirstlane.
 __device__ __forceinline__ void copy16_async_untracked(const void* gbase, uint32_t lane_off, char* lds_wave_base) {
   const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(lds_wave_base)));
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(gbase), "{m0}"(lds_addr) : "memory");

@@ -61,12 +61,14 @@ struct AttendParams {
   float* delta;         // [G, B, H, n_q, K, 64, 2] {log2 w_k - lse_{t,k} log2 e, e_{t,k} = <dout_t, O_{t,k}>}
   float* dw_part;       // [G, B, n_q, H, K] per-head sums of e over a chunk's tokens
   float* wts;           // [G, B, n_q, K] fusion weights (0 on invalid slots)
-  int32_t* pairs;       // [B, n_kv, pair_cap, 2] {(g, row, slot) code, fusion weight} per retrieval of
-                        // each key chunk, in (g, row, slot) order
+  int32_t* pairs;       // [B, n_kv, pair_cap, 2] one entry per retrieval of each key chunk, in
+                        // (g, row, slot) order: {(g n_q + row) K + slot, value} (landmark
+                        // gradients), or {row + shift, 16 g + slot} with entry_decoded
   int32_t* counts;      // [B, n_kv] list lengths
   int64_t n_q, n_kv, q_base;
   int32_t G, B, H, K, shift;
   int32_t pair_cap;     // G * n_q: most retrievals one key chunk can receive
+  int32_t entry_decoded;  // inverse index entries for the key-major pass (see pairs)
   int32_t causal_rows;  // inverse index: 1 = list only rows whose global chunk lies after the key
                         // chunk (the landmark gradients' rule j < q_base + row); 0 = every row
                         // (the GCA backward, whose other passes count every 0 <= j < n_kv)
