@@ -7,8 +7,9 @@ bf16, synthetic N(0,1)/8 inputs).  Prints one JSON line: tokens/s with inputs re
 the roofline position of the dominant kernel (HIP events around each kernel launch inside the
 timed region), the CPU oracle timed on a bounded sample of the same workload, the per-chunk
 retrieve+attend latency over 1M- and 16M-token histories held in HBM, and the rows beside the
-step: landmark gradients, sliding-window attention, the forward-only workload (one group, no
-Gumbel noise, no LSE) and the step at 4K/16K/64K contexts with the same tokens per batch.
+step: landmark gradients, sliding-window attention, the window and GCA fused in one call, the
+forward-only workload (one group, no Gumbel noise, no LSE) and the step at 4K/16K/64K contexts
+with the same tokens per batch.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-inference] [--no-cpu-baseline]
                     [--no-scaling] [--copy-calibration]
@@ -326,6 +327,63 @@ def window_timing(B=8, H=12, n_c=256, window=512, iters=10):
         res["bwd_tflops"] = bwd_flops / (bwd_us * 1e-6) / 1e12
     res["mfma_frac"] = (fwd_flops + bwd_flops) / (us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12)
     del q, k, v, do, o, lse, grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def fused_timing(B=8, H=12, n_c=256, window=512, K=8, iters=10):
+    """The layer's sliding window and GCA over the same queries, summed (G = 1, W = 512, K = 8,
+    bf16, N(0,1)/8 inputs at the training shape): gca_fused_forward + gca_fused_backward against
+    the separate calls (gca_sw_forward + gca_forward, gca_sw_backward + gca_backward) plus the two
+    sums a caller of the separate calls needs (o and dq).  The retrieval is not timed (the same
+    indices serve both)."""
+    import torch
+
+    from long_context_lm_amd import gca
+
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    L = 64 * n_c
+
+    def mk(shape):
+        return (torch.randn(shape, generator=gen, device="cuda") / 8).to(torch.bfloat16)
+
+    q, k_sw, v_sw, k, v, do = (mk((B, H, L, 64)) for _ in range(6))
+    cfg = gca.Config(B=B, G=1, H=H, n_q=n_c, n_kv=n_c, topk=K, dtype="bf16", use_gumbel=True, seed=1)
+    idx, sc = gca.retrieve(cfg, mk((1, B, n_c, 64)), mk((1, B, n_c, 64)))
+    o = torch.empty_like(q)
+    lse_sw = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    lse = torch.empty(cfg.shape("lse"), dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+             torch.empty(idx.shape, dtype=torch.float32, device="cuda"))
+    ws = torch.empty(gca.workspace_size(gca.OP_FUSED_BACKWARD, cfg), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        gca.fused_forward(cfg, q, k_sw, v_sw, k, v, idx, sc, window, o=o, lse_sw=lse_sw, lse=lse)
+        gca.fused_backward(cfg, q, k_sw, v_sw, k, v, idx, sc, o, lse_sw, lse, do, window, ws=ws, out=grads)
+
+    swc = gca.sw_config(B, H, n_c)
+    ws_sw = torch.empty(gca.workspace_size(gca.OP_SW_BACKWARD, swc), dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty(gca.workspace_size(gca.OP_BACKWARD, cfg), dtype=torch.uint8, device="cuda")
+    o_sw, o_g = torch.empty_like(q), torch.empty_like(q)
+    g_sw = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    g_g = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), grads[5])
+    q1, do1, o_g1 = q[None], do[None], o_g[None]
+
+    def separate():
+        gca.sw_forward(swc, q, k_sw, v_sw, window, o=o_sw, lse=lse_sw)
+        gca.forward(cfg, q1, k, v, idx, sc, o=o_g1, lse=lse)
+        torch.add(o_sw, o_g, out=o)
+        gca.sw_backward(swc, q, k_sw, v_sw, o_sw, lse_sw, do, window, ws=ws_sw, out=g_sw)
+        gca.backward(cfg, q1, k, v, idx, sc, lse, do1, ws=ws_g, out=(g_g[0][None], g_g[1], g_g[2], g_g[3]))
+        torch.add(g_sw[0], g_g[0], out=grads[0])
+
+    ms_f, kern_f = _timed(fused, iters)
+    ms_s, kern_s = _timed(separate, iters)
+    res = {"workload": f"sliding window (W={window}) + GCA (K={K}, G=1) over the same queries, summed; B={B} L={L} "
+                       f"H={H} d=64 bf16, inputs N(0,1)/8; forward + backward",
+           "fused_us": ms_f * 1e3, "separate_us": ms_s * 1e3, "tokens_per_s_fused": B * L / (ms_f * 1e-3),
+           "kernels_us_fused": kern_f, "kernels_us_separate": kern_s}
+    del q, k_sw, v_sw, k, v, do, o, lse_sw, lse, grads, ws, ws_sw, ws_g, o_sw, o_g, g_sw, g_g
     torch.cuda.empty_cache()
     return res
 
@@ -822,6 +880,10 @@ def main():
         + ", ".join(f"{k} {v:.1f}" for k, v in sw["kernels_us"].items())
         + f"; fwd {sw.get('fwd_tflops', 0):.0f} TFLOP/s, bwd {sw.get('bwd_tflops', 0):.0f} TFLOP/s, "
         f"matrix-core fraction {sw['mfma_frac']:.3f}")
+    log("sliding window + GCA in one call (fused) against the separate calls, at the training shape")
+    fz = fused_timing()
+    log(f"  fused {fz['fused_us']:.1f} us, separate {fz['separate_us']:.1f} us per fwd+bwd; fused: "
+        + ", ".join(f"{k} {v:.1f}" for k, v in fz["kernels_us_fused"].items()))
     log("forward only at the training shape (G=1, no Gumbel, no LSE)")
     fwd = forward_timing()
     log(f"  {fwd['us_per_call']:.1f} us per call ({fwd['tokens_per_s'] / 1e6:.1f} M tokens/s), "
@@ -889,6 +951,7 @@ def main():
         "inference_latency": infer,
         "landmark_backward": lmk,
         "sliding_window": sw,
+        "fused_window_gca": fz,
         "forward_only": fwd,
         "length_scaling": scaling,
     }

@@ -77,7 +77,8 @@ typedef enum {
   GCA_OP_FORWARD = 1,
   GCA_OP_BACKWARD = 2,
   GCA_OP_LANDMARK_BACKWARD = 3,
-  GCA_OP_SW_BACKWARD = 4
+  GCA_OP_SW_BACKWARD = 4,
+  GCA_OP_FUSED_BACKWARD = 5
 } gca_op;
 
 /* Sizes and options of one problem.  Fields are read, never written. */
@@ -207,6 +208,44 @@ gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void
 gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const void* q, const void* k,
                            const void* v, const void* o, const float* lse, const void* dout,
                            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fused layer attention [Notes, Loss / training strategy: the layers that run GCA also run
+ * sliding-window self-attention, W = 512, beside the top-k retrieval].  Reading taken: both read
+ * the layer's queries and their outputs are summed, with one retrieval group in the layer:
+ *   o = SW(q, k_sw, v_sw; window) + GCA(q, k, v, idx, score)
+ * SW as gca_sw_forward (token i attends to keys max(0, i - window + 1) .. i of k_sw, v_sw), GCA as
+ * gca_forward with G = 1.  One kernel per query tile computes both on one Q tile and stores the
+ * sum once.
+ * problem: G must be 1; uses B, H, n_q_chunks (L = 64 n_q_chunks), n_kv_chunks, topk, shift,
+ * dtype, attn_scale.  window: positive multiple of 64.
+ * q, o [B, H, L, 64] (the same memory as [1, B, H, L, 64]); k_sw, v_sw [B, H, L, 64] (the layer's
+ * own keys and values); k, v [B, H, n_kv * 64, 64] (the history GCA retrieves from; may alias
+ * k_sw, v_sw); idx, score [1, B, n_q, K]: inputs.  o: output.  lse_sw [B, H, L] fp32 (the window's
+ * natural log-sum-exp) and lse [1, B, H, n_q, K, 64] fp32 (as gca_forward): outputs, each may be
+ * NULL (the backward needs both).  No workspace.  Alignment: lse_sw 4 bytes, the rest as above.
+ */
+gca_status gca_fused_forward(const gca_problem* problem, int32_t window, const void* q, const void* k_sw,
+                             const void* v_sw, const void* k, const void* v, const int32_t* idx,
+                             const float* score, void* o, float* lse_sw, float* lse, void* stream);
+
+/*
+ * Backward of gca_fused_forward, with dout the gradient of o:
+ *   dq = dq_sw + dq_gca (one pass per query tile), dk_sw, dv_sw (the window's keys and values,
+ *   as gca_sw_backward), dk, dv, dscore (the history's, as gca_backward with G = 1).
+ * The window's D = <dout, o_sw> is taken as <dout, o> - sum_k w_k e_k with the e_k of the GCA
+ * slots (o_gca = sum_k w_k O_k), so only the fused output o is needed.
+ * Inputs: q, k_sw, v_sw, k, v, idx, score, o, lse_sw, lse (from gca_fused_forward), dout.
+ * Outputs (overwritten): dq [B, H, L, 64], dk_sw, dv_sw [B, H, L, 64], dk, dv [B, H, n_kv*64, 64],
+ * dscore [1, B, n_q, K].  k_sw and k are separate tensors here even when the caller aliases them:
+ * then the gradient of that tensor is dk_sw + dk.  ws: >= gca_workspace_size(FUSED_BACKWARD)
+ * (the GCA backward's workspace plus B * H * L * 8 bytes; contents need no setup).
+ */
+gca_status gca_fused_backward(const gca_problem* problem, int32_t window, const void* q, const void* k_sw,
+                              const void* v_sw, const void* k, const void* v, const int32_t* idx,
+                              const float* score, const void* o, const float* lse_sw, const float* lse,
+                              const void* dout, void* dq, void* dk_sw, void* dv_sw, void* dk, void* dv,
+                              float* dscore, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Token-level decode [Notes, Key designs: GCA; Key designs: memory-offload inference]: while the

@@ -180,6 +180,12 @@ struct TileOffsets {
 #pragma unroll
     for (int n = 0; n < kCopies; ++n) copy16_async_untracked(g, cp[n], lds + (n * kWaves + wave) * 1024);
   }
+  // the same, to the LDS address lds_addr (lds_address of the buffer)
+  __device__ __forceinline__ void copy_at(const T* __restrict__ g, uint32_t lds_addr, int wave) const {
+#pragma unroll
+    for (int n = 0; n < kCopies; ++n)
+      copy16_async_untracked_at(g, cp[n], lds_addr + static_cast<uint32_t>((n * kWaves + wave) * 1024));
+  }
 
   __device__ __forceinline__ Frag<T> kfrag(const char* Ks, int tt, int s) const {
     if constexpr (sizeof(T) == 2) {
@@ -1724,6 +1730,548 @@ __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
   if (in_range) p.dscore[gid * p.K + k] = valid ? w * (dw - wdw) : 0.f;
 }
 
+// ------------------------------------------------- fused layer attention (window + GCA), forward
+// The layers that run GCA also run sliding-window self-attention (W = 512) [Notes, Loss /
+// training strategy].  Reading taken: both read the layer's queries and their outputs are summed,
+// with one retrieval group per layer:
+//   o = SW(q, k_sw, v_sw; W) + GCA(q, k, v, idx, score).
+// One query tile t walks one list of items: the window's key tiles kt0 .. t (online softmax, the
+// edge tiles masked), then the valid retrieval slots (one softmax each, weighted by w).  One K and
+// one V buffer, the copy pipeline running straight through from the last window tile to the first
+// retrieved chunk.  After the window's last tile the accumulators are normalized (1 / l per query),
+// so they hold the window's output, and each slot adds w_k O_k to them.  The Q tile is loaded
+// once and the sum is stored once.
+
+// Fused forward, one wave per 64-query tile (bf16), the pipeline of attend_fwd_wave_kernel.
+template <bool kLse>
+__global__ __launch_bounds__(64) void fused_fwd_kernel(AttendParams p) {
+  using T = bf16_t;
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, 1>;
+  constexpr int kC = Off::kCopies;
+  __shared__ __align__(1024) char Ks[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+
+  const int lane = threadIdx.x, li = lane & 31, hl = lane >> 5;
+  const QTileCoord c = query_tile_coord(p);
+  const int64_t Lq = p.n_q * kChunk;
+  const int64_t row0 = (static_cast<int64_t>(c.b) * p.H + c.h) * Lq;  // this (batch row, head)
+  const int64_t qrow0 = row0 + c.t * kChunk;
+  const WaveSlots sl = wave_slots(p, c.g, c.b, c.t - p.shift);
+  Frag<T> qf[2][4];
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const T* q = static_cast<const T*>(p.q) + (qrow0 + 32 * qh + li) * kDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qh][s].load(q + 16 * s + 8 * hl);
+  }
+  Off off;
+  off.init(0);
+  // copies address the buffers by their LDS addresses: with the two item loops below, the
+  // backend could not fold the null check of the generic pointer round trip of copy()
+  const uint32_t ks_addr = lds_address(Ks), vs_addr = lds_address(Vs);
+  float* const lse_q = kLse ? p.lse + slot_vec_offset(p, c.gbh, c.t, 0) + lane : nullptr;
+  if (kLse) {  // invalid slots: -inf (before any copy, so the copy counts below stay exact)
+    for (int k = 0; k < p.K; ++k)
+      if (!((sl.valid >> k) & 1u)) lse_q[k * kChunk] = -__builtin_inff();
+  }
+  const int64_t kt0 = c.t - p.m > 0 ? c.t - p.m : 0;
+  const int n_sw = static_cast<int>(c.t - kt0 + 1);
+  const int n_items = n_sw + __popc(sl.valid);
+  // item i: window tile kt0 + i (i < n_sw), else the next valid slot; separate cursors for the
+  // K copies, the V copies and the softmax, which reach each item at different times
+  uint32_t rem_k = sl.valid, rem_v = sl.valid, rem_s = sl.valid;
+  auto item_tile = [&](const void* sw_base, const void* kv_base, int i, uint32_t& rem) {
+    if (i < n_sw) return static_cast<const T*>(sw_base) + (row0 + (kt0 + i) * kChunk) * kDim;
+    const int slot = __builtin_ctz(rem);
+    rem &= rem - 1;
+    return kv_tile<T>(kv_base, p, c.b, c.h, __builtin_amdgcn_readlane(sl.j, slot));
+  };
+  off.copy_at(item_tile(p.k_sw, p.k, 0, rem_k), ks_addr, 0);
+  off.copy_at(item_tile(p.v_sw, p.v, 0, rem_v), vs_addr, 0);
+
+  f32x16_t oacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+  float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
+  const float c2 = p.attn_scale * kLog2e;
+  // the window's key tiles: online softmax; per query half, the softmax, then its P V products
+  for (int i = 0; i < n_sw; ++i) {  // wave-uniform
+    wait_vm_outstanding<kC>();  // K(i) landed: only V(i) may be in flight
+    f32x16_t sacc[2][2];
+    {  // K(i) into registers; the copy of K(i + 1) started behind it; S(i) = K(i) Q^T
+      Frag<T> kf[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[tt][s] = off.kfrag(Ks, tt, s);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K(i) in registers: the buffer is free
+      if (i + 1 < n_items) off.copy_at(item_tile(p.k_sw, p.k, i + 1, rem_k), ks_addr, 0);
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          sacc[qh][tt] = zero16();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sacc[qh][tt] = mma(kf[tt][s], qf[qh][s], sacc[qh][tt]);
+        }
+    }
+    const int64_t kt = kt0 + i;
+    const bool lower_edge = kt == c.t - p.m, diagonal = kt == c.t;
+    if (lower_edge || diagonal) sw_mask(sacc, lower_edge, diagonal);
+    Frag<T> vf[4][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qh][tt][r]);
+      mx = xor32_max(mx) * c2;  // log2 units
+      constexpr float kLazy = 8.f;  // as in sw_fwd_kernel
+      const bool grow = __ballot(mx > m_run[qh] + kLazy) != 0;
+      const float m_new = grow ? fmaxf(m_run[qh], mx) : m_run[qh];
+      const bool none = m_new == -__builtin_inff();
+      const float alpha = none ? 1.f : fast_exp2(m_run[qh] - m_new);
+      const float bias = none ? 0.f : -m_new;
+      float l = 0.f;
+      Frag<T> pf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = fast_exp2(__builtin_fmaf(sacc[qh][s >> 1][8 * (s & 1) + e], c2, bias));
+          l += x[e];
+        }
+        pf[s].set(x);
+      }
+      l_run[qh] = l_run[qh] * alpha + xor32_sum(l);
+      m_run[qh] = m_new;
+      if (grow) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qh][dt][r] *= alpha;
+      }
+      if (qh == 0) {  // V(i) into registers (landed: at most the K(i + 1) copies are outstanding);
+                      // the copy of V(i + 1) started behind it
+        if (i + 1 < n_items) wait_vm_outstanding<kC>();
+        else wait_vm_outstanding<0>();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) vf[s][dt] = off.vfrag(Vs, s, dt);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V(i) in registers: the buffer is free
+        if (i + 1 < n_items) off.copy_at(item_tile(p.v_sw, p.v, i + 1, rem_v), vs_addr, 0);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) oacc[qh][dt] = mma(vf[s][dt], pf[s], oacc[qh][dt]);
+    }
+  }
+  // the window is complete: its output, normalized per query
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const float f = __builtin_amdgcn_rcpf(l_run[qh]);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qh][dt][r] *= f;
+  }
+  // the retrieved slots: one softmax each, weighted by w
+  bool stored = false;  // the previous slot issued an lse store after its copies
+  for (int i = n_sw; i < n_items; ++i) {  // wave-uniform
+    if (stored) wait_vm_outstanding<kC + 1>();  // K(i) landed: only V(i) and that store may not have
+    else wait_vm_outstanding<kC>();
+    f32x16_t sacc[2][2];
+    {  // K(i) into registers; the copy of K(i + 1) started behind it; S(i) = K(i) Q^T
+      Frag<T> kf[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[tt][s] = off.kfrag(Ks, tt, s);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K(i) in registers: the buffer is free
+      if (i + 1 < n_items) off.copy_at(item_tile(p.k_sw, p.k, i + 1, rem_k), ks_addr, 0);
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          sacc[qh][tt] = zero16();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sacc[qh][tt] = mma(kf[tt][s], qf[qh][s], sacc[qh][tt]);
+        }
+    }
+    const int slot = __builtin_ctz(rem_s);
+    rem_s &= rem_s - 1;
+    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sl.w), slot));
+    float lse_v[2];
+    Frag<T> vf[4][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float l;
+      const float mx = tile_softmax(sacc[qh], c2, l);
+      lse_v[qh] = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
+      const float f = wk * __builtin_amdgcn_rcpf(l);
+      Frag<T> pf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sacc[qh][s >> 1][8 * (s & 1) + e] * f;
+        pf[s].set(x);
+      }
+      if (qh == 0) {  // V(i) into registers (landed: at most the K(i + 1) copies are outstanding);
+                      // the copy of V(i + 1) started behind it
+        if (i + 1 < n_items) wait_vm_outstanding<kC>();
+        else wait_vm_outstanding<0>();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) vf[s][dt] = off.vfrag(Vs, s, dt);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V(i) in registers: the buffer is free
+        if (i + 1 < n_items) off.copy_at(item_tile(p.v_sw, p.v, i + 1, rem_v), vs_addr, 0);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) oacc[qh][dt] = mma(vf[s][dt], pf[s], oacc[qh][dt]);
+    }
+    if (kLse) lse_q[slot * kChunk] = hl ? lse_v[1] : lse_v[0];
+    stored = kLse;
+  }
+
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    T* o = static_cast<T*>(p.o) + (qrow0 + 32 * qh + li) * kDim;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        store4(o + 32 * dt + 8 * a + 4 * hl, oacc[qh][dt][4 * a], oacc[qh][dt][4 * a + 1],
+               oacc[qh][dt][4 * a + 2], oacc[qh][dt][4 * a + 3]);
+    if (p.lse_sw && hl == qh)  // lane (li, hl) writes query 32 hl + li
+      p.lse_sw[qrow0 + 32 * qh + li] = m_run[qh] * kLn2f + __builtin_amdgcn_logf(l_run[qh]) * kLn2f;
+  }
+}
+
+// Fused forward, two waves of 32 queries per tile (fp32 tiles: the pipeline of attend_fwd_kernel
+// and sw_fwd2_kernel, single K and V buffers published by barriers).
+template <typename T, bool kLse>
+__global__ __launch_bounds__(kThreads) void fused_fwd2_kernel(AttendParams p) {
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, kWaves>;
+  constexpr int kC = Off::kCopies;
+  __shared__ __align__(1024) char Ks[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+  __shared__ SlotTable st;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hl = lane >> 5;
+  const QTileCoord c = query_tile_coord(p);
+  const int64_t Lq = p.n_q * kChunk;
+  const int64_t row0 = (static_cast<int64_t>(c.b) * p.H + c.h) * Lq;
+  const int64_t qrow0 = row0 + c.t * kChunk;
+  const int my_q = 32 * wave + li;
+
+  if (tid == 0) build_slot_table(st, p, c.g, c.b, c.t - p.shift);
+  Frag<T> qf[4];
+  const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s].load(q + 16 * s + 8 * hl);
+  Off off;
+  off.init(wave);
+  __syncthreads();
+
+  const int64_t kt0 = c.t - p.m > 0 ? c.t - p.m : 0;
+  const int n_sw = static_cast<int>(c.t - kt0 + 1);
+  const int n_items = n_sw + st.n;
+  float* const lse_q = kLse ? p.lse + slot_vec_offset(p, c.gbh, c.t, 0) + my_q : nullptr;
+  if (kLse) {  // invalid slots: -inf (before any copy, so the copy counts below stay exact)
+    for (int e = tid; e < p.K * kChunk; e += kThreads)
+      if (!((st.valid_mask >> (e / kChunk)) & 1u)) p.lse[slot_vec_offset(p, c.gbh, c.t, 0) + e] = -__builtin_inff();
+  }
+  auto item_tile = [&](const void* sw_base, const void* kv_base, int i) {
+    if (i < n_sw) return static_cast<const T*>(sw_base) + (row0 + (kt0 + i) * kChunk) * kDim;
+    return kv_tile<T>(kv_base, p, c.b, c.h, __builtin_amdgcn_readfirstlane(st.j[i - n_sw]));
+  };
+  off.copy(item_tile(p.k_sw, p.k, 0), Ks, wave);
+  off.copy(item_tile(p.v_sw, p.v, 0), Vs, wave);
+  barrier_copies_landed<kC>();  // K(0) landed and visible; V(0) may still be in flight
+
+  f32x16_t oacc[2] = {zero16(), zero16()};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  const float c2 = p.attn_scale * kLog2e;
+  for (int i = 0; i < n_items; ++i) {
+    const bool more = i + 1 < n_items, is_sw = i < n_sw;
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sacc[tt] = mma(off.kfrag(Ks, tt, s), qf[s], sacc[tt]);
+    }
+    barrier_lds_reads_done();  // every wave has read K(i)
+    if (more) off.copy(item_tile(p.k_sw, p.k, i + 1), Ks, wave);
+    Frag<T> pf[4];
+    float lse_v = 0.f;
+    int slot = 0;
+    if (is_sw) {
+      const int64_t kt = kt0 + i;
+      const bool lower_edge = kt == c.t - p.m, diagonal = kt == c.t;
+      if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[tt][r]);
+      mx = xor32_max(mx) * c2;
+      constexpr float kLazy = 8.f;
+      const bool grow = __ballot(mx > m_run + kLazy) != 0;
+      const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+      const bool none = m_new == -__builtin_inff();
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+      const float bias = none ? 0.f : -m_new;
+      float l = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + e], c2, bias));
+          l += x[e];
+        }
+        pf[s].set(x);
+      }
+      l_run = l_run * alpha + xor32_sum(l);
+      m_run = m_new;
+      if (grow) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+    } else {
+      slot = __builtin_amdgcn_readfirstlane(st.slot[i - n_sw]);
+      const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st.w[i - n_sw])));
+      float l;
+      const float mx = tile_softmax(sacc, c2, l);
+      lse_v = mx * p.attn_scale + __builtin_amdgcn_logf(l) * kLn2f;
+      const float f = w * __builtin_amdgcn_rcpf(l);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sacc[s >> 1][8 * (s & 1) + e] * f;
+        pf[s].set(x);
+      }
+    }
+    if (more) barrier_copies_landed<kC>();  // V(i) landed and visible (K(i + 1) may be in flight)
+    else barrier_copies_landed<0>();
+    const bool store = kLse && !is_sw;
+    if (store && hl == 0) lse_q[slot * kChunk] = lse_v;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) oacc[dt] = mma(off.vfrag(Vs, s, dt), pf[s], oacc[dt]);
+    if (is_sw && i + 1 == n_sw) {  // the window is complete: its output, normalized per query
+      const float f = __builtin_amdgcn_rcpf(l_run);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= f;
+    }
+    if (more) {
+      barrier_lds_reads_done();  // every wave has read V(i)
+      off.copy(item_tile(p.v_sw, p.v, i + 1), Vs, wave);
+      if (store) barrier_copies_landed<kC + 1>();  // K(i + 1) landed (the lse store, V(i + 1) may not)
+      else barrier_copies_landed<kC>();
+    }
+  }
+
+  T* o = static_cast<T*>(p.o) + (qrow0 + my_q) * kDim;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4(o + 32 * dt + 8 * a + 4 * hl, oacc[dt][4 * a], oacc[dt][4 * a + 1], oacc[dt][4 * a + 2],
+             oacc[dt][4 * a + 3]);
+  if (p.lse_sw && hl == 0) p.lse_sw[qrow0 + my_q] = m_run * kLn2f + __builtin_amdgcn_logf(l_run) * kLn2f;
+}
+
+// ------------------------------------------------ fused layer attention (window + GCA), backward
+// Query-major pass of the fused layer: dq = dq_window + dq_gca for one 64-query tile (two waves
+// of 32 queries, the pipeline of bwd_query_kernel: K double-buffered, V single).  The retrieved
+// slots come first, as in bwd_query_kernel: each gives e_{t,k} = <dO_t, O_{t,k}>, writes the
+// {bias, e} pairs and per-head sums of the key-major GCA pass, and adds its dQ.  Their weighted
+// sum is <dO, o_gca>, so the window's D = <dO, o_window> = <dO, o> - sum_k w_k e_k comes from the
+// stored fused output o without the window's own output.  Then the window's key tiles, as in
+// sw_bwd_query_kernel, add dS K with dS = P (dP - D).  The window's key-major pass reads the
+// {-lse_sw log2 e, D} pairs written at the end.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams p) {
+  using TL = Tile<T>;
+  using Off = TileOffsets<T, kWaves>;
+  __shared__ __align__(1024) char Ka[TL::kBytes];
+  __shared__ __align__(1024) char Kb[TL::kBytes];
+  __shared__ __align__(1024) char Vs[TL::kBytes];
+  __shared__ float dw_s[2][kMaxTopk];
+  __shared__ SlotTable st;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hl = lane >> 5;
+  const QTileCoord c = query_tile_coord(p);
+  const int64_t Lq = p.n_q * kChunk;
+  const int64_t row0 = (static_cast<int64_t>(c.b) * p.H + c.h) * Lq;
+  const int64_t qrow0 = row0 + c.t * kChunk;
+  const int my_q = 32 * wave + li;
+  const int64_t my_row = qrow0 + my_q;
+  const int64_t row = c.t - p.shift;
+
+  if (tid == 0) build_slot_table(st, p, c.g, c.b, row);
+  if (tid < 2 * kMaxTopk) dw_s[tid / kMaxTopk][tid % kMaxTopk] = 0.f;
+  Frag<T> qf[4], df[4];
+  float dd = 0.f;
+  {
+    Frag<T> of[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[s].load(static_cast<const T*>(p.q) + my_row * kDim + 16 * s + 8 * hl);
+      df[s].load(static_cast<const T*>(p.dout) + my_row * kDim + 16 * s + 8 * hl);
+      of[s].load(static_cast<const T*>(p.o) + my_row * kDim + 16 * s + 8 * hl);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dd += frag_dot(df[s], of[s]);
+  }
+  const float d_all = xor32_sum(dd);  // <dO, o> of this lane's query (fused output)
+  const float bias_sw = -p.lse_sw[my_row] * kLog2e;
+  Off off;
+  off.init(wave);
+  __syncthreads();
+
+  const int nslots = st.n;
+  if (c.h == 0 && row >= 0 && tid < p.K)
+    p.wts[((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.K + tid] = st.w_all[tid];
+  const float* lse_q = p.lse_in + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
+  f32x2_t* delta_q = reinterpret_cast<f32x2_t*>(p.delta) + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
+  const int64_t kt0 = c.t - p.m > 0 ? c.t - p.m : 0;
+  const int n_items = nslots + static_cast<int>(c.t - kt0 + 1);
+  auto item_tile = [&](const void* kv_base, const void* sw_base, int i) {
+    if (i < nslots) return kv_tile<T>(kv_base, p, c.b, c.h, __builtin_amdgcn_readfirstlane(st.j[i]));
+    return static_cast<const T*>(sw_base) + (row0 + (kt0 + (i - nslots)) * kChunk) * kDim;
+  };
+  auto slot_of = [&](int n) { return __builtin_amdgcn_readfirstlane(st.slot[n]); };
+  float lse_cur = 0.f;
+  off.copy(item_tile(p.k, p.k_sw, 0), Ka, wave);
+  off.copy(item_tile(p.v, p.v_sw, 0), Vs, wave);
+  if (nslots > 0) lse_cur = lse_q[slot_of(0) * kChunk];
+  barrier_copies_landed<0>();
+
+  f32x16_t dqacc[2] = {zero16(), zero16()};
+  float d_gca = 0.f;  // sum over the slots of w_k e_k (this lane's query)
+  const float c2 = p.attn_scale * kLog2e;
+  auto step = [&](int i, char* const Kc, char* const Kn) {
+    const bool more = i + 1 < n_items, is_gca = i < nslots;
+    float lse_nxt = 0.f;
+    if (more) {  // the other K buffer was released by the previous item's closing barrier
+      off.copy(item_tile(p.k, p.k_sw, i + 1), Kn, wave);
+      if (i + 1 < nslots) lse_nxt = lse_q[slot_of(i + 1) * kChunk];
+    }
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = zero16();
+      pacc[tt] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sacc[tt] = mma(off.kfrag(Kc, tt, s), qf[s], sacc[tt]);
+        pacc[tt] = mma(off.kfrag(Vs, tt, s), df[s], pacc[tt]);
+      }
+    }
+    barrier_lds_reads_done();  // every wave has read V(i)
+    if (more) off.copy(item_tile(p.v, p.v_sw, i + 1), Vs, wave);
+    Frag<T> zf[4];
+    if (is_gca) {
+      // P = exp(z - lse); e = sum_u P dP' = <dO, O_slot>; dz = w P (dP' - e)
+      const int slot = slot_of(i);
+      const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st.w[i])));
+      const float bias = -lse_cur * kLog2e;
+      float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[0][r] = fast_exp2(__builtin_fmaf(sacc[0][r], c2, bias));
+        sacc[1][r] = fast_exp2(__builtin_fmaf(sacc[1][r], c2, bias));
+        e0 = __builtin_fmaf(sacc[0][r], pacc[0][r], e0);
+        e1 = __builtin_fmaf(sacc[1][r], pacc[1][r], e1);
+      }
+      const float e = xor32_sum(e0 + e1);
+      d_gca = __builtin_fmaf(w, e, d_gca);
+      if (hl == 0) delta_q[slot * kChunk] = f32x2_t{__builtin_amdgcn_logf(w) + bias, e};
+      const float es = sum_queries32(e);
+      if (lane == 0) dw_s[wave][slot] = es;
+      const float we = -w * e;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) {
+          const int tt = s >> 1, r = 8 * (s & 1) + ee;
+          x[ee] = sacc[tt][r] * __builtin_fmaf(w, pacc[tt][r], we);
+        }
+        zf[s].set(x);
+      }
+    } else {
+      // the window's key tile kt: P = exp(z - lse_sw), dS = P (dP - D), masked on the edge tiles
+      const int64_t kt = kt0 + (i - nslots);
+      const bool lower_edge = kt == c.t - p.m, diagonal = kt == c.t;
+      if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+      const float d_sw = d_all - d_gca;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float x[8];
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) {
+          const int tt = s >> 1, r = 8 * (s & 1) + ee;
+          const float pw = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias_sw));
+          x[ee] = pw * (pacc[tt][r] - d_sw);
+        }
+        zf[s].set(x);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dqacc[dt] = mma(off.vfrag(Kc, s, dt), zf[s], dqacc[dt]);
+    lse_cur = lse_nxt;
+    // K(i + 1), its lse and V(i + 1) landed (a slot's delta store may not have); every wave has
+    // also read K(i), whose buffer the next item refills
+    if (more) {
+      if (is_gca) barrier_copies_landed_reads_done<1>();
+      else barrier_copies_landed_reads_done<0>();
+    }
+  };
+  for (int i = 0; i < n_items; i += 2) {
+    step(i, Ka, Kb);
+    if (i + 1 < n_items) step(i + 1, Kb, Ka);
+  }
+
+  T* dq = static_cast<T*>(p.dq) + my_row * kDim;
+  const float sc = p.attn_scale;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4(dq + 32 * dt + 8 * a + 4 * hl, sc * dqacc[dt][4 * a], sc * dqacc[dt][4 * a + 1],
+             sc * dqacc[dt][4 * a + 2], sc * dqacc[dt][4 * a + 3]);
+  if (hl == 0) reinterpret_cast<f32x2_t*>(p.sw_stats)[my_row] = f32x2_t{bias_sw, d_all - d_gca};
+  __syncthreads();
+  if (row >= 0 && tid < p.K) {
+    const int64_t o = (((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.H + c.h) * p.K + tid;
+    p.dw_part[o] = dw_s[0][tid] + dw_s[1][tid];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
@@ -1745,6 +2293,25 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s) {
     if (p.lse) hipLaunchKernelGGL((attend_fwd_wave_kernel<true>), grid, dim3(64), 0, s, p);
     else hipLaunchKernelGGL((attend_fwd_wave_kernel<false>), grid, dim3(64), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_fwd(const AttendParams& p, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.H * p.n_q));
+  if (f32) {
+    if (p.lse) hipLaunchKernelGGL((fused_fwd2_kernel<float, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((fused_fwd2_kernel<float, false>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (p.lse) hipLaunchKernelGGL((fused_fwd_kernel<true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((fused_fwd_kernel<false>), grid, dim3(64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_bwd_query(const AttendParams& p, bool f32, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.G) * p.B * p.H * p.n_q));
+  if (f32) hipLaunchKernelGGL(fused_bwd_query_kernel<float>, grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(fused_bwd_query_kernel<bf16_t>, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

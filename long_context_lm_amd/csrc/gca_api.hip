@@ -16,7 +16,7 @@ const char* kernel_name(int id) {
   static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
                                            "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd",
-                                           "sw_bwd_query", "sw_bwd_key"};
+                                           "sw_bwd_query", "sw_bwd_key", "fused_fwd", "fused_bwd_query"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -227,6 +227,10 @@ gca_status gca_workspace_size(int op, const gca_problem* problem, size_t* bytes)
     case GCA_OP_LANDMARK_BACKWARD: *bytes = plan_landmark(problem).total; return GCA_OK;
     case GCA_OP_SW_BACKWARD:
       *bytes = align_up(static_cast<size_t>(problem->B) * problem->H * problem->n_q_chunks * 64 * 8);
+      return GCA_OK;
+    case GCA_OP_FUSED_BACKWARD:
+      *bytes = plan_backward(problem).total +
+               align_up(static_cast<size_t>(problem->B) * problem->H * problem->n_q_chunks * 64 * 8);
       return GCA_OK;
     default: return GCA_ERR_INVALID_ARGUMENT;
   }
@@ -569,6 +573,118 @@ gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const voi
   const bool f32 = problem->dtype == GCA_F32;
   GCA_TRY(launch(kSwBwdQuery, s, [&] { return launch_sw_bwd_query(w, f32, s); }));
   return launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(w, f32, s); });
+}
+
+// Fused layer attention: one retrieval group, window W = 64 m over the layer's own keys.
+static gca_status fused_check(const gca_problem* p, int32_t window) {
+  GCA_TRY(validate_problem(p));
+  if (p->G != 1) return GCA_ERR_INVALID_ARGUMENT;
+  if (window < 64 || window % 64 != 0) return GCA_ERR_INVALID_ARGUMENT;
+  return GCA_OK;
+}
+
+gca_status gca_fused_forward(const gca_problem* problem, int32_t window, const void* q, const void* k_sw,
+                             const void* v_sw, const void* k, const void* v, const int32_t* idx, const float* score,
+                             void* o, float* lse_sw, float* lse, void* stream) {
+  GCA_TRY(fused_check(problem, window));
+  const gca_problem* p = problem;
+  const bool any = p->n_q_chunks > 0;
+  const bool kv = any && p->n_kv_chunks > 0;
+  for (const void* t : {q, k_sw, v_sw, static_cast<const void*>(o)}) GCA_TRY(check_tensor(t, any, 16));
+  GCA_TRY(check_tensor(k, kv, 16));
+  GCA_TRY(check_tensor(v, kv, 16));
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(score, any, 4));
+  if (lse_sw != nullptr) GCA_TRY(check_tensor(lse_sw, any, 4));
+  if (lse != nullptr) GCA_TRY(check_tensor(lse, any, 16));
+  if (!any) return GCA_OK;
+  AttendParams a = attend_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_sw = k_sw;
+  a.v_sw = v_sw;
+  a.idx = idx;
+  a.score = score;
+  a.o = o;
+  a.lse = lse;
+  a.lse_sw = lse_sw;
+  a.m = window / 64;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = p->dtype == GCA_F32;
+  return launch(kFusedFwd, s, [&] { return launch_fused_fwd(a, f32, s); });
+}
+
+gca_status gca_fused_backward(const gca_problem* problem, int32_t window, const void* q, const void* k_sw,
+                              const void* v_sw, const void* k, const void* v, const int32_t* idx,
+                              const float* score, const void* o, const float* lse_sw, const float* lse,
+                              const void* dout, void* dq, void* dk_sw, void* dv_sw, void* dk, void* dv,
+                              float* dscore, void* ws, size_t ws_bytes, void* stream) {
+  GCA_TRY(fused_check(problem, window));
+  const gca_problem* p = problem;
+  const bool any = p->n_q_chunks > 0;
+  const bool kv = p->n_kv_chunks > 0;
+  for (const void* t : {q, k_sw, v_sw, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk_sw),
+                        static_cast<const void*>(dv_sw)})
+    GCA_TRY(check_tensor(t, any, 16));
+  GCA_TRY(check_tensor(k, kv, 16));
+  GCA_TRY(check_tensor(v, kv, 16));
+  GCA_TRY(check_tensor(dk, kv, 16));
+  GCA_TRY(check_tensor(dv, kv, 16));
+  GCA_TRY(check_tensor(idx, any, 4));
+  GCA_TRY(check_tensor(score, any, 4));
+  GCA_TRY(check_tensor(dscore, any, 4));
+  GCA_TRY(check_tensor(lse_sw, any, 4));
+  GCA_TRY(check_tensor(lse, any, 16));
+  const BackwardLayout L = plan_backward(p);
+  size_t need = 0;
+  GCA_TRY(gca_workspace_size(GCA_OP_FUSED_BACKWARD, p, &need));
+  GCA_TRY(check_ws(need, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!any && !kv) return GCA_OK;
+
+  char* w = static_cast<char*>(ws);
+  AttendParams a = attend_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_sw = k_sw;
+  a.v_sw = v_sw;
+  a.idx = idx;
+  a.score = score;
+  a.o = const_cast<void*>(o);
+  a.lse_in = lse;
+  a.lse_sw = const_cast<float*>(lse_sw);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dscore = dscore;
+  a.m = window / 64;
+  a.delta = reinterpret_cast<float*>(w + L.delta);
+  a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
+  a.wts = reinterpret_cast<float*>(w + L.wts);
+  a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
+  a.counts = reinterpret_cast<int32_t*>(w + L.counts);
+  a.sw_stats = reinterpret_cast<float*>(w + L.total);
+  a.entry_decoded = 1;
+  const bool f32 = p->dtype == GCA_F32;
+  if (any) {
+    GCA_TRY(launch(kFusedBwdQuery, s, [&] { return launch_fused_bwd_query(a, f32, s); }));
+    SwParams sw = sw_params(p, window);
+    sw.q = q;
+    sw.k = k_sw;
+    sw.v = v_sw;
+    sw.dout = dout;
+    sw.dk = dk_sw;
+    sw.dv = dv_sw;
+    sw.stats = a.sw_stats;
+    GCA_TRY(launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(sw, f32, s); }));
+  }
+  if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
+  if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
+  if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
+  return GCA_OK;
 }
 
 // The device address of a K/V source: device memory as it is; pinned host memory (hipHostMalloc)

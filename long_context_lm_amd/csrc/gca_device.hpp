@@ -190,6 +190,17 @@ __device__ __forceinline__ void copy16_async_untracked(const void* gbase, uint32
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(gbase), "{m0}"(lds_addr) : "memory");
 }
 
+// The same copy with the LDS destination given as its 32-bit LDS address (see lds_address):
+// no generic-pointer round trip, whose null check the backend cannot always fold.
+__device__ __forceinline__ void copy16_async_untracked_at(const void* gbase, uint32_t lane_off, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(gbase), "{m0}"(lds_addr) : "memory");
+}
+
+// 32-bit LDS address of a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const char* lds) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(lds)));
+}
+
 // Start copying one 64x64 tile (global row stride 64 elements) into swizzled LDS.  All threads of
 // a workgroup of kWaves waves call it; each wave issues its share of the 1 KiB wave copies.  The
 // data is usable after wait_async_copies() and a workgroup barrier.

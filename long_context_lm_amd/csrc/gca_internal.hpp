@@ -22,6 +22,8 @@ enum KernelId {
   kSwFwd,
   kSwBwdQuery,
   kSwBwdKey,
+  kFusedFwd,
+  kFusedBwdQuery,
   kNumKernels
 };
 const char* kernel_name(int id);
@@ -68,6 +70,12 @@ struct AttendParams {
   int64_t n_q, n_kv, q_base;
   int32_t G, B, H, K, shift;
   int32_t pair_cap;     // G * n_q: most retrievals one key chunk can receive
+  // fused layer attention (sliding window + GCA over the same queries, G = 1); unused otherwise
+  const void* k_sw;     // [B, H, n_q * 64, 64] the window's keys and values
+  const void* v_sw;
+  float* lse_sw;        // forward output / backward input [B, H, n_q * 64] (may be null in the forward)
+  float* sw_stats;      // backward: [B, H, n_q * 64, 2] {-lse_sw log2 e, D_sw} for the window's key pass
+  int32_t m;            // window in chunks (W = 64 m); 0 = no window
   int32_t entry_decoded;  // inverse index entries for the key-major pass (see pairs)
   int32_t causal_rows;  // inverse index: 1 = list only rows whose global chunk lies after the key
                         // chunk (the landmark gradients' rule j < q_base + row); 0 = every row
@@ -138,5 +146,7 @@ hipError_t launch_decode_tokens(const AttendParams& p, int32_t n_tok, bool f32, 
 hipError_t launch_sw_fwd(const SwParams& p, bool f32, hipStream_t s);
 hipError_t launch_sw_bwd_query(const SwParams& p, bool f32, hipStream_t s);
 hipError_t launch_sw_bwd_key(const SwParams& p, bool f32, hipStream_t s);
+hipError_t launch_fused_fwd(const AttendParams& p, bool f32, hipStream_t s);
+hipError_t launch_fused_bwd_query(const AttendParams& p, bool f32, hipStream_t s);
 
 }  // namespace gca

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgca.so")
 
 GCA_OK = 0
-OP_RETRIEVE, OP_FORWARD, OP_BACKWARD, OP_LANDMARK_BACKWARD, OP_SW_BACKWARD = 0, 1, 2, 3, 4
+OP_RETRIEVE, OP_FORWARD, OP_BACKWARD, OP_LANDMARK_BACKWARD, OP_SW_BACKWARD, OP_FUSED_BACKWARD = 0, 1, 2, 3, 4, 5
 DTYPES = {"bf16": 0, "f32": 1}
 
 
@@ -61,6 +61,8 @@ EXPORTS = (
     "gca_decode_tokens",
     "gca_sw_forward",
     "gca_sw_backward",
+    "gca_fused_forward",
+    "gca_fused_backward",
 )
 
 _lib = None
@@ -95,7 +97,10 @@ def load() -> ctypes.CDLL:
     lib.gca_decode_tokens.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
     lib.gca_sw_forward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     lib.gca_sw_backward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("gca_workspace_size", "gca_retrieve", "gca_retrieve_static", "gca_forward", "gca_backward", "gca_landmark_backward",
+    lib.gca_fused_forward.argtypes = [P, ctypes.c_int32] + [vp] * 10 + [vp]
+    lib.gca_fused_backward.argtypes = [P, ctypes.c_int32] + [vp] * 18 + [sz, vp]
+    for f in ("gca_fused_forward", "gca_fused_backward", "gca_workspace_size", "gca_retrieve", "gca_retrieve_static",
+              "gca_forward", "gca_backward", "gca_landmark_backward",
               "gca_profile_enable", "gca_profile_collect"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gca_status_string.argtypes = [ctypes.c_int]
@@ -402,6 +407,70 @@ def sw_backward(cfg: Config, q, k, v, o, lse, dout, window: int = 512, ws=None, 
                                                      _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                                      _ptr(ws), n, _stream()))
     return dq, dk, dv
+
+
+def fused_forward(cfg: Config, q, k_sw, v_sw, k, v, idx, score, window: int = 512, need_lse: bool = True,
+                  o=None, lse_sw=None, lse=None):
+    """gca_fused_forward (G = 1): o = SW(q, k_sw, v_sw; window) + GCA(q, k, v, idx, score).
+    q, k_sw, v_sw [B,H,L,64]; k, v [B,H,n_kv*64,64]; returns (o like q, lse_sw [B,H,L] or None,
+    lse [1,B,H,n_q,K,64] or None)."""
+    import torch
+
+    dev, ft = q.device, _torch_dtype(cfg)
+    if cfg.G != 1:
+        raise ValueError("the fused layer attention has one retrieval group (G = 1)")
+    seq = (cfg.B, cfg.H, cfg.n_q * 64, 64)
+    o = torch.empty_like(q) if o is None else o
+    if need_lse:
+        lse_sw = torch.empty(seq[:-1], dtype=torch.float32, device=dev) if lse_sw is None else lse_sw
+        lse = torch.empty(cfg.shape("lse"), dtype=torch.float32, device=dev) if lse is None else lse
+    for name, t in (("q", q), ("k_sw", k_sw), ("v_sw", v_sw), ("o", o)):
+        _expect(name, t, seq, ft, dev)
+    _expect("k", k, cfg.shape("kv"), ft, dev)
+    _expect("v", v, cfg.shape("kv"), ft, dev)
+    _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
+    _expect("score", score, cfg.shape("sel"), torch.float32, dev)
+    if need_lse:
+        _expect("lse_sw", lse_sw, seq[:-1], torch.float32, dev)
+        _expect("lse", lse, cfg.shape("lse"), torch.float32, dev)
+    prob = cfg.problem()
+    _check("gca_fused_forward", load().gca_fused_forward(
+        ctypes.byref(prob), int(window), _ptr(q), _ptr(k_sw), _ptr(v_sw), _ptr(k), _ptr(v), _ptr(idx), _ptr(score),
+        _ptr(o), _ptr(lse_sw) if need_lse else None, _ptr(lse) if need_lse else None, _stream()))
+    return o, (lse_sw if need_lse else None), (lse if need_lse else None)
+
+
+def fused_backward(cfg: Config, q, k_sw, v_sw, k, v, idx, score, o, lse_sw, lse, dout, window: int = 512,
+                   ws=None, out=None):
+    """gca_fused_backward: returns (dq, dk_sw, dv_sw, dk, dv, dscore)."""
+    import torch
+
+    dev, ft = q.device, _torch_dtype(cfg)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k_sw), torch.empty_like(v_sw), torch.empty_like(k),
+               torch.empty_like(v), torch.empty(idx.shape, dtype=torch.float32, device=dev))
+    dq, dk_sw, dv_sw, dk, dv, dscore = out
+    seq = (cfg.B, cfg.H, cfg.n_q * 64, 64)
+    for name, t in (("q", q), ("k_sw", k_sw), ("v_sw", v_sw), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk_sw", dk_sw), ("dv_sw", dv_sw)):
+        _expect(name, t, seq, ft, dev)
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _expect(name, t, cfg.shape("kv"), ft, dev)
+    _expect("idx", idx, cfg.shape("sel"), torch.int32, dev)
+    _expect("score", score, cfg.shape("sel"), torch.float32, dev)
+    _expect("dscore", dscore, cfg.shape("sel"), torch.float32, dev)
+    _expect("lse_sw", lse_sw, seq[:-1], torch.float32, dev)
+    _expect("lse", lse, cfg.shape("lse"), torch.float32, dev)
+    if ws is None:
+        ws, n = _workspace(OP_FUSED_BACKWARD, cfg, dev)
+    else:
+        n = _ws_bytes(ws, dev)
+    prob = cfg.problem()
+    _check("gca_fused_backward", load().gca_fused_backward(
+        ctypes.byref(prob), int(window), _ptr(q), _ptr(k_sw), _ptr(v_sw), _ptr(k), _ptr(v), _ptr(idx), _ptr(score),
+        _ptr(o), _ptr(lse_sw), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_sw), _ptr(dv_sw), _ptr(dk), _ptr(dv),
+        _ptr(dscore), _ptr(ws), n, _stream()))
+    return dq, dk_sw, dv_sw, dk, dv, dscore
 
 
 def fetched_config(cfg: Config) -> Config:

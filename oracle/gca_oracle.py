@@ -29,6 +29,7 @@ What is computed (all arithmetic in IEEE float64 unless a step says float32):
     (decode_tokens)                                same
   * sliding-window self-attention, W = 512, beside the retrieval
     (sw_attention, sw_attention_backward)          [Notes, Loss / training strategy]
+  * the layer's two attentions summed (fused_attention, fused_attention_backward)     same
 
 Readings taken where the pages leave a step open (each is listed in the design doc):
   R1  score s_ij = fl32(fl32(sum_d lq[i,d]*lk[j,d]) * score_scale) + 0.0f, the sum taken in
@@ -48,6 +49,8 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
   R9  decoding the first n tokens of a chunk gives the chunk forward's first n rows.
   R10 the sliding window of token i is tokens max(0, i - W + 1) .. i (causal, itself included),
       one softmax of attn_scale <q, k>, no positional bias.
+  R11 in a layer that runs both, the window and GCA (one retrieval group) read the same queries
+      and their outputs are summed.
 
 Parity pins: every function here is pinned in tests/test_oracle_pins.py against brute force,
 library routines, closed forms, invariants and finite differences.
@@ -462,3 +465,23 @@ def sw_attention_backward(q, k, v, dout, window, *, attn_scale=0.125):
         dk[:, :, lo:i + 1] += attn_scale * dS[..., None] * q[:, :, i][:, :, None, :]
         dv[:, :, lo:i + 1] += P[..., None] * dout[:, :, i][:, :, None, :]
     return dq, dk, dv
+
+
+def fused_attention(q, k_sw, v_sw, k, v, idx, score, window, *, shift=1, attn_scale=0.125):
+    """A layer's local window and GCA summed (reading R11): the layers that run GCA also run
+    sliding-window self-attention beside the retrieval [Notes, Loss / training strategy].
+      o = sw_attention(q, k_sw, v_sw, window) + forward(q, k, v, idx, score) (one group)
+    q, k_sw, v_sw [B, H, L, d]; k, v [B, H, n_kv*64, d]; idx, score [1, B, n_q, K].
+    Returns o [B, H, L, d], the window's lse [B, H, L] and the GCA lse [1, B, H, L, K] (float64)."""
+    o_sw, lse_sw = sw_attention(q, k_sw, v_sw, window, attn_scale=attn_scale)
+    o_g, lse = forward(np.asarray(q)[None], k, v, idx, score, shift=shift, attn_scale=attn_scale)
+    return o_sw + o_g[0], lse_sw, lse
+
+
+def fused_attention_backward(q, k_sw, v_sw, k, v, idx, score, dout, window, *, shift=1, attn_scale=0.125):
+    """Gradients of sum(dout * fused_attention(...)): the gradient of a sum of the two maps.
+    Returns dq (both parts), dk_sw, dv_sw (the window's), dk, dv, dscore (GCA's), float64."""
+    dq_sw, dk_sw, dv_sw = sw_attention_backward(q, k_sw, v_sw, dout, window, attn_scale=attn_scale)
+    dq_g, dk, dv, dscore = backward(np.asarray(q)[None], k, v, idx, score, np.asarray(dout)[None], shift=shift,
+                                    attn_scale=attn_scale)
+    return dq_sw + dq_g[0], dk_sw, dv_sw, dk, dv, dscore

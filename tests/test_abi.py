@@ -99,7 +99,7 @@ def test_null_problem_and_bad_op():
     n = ctypes.c_size_t(0)
     assert lib.gca_workspace_size(0, None, ctypes.byref(n)) == INVALID
     p = good()
-    assert lib.gca_workspace_size(5, ctypes.byref(p), ctypes.byref(n)) == INVALID
+    assert lib.gca_workspace_size(6, ctypes.byref(p), ctypes.byref(n)) == INVALID
     assert lib.gca_workspace_size(-1, ctypes.byref(p), ctypes.byref(n)) == INVALID
     assert lib.gca_workspace_size(0, ctypes.byref(p), None) == INVALID
     assert lib.gca_retrieve(None, None, None, None, None, None, 0, None) == INVALID
@@ -197,6 +197,26 @@ def test_pointer_checks():
                                None) == MISALIGNED
     assert lib.gca_sw_backward(ctypes.byref(sw), 512, *([z] * 6), None, z, z, z, need, None) == INVALID
     assert lib.gca_sw_backward(ctypes.byref(sw), 96, *args, z, need, None) == INVALID
+    # fused layer attention: one group, a window that is a positive multiple of 64; its backward's
+    # workspace is the GCA backward's plus 8 bytes per query token
+    fz = good(G=1)
+    assert lib.gca_fused_forward(ctypes.byref(good(G=2)), 512, *([z] * 10), None) == INVALID
+    for window in (0, 32, 100):
+        assert lib.gca_fused_forward(ctypes.byref(fz), window, *([z] * 10), None) == INVALID
+    assert lib.gca_fused_forward(ctypes.byref(fz), 512, mis, *([z] * 9), None) == MISALIGNED
+    assert lib.gca_fused_forward(ctypes.byref(fz), 512, *([z] * 7), None, None, None, None) == INVALID  # no o
+    assert lib.gca_fused_forward(ctypes.byref(good(G=1, n_q_chunks=0)), 512, *([None] * 10), None) == OK
+    st_f, need_f = ws_size(fz, 5)
+    st_b, need_b = ws_size(fz, 2)
+    assert st_f == OK and st_b == OK and need_f == need_b + 2 * 3 * 8 * 64 * 8
+    fargs = [z] * 18
+    assert lib.gca_fused_backward(ctypes.byref(fz), 512, *fargs, need_f - 1, None) == WS_SMALL
+    assert lib.gca_fused_backward(ctypes.byref(fz), 512, *fargs[:17], None, need_f, None) == INVALID
+    assert lib.gca_fused_backward(ctypes.byref(fz), 96, *fargs, need_f, None) == INVALID
+    assert lib.gca_fused_backward(ctypes.byref(fz), 512, *fargs[:8], ctypes.c_void_p(FAKE + 2), *fargs[9:], need_f,
+                                  None) == MISALIGNED  # lse_sw: 4-byte alignment
+    assert lib.gca_fused_backward(ctypes.byref(fz), 512, *fargs[:9], ctypes.c_void_p(FAKE + 4), *fargs[10:], need_f,
+                                  None) == MISALIGNED  # the GCA lse: 16-byte alignment
     # backward beyond the int32 range of inverse-index codes (G * n_q * K >= 2^31)
     big = good(n_q_chunks=1 << 28, n_kv_chunks=1025, H=1, B=1)
     assert lib.gca_backward(ctypes.byref(big), z, z, z, z, z, z, z, z, z, z, z, z, 1 << 40, None) == UNSUPPORTED

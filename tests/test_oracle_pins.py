@@ -622,3 +622,37 @@ def test_sw_attention_backward_finite_difference():
             dn = (O.sw_attention(q, k, v, W, attn_scale=0.5)[0] * do).sum()
             arr[idx] = old
             assert abs((up - dn) / (2 * eps) - grad[idx]) < 1e-6
+
+
+# ----------------------------------------------------------- fused layer attention (window + GCA)
+def test_fused_attention_matches_autograd_of_independent_expression():
+    """The layer's window and GCA summed, against torch: band-masked sdpa plus the independent GCA
+    re-expression, forward and all six gradients by autograd."""
+    shp, x, idx, sc = _small_case(seed=11, G=1, B=1, H=2, n=6, K=3)
+    rng = np.random.default_rng(11)
+    k_sw = rng.standard_normal(x["k"].shape)
+    v_sw = rng.standard_normal(x["v"].shape)
+    dout = rng.standard_normal(x["q"].shape[1:])
+    window = 100
+    q0 = x["q"][0]
+    o, lse_sw, lse = O.fused_attention(q0, k_sw, v_sw, x["k"], x["v"], idx, sc, window)
+    t = {n: torch.tensor(a, requires_grad=True) for n, a in
+         (("q", q0), ("k_sw", k_sw), ("v_sw", v_sw), ("k", x["k"]), ("v", x["v"]))}
+    s_t = torch.tensor(sc.astype(np.float64), requires_grad=True)
+    L = q0.shape[-2]
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    o_sw = torch.nn.functional.scaled_dot_product_attention(t["q"], t["k_sw"], t["v_sw"],
+                                                            attn_mask=(j <= i) & (j > i - window), scale=0.125)
+    out = o_sw + _torch_gca(t["q"][None], t["k"], t["v"], idx, s_t, 1, 0.125)[0]
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-11, atol=1e-12)
+    out.backward(torch.from_numpy(dout))
+    grads = O.fused_attention_backward(q0, k_sw, v_sw, x["k"], x["v"], idx, sc, dout, window)
+    for name, got, ref in zip(("dq", "dk_sw", "dv_sw", "dk", "dv"), grads[:5],
+                              (t["q"].grad, t["k_sw"].grad, t["v_sw"].grad, t["k"].grad, t["v"].grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+    np.testing.assert_allclose(grads[5], np.where(idx >= 0, s_t.grad.numpy(), 0.0), rtol=1e-9, atol=1e-11)
+    # the window's log-sum-exp against a direct logsumexp over its band
+    z = 0.125 * torch.from_numpy(q0) @ torch.from_numpy(k_sw).transpose(-1, -2)
+    ref_lse = torch.logsumexp(z.masked_fill(~((j <= i) & (j > i - window)), float("-inf")), dim=-1)
+    np.testing.assert_allclose(lse_sw, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
