@@ -31,7 +31,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/attend.hip", "csrc/retrieve.hip", "csrc/gca_device.hpp", "csrc/gca_internal.hpp"]
 SHORT = ["score_topk", "topk_merge", "attend_fwd", "inverse_index", "bwd_query", "bwd_key", "score_grad",
          "lmk_query_grad", "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd", "sw_bwd_query",
-         "sw_bwd_key"]
+         "sw_bwd_key", "fused_fwd", "fused_bwd_query"]
 COPY_BYTES = 1 << 30
 
 
@@ -44,10 +44,10 @@ def source_hash() -> str:
 
 
 def short_name(kernel: str):
-    # whole kernel names (with an optional variant suffix, e.g. attend_fwd_wave_kernel) only:
-    # "bwd_query" must not match sw_bwd_query_kernel
+    # whole kernel names (with an optional variant suffix, e.g. attend_fwd_wave_kernel or the
+    # two-wave fused_fwd2_kernel) only: "bwd_query" must not match sw_bwd_query_kernel
     for s in SHORT:
-        if re.search(r"(?<![A-Za-z0-9_])" + s + r"(_[a-z]+)?_kernel\b", kernel):
+        if re.search(r"(?<![A-Za-z0-9_])" + s + r"[0-9]?(_[a-z]+)?_kernel\b", kernel):
             return s
     if "copy" in kernel.lower() or "elementwise" in kernel.lower():
         return "copy"
