@@ -1082,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
   if (c.h == 0 && row >= 0 && tid < p.K)
     p.wts[((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.K + tid] = st.w_all[tid];
   const float* lse_q = p.lse_in + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
-  f32x2_t* delta_q = reinterpret_cast<f32x2_t*>(p.delta) + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
+  float* delta_q = p.delta + 2 * slot_vec_offset(p, c.gbh, c.t, 0) + 64 * hl + my_q;
   auto chunk_of = [&](int n) { return __builtin_amdgcn_readfirstlane(st.j[n]); };
   auto slot_of = [&](int n) { return __builtin_amdgcn_readfirstlane(st.slot[n]); };
   float lse_cur = 0.f;
@@ -1132,7 +1132,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     }
     const float e = xor32_sum(e0 + e1);
     // for the key-major pass: P_w = exp2(z log2e + bias) with bias = log2 w - lse log2 e, and e
-    if (hl == 0) delta_q[slot * kChunk] = f32x2_t{__builtin_amdgcn_logf(w) + bias, e};
+    delta_q[2 * slot * kChunk] = hl ? -e : __builtin_amdgcn_logf(w) + bias;
     const float es = sum_queries32(e);
     if (lane == 0) dw_s[wave][slot] = es;
     const float we = -w * e;
@@ -1449,6 +1449,22 @@ __device__ __forceinline__ PairRef decode_pair(const i32x2_t ent) {
   return r;
 }
 
+// Work item of a key-major workgroup.  A key chunk's list is longer the earlier the chunk (causal
+// retrieval offers chunk j to every later row), so (batch row, head) blocks are taken two at a
+// time and walked chunk-major within the pair: both blocks' long lists start before either
+// block's short ones, and the last block on each XCD does not leave its longest lists to run
+// alone at the end of the launch.  An odd last block runs by itself.
+__device__ __forceinline__ void key_item(int64_t lid, int64_t n_kv, int64_t n_bh, int64_t& bh, int64_t& j) {
+  const int64_t pair = lid / (2 * n_kv), r = lid - pair * 2 * n_kv;
+  if (2 * pair + 1 < n_bh) {
+    bh = 2 * pair + (r & 1);
+    j = r >> 1;
+  } else {
+    bh = 2 * pair;
+    j = r;
+  }
+}
+
 // One workgroup of two waves per (batch row, head, key chunk); each wave owns 32 of its keys and
 // walks the chunk's retrievals, double-buffered: the next entry's Q and dO tiles and its 64
 // {bias, e} pairs are copied in at the start of the current one.
@@ -1464,9 +1480,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t j = lid % p.n_kv;
-  const int64_t bh = lid / p.n_kv;
+  int64_t bh, j;
+  key_item(xcd_logical_block(blockIdx.x, gridDim.x), p.n_kv, static_cast<int64_t>(p.B) * p.H, bh, j);
   const int h = static_cast<int>(bh % p.H);
   const int b = static_cast<int>(bh / p.H);
   const int my_u = 32 * wave + li;
@@ -1498,9 +1513,11 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     const int64_t qrow0 = gbh * Lq + r.t * kChunk;
     off.copy(static_cast<const T*>(p.q) + qrow0 * kDim, buf, wave);
     off.copy(static_cast<const T*>(p.dout) + qrow0 * kDim, buf + TL::kBytes, wave);
-    // wave w copies the pairs of queries 32 w .. 32 w + 31 (16 bytes per lane, lanes < 16)
-    const float* src = p.delta + 2 * (slot_vec_offset(p, gbh, r.t, r.slot) + 32 * wave);
-    if (lane < 16) copy16_async_untracked(src, 16u * lane, buf + 2 * TL::kBytes + 256 * wave);
+    // wave w copies the biases and the -e of queries 32 w .. 32 w + 31 (16 bytes per lane,
+    // lanes < 16): lanes 0-7 the biases, lanes 8-15 the -e, to [32 biases, 32 -e] at 256 w
+    const float* src = p.delta + 2 * slot_vec_offset(p, gbh, r.t, r.slot) + 32 * wave;
+    if (lane < 16)
+      copy16_async_untracked(src, 256u * (lane >> 3) + 16u * (lane & 7), buf + 2 * TL::kBytes + 256 * wave);
   };
 
   int32_t n = 0;  // entries in the current round
@@ -1508,26 +1525,29 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     if (pr + 1 < n) fill(ents[pr + 1], nxt);
     const char* Qs = cur;
     const char* Ds = cur + TL::kBytes;
-    const f32x4_t* vec = reinterpret_cast<const f32x4_t*>(cur + 2 * TL::kBytes);  // {b, e, b, e}
+    // [32 biases, 32 -e] of queries 0-31, then of queries 32-63
+    const float* vec = reinterpret_cast<const float*>(cur + 2 * TL::kBytes);
     // Both 32-query tiles' scores first, then each tile's elementwise work beside the other
     // tile's matrix-core work (the second tile's S and dP' products run beside the first tile's
     // exp and dz, the first tile's dK and dV products beside the second tile's).  Every row
     // fragment of the entry is read before the first product, so the products wait once for the
     // LDS reads instead of once per product.
+    // The dP' products start from -e of their queries, so they leave dP' - e.
     Frag<T> qr[2][4], dr[2][4];
+    f32x16_t sacc[2], pacc[2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         qr[qt][s] = off.kfrag(Qs, qt, s);
         dr[qt][s] = off.kfrag(Ds, qt, s);
       }
+      pacc[qt] = *reinterpret_cast<const f32x16_t*>(vec + 64 * qt + 32 + 16 * hl);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-    f32x16_t sacc[2], pacc[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       sacc[qt] = zero16();
-      pacc[qt] = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         sacc[qt] = mma(qr[qt][s], kf[s], sacc[qt]);
@@ -1540,18 +1560,15 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
       Frag<T> pf[2], zf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int q0 = 32 * qt + 16 * hl + 8 * half;
-        f32x4_t be[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) be[i] = vec[q0 / 2 + i];
+        const f32x4_t* bq = reinterpret_cast<const f32x4_t*>(vec + 64 * qt + 16 * hl + 8 * half);
+        const f32x4_t b0 = bq[0], b1 = bq[1];
         float xp[8], xz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const float bias_q = be[e >> 1][2 * (e & 1)], e_q = be[e >> 1][2 * (e & 1) + 1];
-          const float pw = fast_exp2(__builtin_fmaf(sacc[qt][r], c2, bias_q));
+          const float pw = fast_exp2(__builtin_fmaf(sacc[qt][r], c2, e < 4 ? b0[e] : b1[e - 4]));
           xp[e] = pw;
-          xz[e] = pw * (pacc[qt][r] - e_q);
+          xz[e] = pw * pacc[qt][r];
         }
         pf[half].set(xp);
         zf[half].set(xz);
@@ -2154,7 +2171,7 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
   if (c.h == 0 && row >= 0 && tid < p.K)
     p.wts[((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.K + tid] = st.w_all[tid];
   const float* lse_q = p.lse_in + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
-  f32x2_t* delta_q = reinterpret_cast<f32x2_t*>(p.delta) + slot_vec_offset(p, c.gbh, c.t, 0) + my_q;
+  float* delta_q = p.delta + 2 * slot_vec_offset(p, c.gbh, c.t, 0) + 64 * hl + my_q;
   const int64_t kt0 = c.t - p.m > 0 ? c.t - p.m : 0;
   const int n_items = nslots + static_cast<int>(c.t - kt0 + 1);
   auto item_tile = [&](const void* kv_base, const void* sw_base, int i) {
@@ -2207,7 +2224,7 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
       }
       const float e = xor32_sum(e0 + e1);
       d_gca = __builtin_fmaf(w, e, d_gca);
-      if (hl == 0) delta_q[slot * kChunk] = f32x2_t{__builtin_amdgcn_logf(w) + bias, e};
+      delta_q[2 * slot * kChunk] = hl ? -e : __builtin_amdgcn_logf(w) + bias;
       const float es = sum_queries32(e);
       if (lane == 0) dw_s[wave][slot] = es;
       const float we = -w * e;

@@ -160,7 +160,7 @@ BackwardLayout plan_backward(const gca_problem* p) {
   const size_t nq = static_cast<size_t>(p->n_q_chunks), nkv = static_cast<size_t>(p->n_kv_chunks);
   size_t off = 0;
   l.delta = off;
-  off += align_up(G * B * H * nq * 64 * K * 2 * sizeof(float));  // {bias, e} per (token, slot)
+  off += align_up(G * B * H * nq * 64 * K * 2 * sizeof(float));  // bias and -e per (token, slot)
   l.dw_part = off;
   off += align_up(G * B * nq * H * K * sizeof(float));
   l.wts = off;

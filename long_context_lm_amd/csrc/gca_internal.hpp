@@ -60,7 +60,8 @@ struct AttendParams {
   void* dk;
   void* dv;
   float* dscore;
-  float* delta;         // [G, B, H, n_q, K, 64, 2] {log2 w_k - lse_{t,k} log2 e, e_{t,k} = <dout_t, O_{t,k}>}
+  float* delta;         // [G, B, H, n_q, K, 2, 64]: 64 biases log2 w_k - lse_{t,k} log2 e, then the
+                        // 64 negated e_{t,k} = <dout_t, O_{t,k}>
   float* dw_part;       // [G, B, n_q, H, K] per-head sums of e over a chunk's tokens
   float* wts;           // [G, B, n_q, K] fusion weights (0 on invalid slots)
   int32_t* pairs;       // [B, n_kv, pair_cap, 2] one entry per retrieval of each key chunk, in
