@@ -1449,25 +1449,9 @@ __device__ __forceinline__ PairRef decode_pair(const i32x2_t ent) {
   return r;
 }
 
-// Work item of a key-major workgroup.  A key chunk's list is longer the earlier the chunk (causal
-// retrieval offers chunk j to every later row), so (batch row, head) blocks are taken two at a
-// time and walked chunk-major within the pair: both blocks' long lists start before either
-// block's short ones, and the last block on each XCD does not leave its longest lists to run
-// alone at the end of the launch.  An odd last block runs by itself.
-__device__ __forceinline__ void key_item(int64_t lid, int64_t n_kv, int64_t n_bh, int64_t& bh, int64_t& j) {
-  const int64_t pair = lid / (2 * n_kv), r = lid - pair * 2 * n_kv;
-  if (2 * pair + 1 < n_bh) {
-    bh = 2 * pair + (r & 1);
-    j = r >> 1;
-  } else {
-    bh = 2 * pair;
-    j = r;
-  }
-}
-
 // One workgroup of two waves per (batch row, head, key chunk); each wave owns 32 of its keys and
 // walks the chunk's retrievals, double-buffered: the next entry's Q and dO tiles and its 64
-// {bias, e} pairs are copied in at the start of the current one.
+// biases and 64 -e are copied in at the start of the current one.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   using TL = Tile<T>;
@@ -1480,8 +1464,9 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  int64_t bh, j;
-  key_item(xcd_logical_block(blockIdx.x, gridDim.x), p.n_kv, static_cast<int64_t>(p.B) * p.H, bh, j);
+  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t j = lid % p.n_kv;
+  const int64_t bh = lid / p.n_kv;
   const int h = static_cast<int>(bh % p.H);
   const int b = static_cast<int>(bh / p.H);
   const int my_u = 32 * wave + li;
