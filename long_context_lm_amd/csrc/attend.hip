@@ -43,6 +43,7 @@ namespace {
 constexpr int kThreads = 128;  // two waves
 constexpr int kWaves = 2;
 constexpr int kEntRound = 512;  // inverse-index entries staged in LDS at a time
+constexpr int kSegEntries = 128;  // longest list one key-major workgroup walks when lists are split
 constexpr int64_t kWideMaxTiles = 256;  // query tiles up to which the forward runs one slot per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2f = 0.6931471805599453f;
@@ -1047,6 +1048,8 @@ __device__ __forceinline__ float sum_queries32(float x) {
 // copied into the single V buffer as soon as both waves have read it.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
+  // the split-list counters of the key-major pass that follows start at zero
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.long_ctl != nullptr) *p.long_ctl = 0;
   using TL = Tile<T>;
   using Off = TileOffsets<T, kWaves>;
   __shared__ __align__(1024) char Ka[TL::kBytes];
@@ -1449,24 +1452,20 @@ __device__ __forceinline__ PairRef decode_pair(const i32x2_t ent) {
   return r;
 }
 
-// One workgroup of two waves per (batch row, head, key chunk); each wave owns 32 of its keys and
-// walks the chunk's retrievals, double-buffered: the next entry's Q and dO tiles and its 64
-// biases and 64 -e are copied in at the start of the current one.
+// Key-major walk of one key chunk's entries e0 .. e1 - 1 (one (batch row, head, key chunk)):
+// each wave owns 32 of the chunk's keys and accumulates their dK (unscaled) and dV over the
+// entries, double-buffered: the next entry's Q and dO tiles and its 64 biases and 64 -e are
+// copied in at the start of the current one.  Every copy has landed and every LDS read is done
+// when it returns, so walks can follow one another in the same workgroup.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
+__device__ __forceinline__ void key_walk(const AttendParams& p, int64_t bh, int64_t j, int32_t e0, int32_t e1,
+                                         char* buf0, char* buf1, i32x2_t* ents, f32x16_t (&dkacc)[2],
+                                         f32x16_t (&dvacc)[2]) {
   using TL = Tile<T>;
   using Off = TileOffsets<T, kWaves>;
-  constexpr int kVecBytes = kChunk * 8;  // {bias, e} of the 64 queries of one entry
-  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];  // [Q tile, dO tile, vectors]
-  __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
-  __shared__ i32x2_t ents[kEntRound];
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t j = lid % p.n_kv;
-  const int64_t bh = lid / p.n_kv;
   const int h = static_cast<int>(bh % p.H);
   const int b = static_cast<int>(bh / p.H);
   const int my_u = 32 * wave + li;
@@ -1482,12 +1481,10 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   }
   Off off;
   off.init(wave);
-  f32x16_t dkacc[2] = {zero16(), zero16()};
-  f32x16_t dvacc[2] = {zero16(), zero16()};
+  dkacc[0] = dkacc[1] = dvacc[0] = dvacc[1] = zero16();
   const float c2 = p.attn_scale * kLog2e;
   const int64_t Lq = p.n_q * kChunk;
   const int64_t segment = static_cast<int64_t>(b) * p.n_kv + j;
-  const int32_t count = p.counts[segment];
   const i32x2_t* list = reinterpret_cast<const i32x2_t*>(p.pairs) + segment * p.pair_cap;
 
   // The list is walked in rounds of up to kEntRound entries {code, weight}, staged in LDS.  Each
@@ -1569,10 +1566,20 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
     // the next entry's copies landed, and every wave is done with this entry's buffer
     barrier_copies_landed_reads_done<0>();
   };
-  for (int32_t round0 = 0; round0 < count; round0 += kEntRound) {
-    n = count - round0 < kEntRound ? count - round0 : kEntRound;
+  // ents is read only inside body, before its closing barrier, so when a round (or a walk) ends
+  // every wave is done with it and the next round may restage it.
+  for (int32_t round0 = e0; round0 < e1; round0 += kEntRound) {
+    n = e1 - round0 < kEntRound ? e1 - round0 : kEntRound;
     for (int e = tid; e < n; e += kThreads) ents[e] = list[round0 + e];
     __syncthreads();
+    // The K and V fragments are in registers here (the barrier waited for every load), so the
+    // compiler has no load of its own left to wait for in the entry loop, where a vmcnt wait
+    // would also wait for the untracked prefetch copies.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      pin_in_registers(kf[s]);
+      pin_in_registers(vf[s]);
+    }
     fill(ents[0], buf0);
     barrier_copies_landed_reads_done<0>();
     for (int32_t pr = 0; pr < n; pr += 2) {
@@ -1580,10 +1587,14 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
       if (pr + 1 < n) body(pr + 1, buf1, buf0);
     }
   }
+}
 
-  T* dk = static_cast<T*>(p.dk) + krow * kDim;
-  T* dv = static_cast<T*>(p.dv) + krow * kDim;
-  const float sc = p.attn_scale;
+// dK, dV of one wave's 32 keys from its accumulators: into the dK, dV tensors (dK scaled by
+// attn_scale), or unscaled into a float [2][64 keys][64] partial of a split list.
+template <typename D>
+__device__ __forceinline__ void store_key_grads(D* dk, D* dv, float sc, const f32x16_t (&dkacc)[2],
+                                                const f32x16_t (&dvacc)[2]) {
+  const int hl = (threadIdx.x >> 5) & 1;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -1593,6 +1604,67 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
              sc * dkacc[dt][4 * a + 3]);
       store4(dv + d0, dvacc[dt][4 * a], dvacc[dt][4 * a + 1], dvacc[dt][4 * a + 2], dvacc[dt][4 * a + 3]);
     }
+}
+
+// One workgroup of two waves per (batch row, head, key chunk) walks the chunk's entries and
+// writes its dK, dV.  With long lists split (long_ctl set), a chunk of more than kSegEntries
+// entries is left to bwd_key_split_kernel, which runs just before.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
+  using TL = Tile<T>;
+  constexpr int kVecBytes = kChunk * 8;  // biases and -e of the 64 queries of one entry
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];  // [Q tile, dO tile, vectors]
+  __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
+  __shared__ i32x2_t ents[kEntRound];
+  const int my_u = 32 * (threadIdx.x >> 6) + (threadIdx.x & 31);
+  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t j = lid % p.n_kv;
+  const int64_t bh = lid / p.n_kv;
+  const int32_t count = p.counts[(bh / p.H) * p.n_kv + j];
+  // a split list is bwd_key_split_kernel's work: walk nothing and write nothing (not an early
+  // return, which would hold the walk's K/V loads back behind the count's)
+  const bool split = p.long_ctl != nullptr && count > kSegEntries;
+  f32x16_t dkacc[2], dvacc[2];
+  key_walk<T>(p, bh, j, 0, split ? 0 : count, buf0, buf1, ents, dkacc, dvacc);
+  if (split) return;
+  const int64_t krow = (bh * p.n_kv + j) * kChunk + my_u;
+  store_key_grads(static_cast<T*>(p.dk) + krow * kDim, static_cast<T*>(p.dv) + krow * kDim, p.attn_scale, dkacc,
+                  dvacc);
+}
+
+// The long lists' segments: work item f = q * H + h is the walk of segment slot q (at most
+// kSegEntries entries of one long chunk) for head h, taken round-robin by the workgroups, and
+// writes a float partial; score_grad_kernel sums each chunk's partials in segment order.  With
+// no long list, every workgroup ends at once.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_key_split_kernel(AttendParams p) {
+  using TL = Tile<T>;
+  constexpr int kVecBytes = kChunk * 8;
+  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];
+  __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
+  __shared__ i32x2_t ents[kEntRound];
+  const int my_u = 32 * (threadIdx.x >> 6) + (threadIdx.x & 31);
+  const uint64_t ctl = *p.long_ctl;
+  const int32_t n_long = min(static_cast<int32_t>(ctl >> 32), p.long_cap);
+  const int32_t n_seg = min(static_cast<int32_t>(ctl & 0xffffffffu), p.seg_cap);
+  const int64_t items = static_cast<int64_t>(n_seg) * p.H;
+  for (int64_t f = blockIdx.x; f < items; f += gridDim.x) {
+    const int32_t q = static_cast<int32_t>(f / p.H);
+    const int h = static_cast<int>(f - static_cast<int64_t>(q) * p.H);
+    const int32_t at = __builtin_amdgcn_readfirstlane(p.long_seg[q]);
+    if (at < 0 || at >= n_long) return;  // never, by the capacities' bound (see inverse_index_kernel)
+    const i32x4_t ent = reinterpret_cast<const i32x4_t*>(p.long_list)[at];  // {b, j, segments, first slot}
+    const int32_t b = __builtin_amdgcn_readfirstlane(ent[0]);
+    const int32_t j = __builtin_amdgcn_readfirstlane(ent[1]);
+    const int32_t count = p.counts[static_cast<int64_t>(b) * p.n_kv + j];
+    const int32_t e0 = (q - __builtin_amdgcn_readfirstlane(ent[3])) * kSegEntries;
+    const int32_t e1 = count - e0 < kSegEntries ? count : e0 + kSegEntries;
+    if (e0 < 0 || e0 >= e1) return;
+    f32x16_t dkacc[2], dvacc[2];
+    key_walk<T>(p, static_cast<int64_t>(b) * p.H + h, j, e0, e1, buf0, buf1, ents, dkacc, dvacc);
+    float* part = p.long_part + f * (2 * kChunk * kDim) + my_u * kDim;
+    store_key_grads(part, part + kChunk * kDim, 1.f, dkacc, dvacc);
+  }
 }
 
 // ------------------------------------------------------------- inverse retrieval index
@@ -1704,12 +1776,30 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
     }
     __syncthreads();
   }
-  if (tid < 64 && j < p.n_kv) p.counts[static_cast<int64_t>(b) * p.n_kv + j] = total[tid];
+  if (tid < 64 && j < p.n_kv) {
+    const int32_t c = total[tid];
+    p.counts[static_cast<int64_t>(b) * p.n_kv + j] = c;
+    // A list longer than kSegEntries is split for the key-major pass: one 64-bit atomic takes its
+    // place in the list of long chunks (high word) and its segment slots (low word), so the
+    // list stays in slot order.  The order of the chunks in it varies from run to run; what is
+    // computed for each chunk and segment does not.
+    if (p.long_ctl != nullptr && c > kSegEntries) {
+      const int32_t nseg = (c + kSegEntries - 1) / kSegEntries;
+      const unsigned long long old =
+          atomicAdd(reinterpret_cast<unsigned long long*>(p.long_ctl), (1ull << 32) | static_cast<unsigned long long>(nseg));
+      const int32_t at = static_cast<int32_t>(old >> 32), pos = static_cast<int32_t>(old & 0xffffffffull);
+      if (at < p.long_cap && pos + nseg <= p.seg_cap) {  // always, by the capacities' bound
+        reinterpret_cast<i32x4_t*>(p.long_list)[at] = i32x4_t{b, j, nseg, pos};
+        for (int32_t sg = 0; sg < nseg; ++sg) p.long_seg[pos + sg] = at;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------- d(score)
 // dscore_k = w_k (dw_k - sum_k' w_k' dw_k'), dw_k = sum over heads (in order) of the per-head
 // sums of e over the chunk's tokens.  Sixteen lanes per (g, b, row), one lane per slot.
+template <typename T>
 __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int k = threadIdx.x & 15;
@@ -1730,6 +1820,31 @@ __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) wdw += __shfl_xor(wdw, off, 16);
   if (in_range) p.dscore[gid * p.K + k] = valid ? w * (dw - wdw) : 0.f;
+  // dK, dV of the chunks whose lists were split: the segments' partials summed in segment order,
+  // dK scaled by attn_scale, one (chunk, head) per workgroup in turn
+  if (p.long_ctl == nullptr) return;
+  const uint64_t ctl = *p.long_ctl;
+  const int64_t n_long = min(static_cast<int32_t>(ctl >> 32), p.long_cap);
+  constexpr int kPart = 2 * kChunk * kDim;  // floats of one partial: [dK, dV][64 keys][64]
+  for (int64_t it = blockIdx.x; it < n_long * p.H; it += gridDim.x) {
+    const int64_t li = it / p.H;
+    const int h = static_cast<int>(it - li * p.H);
+    const i32x4_t ent = reinterpret_cast<const i32x4_t*>(p.long_list)[li];  // {b, j, segments, first slot}
+    if (ent[0] < 0 || ent[0] >= p.B || ent[1] < 0 || ent[1] >= p.n_kv || ent[2] < 1 || ent[3] < 0 ||
+        ent[3] + ent[2] > p.seg_cap)
+      continue;  // never: every entry is written whole before the key-major pass
+    const int64_t tile = ((static_cast<int64_t>(ent[0]) * p.H + h) * p.n_kv + ent[1]) * kChunk * kDim;
+    const f32x4_t* part = reinterpret_cast<const f32x4_t*>(p.long_part + (static_cast<int64_t>(ent[3]) * p.H + h) * kPart);
+    const int64_t stride = static_cast<int64_t>(p.H) * kPart / 4;
+    for (int e = threadIdx.x; e < kPart / 4; e += 256) {
+      f32x4_t acc = part[e];
+      for (int32_t sg = 1; sg < ent[2]; ++sg) acc += part[sg * stride + e];
+      const bool is_v = e >= kPart / 8;
+      const float sc = is_v ? 1.f : p.attn_scale;
+      T* dst = static_cast<T*>(is_v ? p.dv : p.dk) + tile + 4 * (e & (kPart / 8 - 1));
+      store4(dst, sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
+    }
+  }
 }
 
 // ------------------------------------------------- fused layer attention (window + GCA), forward
@@ -2112,6 +2227,8 @@ __global__ __launch_bounds__(kThreads) void fused_fwd2_kernel(AttendParams p) {
 // {-lse_sw log2 e, D} pairs written at the end.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams p) {
+  // the split-list counters of the key-major pass that follows start at zero
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.long_ctl != nullptr) *p.long_ctl = 0;
   using TL = Tile<T>;
   using Off = TileOffsets<T, kWaves>;
   __shared__ __align__(1024) char Ka[TL::kBytes];
@@ -2360,6 +2477,14 @@ hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_key_split(const AttendParams& p, bool f32, hipStream_t s) {
+  if (f32)
+    hipLaunchKernelGGL(bwd_key_split_kernel<float>, dim3(static_cast<uint32_t>(p.n_help)), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_key_split_kernel<bf16_t>, dim3(static_cast<uint32_t>(p.n_help)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.n_kv;
   if (f32)
@@ -2369,10 +2494,13 @@ hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_grad(const AttendParams& p, hipStream_t s) {
+hipError_t launch_score_grad(const AttendParams& p, bool f32, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(p.G) * p.B * p.n_q;
   const int64_t blocks = (rows + 15) / 16;
-  hipLaunchKernelGGL(score_grad_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p);
+  if (f32)
+    hipLaunchKernelGGL(score_grad_kernel<float>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(score_grad_kernel<bf16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ const char* kernel_name(int id) {
   static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
                                            "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd",
-                                           "sw_bwd_query", "sw_bwd_key", "fused_fwd", "fused_bwd_query"};
+                                           "sw_bwd_query", "sw_bwd_key", "fused_fwd", "fused_bwd_query",
+                                           "bwd_key_split"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -98,6 +99,9 @@ gca_status validate_problem(const gca_problem* p) {
   if (p->n_kv_chunks > 0 && static_cast<int64_t>(p->B) * p->H > big / p->n_kv_chunks) return GCA_ERR_UNSUPPORTED;
   // (group, row, slot) codes of the inverse index travel as int32
   if (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk > big) return GCA_ERR_UNSUPPORTED;
+  // so do the split lists' segment slots (at most B (G n_q K / 64 + 2) of them)
+  if (static_cast<int64_t>(p->B) * (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk / 64 + 2) > big)
+    return GCA_ERR_UNSUPPORTED;
   return GCA_OK;
 }
 
@@ -149,8 +153,13 @@ LandmarkLayout plan_landmark(const gca_problem* p) {
   return l;
 }
 
+// Lists longer than this many entries are split over several key-major workgroups (the
+// kernels' kSegEntries).
+constexpr int64_t kSegEntries = 128;
+
 struct BackwardLayout {
-  size_t delta, dw_part, wts, pairs, counts, total;
+  size_t delta, dw_part, wts, pairs, counts, long_ctl, long_list, long_seg, long_part, total;
+  int64_t long_cap, seg_cap;  // 0: no list can be long, nothing is split
 };
 
 BackwardLayout plan_backward(const gca_problem* p) {
@@ -169,8 +178,38 @@ BackwardLayout plan_backward(const gca_problem* p) {
   off += align_up(B * nkv * G * nq * 2 * sizeof(int32_t));
   l.counts = off;
   off += align_up(B * nkv * sizeof(int32_t));
+  // Split lists.  A batch row holds at most L = G n_q K entries (each retrieval row names at most
+  // K chunks), so at most floor(L / (E + 1)) of its chunks exceed E = kSegEntries entries, and
+  // their segments number at most ceil(L / E) + that many.
+  const int64_t L = static_cast<int64_t>(G * nq * K);
+  if (nkv > 0 && L > kSegEntries) {
+    l.long_cap = static_cast<int64_t>(B) * (L / (kSegEntries + 1));
+    l.seg_cap = static_cast<int64_t>(B) * ((L + kSegEntries - 1) / kSegEntries + L / (kSegEntries + 1));
+    l.long_ctl = off;
+    off += align_up(sizeof(uint64_t));
+    l.long_list = off;
+    off += align_up(static_cast<size_t>(l.long_cap) * 4 * sizeof(int32_t));
+    l.long_seg = off;
+    off += align_up(static_cast<size_t>(l.seg_cap) * sizeof(int32_t));
+    l.long_part = off;
+    off += align_up(static_cast<size_t>(l.seg_cap) * H * 2 * 64 * 64 * sizeof(float));
+  }
   l.total = off;
   return l;
+}
+
+// Points the key-major pass at the split-list areas of the backward workspace (when a list can
+// be long and a query-major pass runs first to clear the counter).
+void set_long_lists(AttendParams& a, const BackwardLayout& L, char* w, bool any) {
+  if (L.seg_cap == 0 || !any) return;
+  a.long_ctl = reinterpret_cast<uint64_t*>(w + L.long_ctl);
+  a.long_list = reinterpret_cast<int32_t*>(w + L.long_list);
+  a.long_seg = reinterpret_cast<int32_t*>(w + L.long_seg);
+  a.long_part = reinterpret_cast<float*>(w + L.long_part);
+  a.long_cap = static_cast<int32_t>(L.long_cap);
+  a.seg_cap = static_cast<int32_t>(L.seg_cap);
+  const int64_t items = L.seg_cap * a.H;  // the most segment walks a call can have
+  a.n_help = static_cast<int32_t>(items < 512 ? items : 512);
 }
 
 gca_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
@@ -419,13 +458,15 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   a.pairs = reinterpret_cast<int32_t*>(w + L.pairs);
   a.counts = reinterpret_cast<int32_t*>(w + L.counts);
   a.entry_decoded = 1;
+  set_long_lists(a, L, w, any);
   const bool f32 = p->dtype == GCA_F32;
   // With no query chunk, only the inverse index (empty lists) and the key-major pass (which
   // writes zero dk, dv for chunks nobody retrieved) run.
   if (any) GCA_TRY(launch(kBwdQuery, s, [&] { return launch_bwd_query(a, f32, s); }));
   if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
+  if (kv && a.long_ctl) GCA_TRY(launch(kBwdKeySplit, s, [&] { return launch_bwd_key_split(a, f32, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
-  if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
+  if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, f32, s); }));
   return GCA_OK;
 }
 
@@ -668,6 +709,7 @@ gca_status gca_fused_backward(const gca_problem* problem, int32_t window, const 
   a.counts = reinterpret_cast<int32_t*>(w + L.counts);
   a.sw_stats = reinterpret_cast<float*>(w + L.total);
   a.entry_decoded = 1;
+  set_long_lists(a, L, w, any);
   const bool f32 = p->dtype == GCA_F32;
   if (any) {
     GCA_TRY(launch(kFusedBwdQuery, s, [&] { return launch_fused_bwd_query(a, f32, s); }));
@@ -682,8 +724,9 @@ gca_status gca_fused_backward(const gca_problem* problem, int32_t window, const 
     GCA_TRY(launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(sw, f32, s); }));
   }
   if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
+  if (kv && a.long_ctl) GCA_TRY(launch(kBwdKeySplit, s, [&] { return launch_bwd_key_split(a, f32, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
-  if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, s); }));
+  if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, f32, s); }));
   return GCA_OK;
 }
 

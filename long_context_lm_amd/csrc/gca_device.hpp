@@ -28,6 +28,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 struct bf16_t {  // storage type of one bf16 value
   uint16_t bits;
@@ -86,6 +87,10 @@ struct Frag<float> {
     v1 = f32x4_t{x[4], x[5], x[6], x[7]};
   }
 };
+
+// An opaque use of a fragment: the value must be in registers at this point of the program.
+__device__ __forceinline__ void pin_in_registers(Frag<bf16_t>& f) { asm volatile("" : "+v"(f.v)); }
+__device__ __forceinline__ void pin_in_registers(Frag<float>& f) { asm volatile("" : "+v"(f.v0), "+v"(f.v1)); }
 
 __device__ __forceinline__ f32x16_t mma(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v),

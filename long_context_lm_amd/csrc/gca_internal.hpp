@@ -24,6 +24,7 @@ enum KernelId {
   kSwBwdKey,
   kFusedFwd,
   kFusedBwdQuery,
+  kBwdKeySplit,
   kNumKernels
 };
 const char* kernel_name(int id);
@@ -81,6 +82,15 @@ struct AttendParams {
   int32_t causal_rows;  // inverse index: 1 = list only rows whose global chunk lies after the key
                         // chunk (the landmark gradients' rule j < q_base + row); 0 = every row
                         // (the GCA backward, whose other passes count every 0 <= j < n_kv)
+  // key-major pass with long lists split (null: no split): {long chunks, segment slots} counter,
+  // long chunks [long_cap][4] {b, j, segments, first slot}, the long chunk of each segment slot
+  // [seg_cap], float partials [seg_cap * H][2][64][64]; n_help workgroups walk the segments
+  // (bwd_key_split_kernel)
+  uint64_t* long_ctl;
+  int32_t* long_list;
+  int32_t* long_seg;
+  float* long_part;
+  int32_t long_cap, seg_cap, n_help;
   float attn_scale;
 };
 
@@ -139,7 +149,8 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_inverse_index(const AttendParams& p, hipStream_t s);
 hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s);
-hipError_t launch_score_grad(const AttendParams& p, hipStream_t s);
+hipError_t launch_bwd_key_split(const AttendParams& p, bool f32, hipStream_t s);
+hipError_t launch_score_grad(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_fetch_chunks(const FetchParams& p, bool f32, hipStream_t s);

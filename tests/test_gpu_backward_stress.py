@@ -7,6 +7,10 @@ sums then run over the longest entry lists the inverse retrieval index can hold:
 512 (group, row, slot) entries, so the key-major pass stages its list in more than one round and
 the landmark key pass walks it in more than eight 64-entry pieces.
 
+The key-major pass splits a list longer than 128 entries into segments that separate workgroups
+walk, and sums their partials in segment order; the hub's list takes that path, and its result
+must not change from one call to the next.
+
 Caller-built indices: gca_forward and gca_backward count every slot with 0 <= idx < n_kv, also
 chunks at or after the row's own chunk (a caller's own selection, or the compact buffers of
 gca_fetch_chunks).  The key-major pass must then include the same slots as the query-major pass.
@@ -69,7 +73,12 @@ def test_hub_chunk_backward_and_landmarks(dtype):
     o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
     dq, dk, dv, ds = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
     dlq, dlk = gca.landmark_backward(cfg, dev["lq"], dev["lk"], idx, ds)
+    # the hub's list is split over several key-major workgroups (segments placed by an atomic
+    # counter whose order varies): a second call must still give the same bits
+    again = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
     torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dscore"), (dq, dk, dv, ds), again):
+        assert torch.equal(a, b), f"{name}: second call differs"
     say("  gpu done; running oracle")
     r_idx, r_sc = O.retrieve(x["lq"], x["lk"], 8, use_gumbel=True, seed=21)
     np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
