@@ -388,6 +388,29 @@ def fused_timing(B=8, H=12, n_c=256, window=512, K=8, iters=10):
     return res
 
 
+def skewed_retrieval_timing(shape, dev, bufs, step, iters=10):
+    """The training step (retrieve + forward + backward, G=2, K=8, Gumbel, bf16) with a hub
+    chunk: every query landmark of a (group, batch row) shares a direction with key landmark 0,
+    which then enters nearly every row's top-k (about 500 of the 512 (group, row) entries of a
+    batch row).  Same q, k, v, dout as the headline step; the step's landmarks are overwritten.
+    The hub's list is split over several key-major workgroups (bwd_key_split)."""
+    import numpy as np
+
+    from long_context_lm_amd import inputs as I
+
+    lq, lk = I.hub_landmarks(shape, seed=5)
+    dev["lq"].copy_(I.to_dtype(lq, "bf16"))
+    dev["lk"].copy_(I.to_dtype(lk, "bf16"))
+    ms, kern = _timed(step, iters)
+    idx = bufs["idx"].cpu().numpy()[:, :, : shape.n_q - 1]
+    per_b = [int(np.bincount(idx[:, b][idx[:, b] >= 0], minlength=shape.n_kv).max()) for b in range(shape.B)]
+    res = {"workload": "GCA retrieve+fwd+bwd, B=8 L=16384 H=12 d=64 K=8 G=2, Gumbel, bf16; landmarks with a hub "
+                       "chunk (chunk 0 in nearly every row's top-k)",
+           "ms_per_step": ms, "tokens_per_s": shape.B * shape.n_q * 64 / (ms * 1e-3), "kernels_us": kern,
+           "max_entries_per_chunk": max(per_b), "mean_entries_per_chunk": float((idx >= 0).sum() / (shape.B * shape.n_kv))}
+    return res
+
+
 def _device_inputs(shape, seed, scale=0.125):
     """Seeded N(0, scale^2) bf16 inputs drawn on the device (timing runs only: their values
     change no launch shape, and host generation of several GiB would dominate the run)."""
@@ -871,6 +894,12 @@ def main():
         cpu = cpu_baseline(shape, host)
         log(f"  oracle {cpu['value']:.0f} tokens/s")
 
+    log("training step with a hub chunk in nearly every row's top-k (skewed retrieval)")
+    skew = skewed_retrieval_timing(shape, dev, bufs, step)
+    log(f"  {skew['ms_per_step']:.3f} ms per step ({skew['tokens_per_s'] / 1e6:.1f} M tokens/s), at most "
+        f"{skew['max_entries_per_chunk']} entries per chunk; "
+        + ", ".join(f"{k} {v:.1f}" for k, v in skew["kernels_us"].items()))
+
     infer = None
     del dev, bufs
     torch.cuda.empty_cache()
@@ -952,6 +981,7 @@ def main():
         "landmark_backward": lmk,
         "sliding_window": sw,
         "fused_window_gca": fz,
+        "skewed_retrieval": skew,
         "forward_only": fwd,
         "length_scaling": scaling,
     }

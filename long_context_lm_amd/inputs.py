@@ -88,6 +88,20 @@ def make_inputs(shape: Shape, dtype: str, seed: int = 0, scale: float = 1.0,
     return {n: to_dtype(normal(shape.tensor_shape(n), seed, n, scale), dtype) for n in names}
 
 
+def hub_landmarks(shape: Shape, seed: int, hub: int = 0):
+    """Landmarks with a hub chunk: every query landmark shares a direction u of its (group,
+    batch row), lq = 0.5 u + sqrt(0.75) z (unit variance), and key landmark `hub` is 2 u, so its
+    score is about 8 against about N(0, 1) for the other chunks and it enters nearly every row's
+    top-k.  float32 arrays lq [G, B, n_q, dl] and lk [G, B, n_kv, dl] (N(0, 1) elsewhere)."""
+    rng = np.random.default_rng([seed, 99])
+    G, B = shape.G, shape.B
+    u = rng.standard_normal((G, B, 1, shape.dl))
+    lq = 0.5 * u + np.sqrt(0.75) * rng.standard_normal((G, B, shape.n_q, shape.dl))
+    lk = rng.standard_normal((G, B, shape.n_kv, shape.dl))
+    lk[:, :, hub] = 2.0 * u[:, :, 0]
+    return lq.astype(np.float32), lk.astype(np.float32)
+
+
 def as_f64(t) -> np.ndarray:
     """Exact float64 copy of a CPU/GPU tensor (bf16 and fp32 values are exact in fp64)."""
     import torch

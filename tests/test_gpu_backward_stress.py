@@ -45,15 +45,9 @@ def _hub_inputs(shape, dtype, seed):
     host = I.make_inputs(shape, dtype, seed=seed, scale=1.0)
     quarter = I.make_inputs(shape, dtype, seed=seed, scale=0.25, names=("v", "dout"))
     host["v"], host["dout"] = quarter["v"], quarter["dout"]
-    rng = np.random.default_rng([seed, 99])
-    G, B, n_q, n_kv = shape.G, shape.B, shape.n_q, shape.n_kv
-    u = rng.standard_normal((G, B, 1, 64))
-    lq = 0.5 * u + np.sqrt(0.75) * rng.standard_normal((G, B, n_q, 64))
-    lk = rng.standard_normal((G, B, n_kv, 64))
-    lk[:, :, 0] = 2.0 * u[:, :, 0]
-    cast = torch.bfloat16 if dtype == "bf16" else torch.float32
-    host["lq"] = torch.from_numpy(lq.astype(np.float32)).to(cast)
-    host["lk"] = torch.from_numpy(lk.astype(np.float32)).to(cast)
+    lq, lk = I.hub_landmarks(shape, seed)
+    host["lq"] = I.to_dtype(lq, dtype)
+    host["lk"] = I.to_dtype(lk, dtype)
     return host
 
 
