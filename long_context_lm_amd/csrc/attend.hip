@@ -730,6 +730,14 @@ __global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
   };
   off.copy(tile(p.k, kt0), Ks, 0);
   off.copy(tile(p.v, kt0), Vs, 0);
+  // The loads above are pinned here, before the loop, so that the compiler waits for them once:
+  // left to their first use in the loop, its vmcnt waits would run in every iteration and also
+  // wait for the untracked prefetch copies in flight.  The first K and V tiles are needed at
+  // once anyway.
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pin_in_registers(qf[qh][s]);
 
   f32x16_t oacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
@@ -1096,6 +1104,15 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     lse_cur = lse_q[slot_of(0) * kChunk];
     barrier_copies_landed<0>();
   }
+  // Every load above has landed (the barrier's own wait).  Pinning the values here lets the
+  // compiler place its waits for them now, where they cost nothing; left to their first use in
+  // the slot loop, its vmcnt waits would also wait for the untracked prefetch copies.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    pin_in_registers(qf[s]);
+    pin_in_registers(df[s]);
+  }
+  asm volatile("" : "+v"(lse_cur));
 
   f32x16_t dqacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
@@ -1154,10 +1171,11 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) dqacc[dt] = mma(off.vfrag(Kc, s, dt), zf[s], dqacc[dt]);
-    lse_cur = lse_nxt;
     // K(n+1), the lse and V(n+1) landed (the delta store may not have): the next slot can start;
     // every wave has also read K(n), whose buffer the next slot refills
     if (more) barrier_copies_landed_reads_done<1>();
+    asm volatile("" : "+v"(lse_nxt));  // landed: the compiler's wait for it goes here, not later
+    lse_cur = lse_nxt;
   };
   for (int n = 0; n < nslots; n += 2) {
     slot_step(n, Ka, Kb);
@@ -1253,6 +1271,17 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
   off.copy(tile(p.k, kt0), Ka, wave);
   off.copy(tile(p.v, kt0), Vs, wave);
   barrier_copies_landed<0>();
+  // The loads above are pinned here, before the loop, so that the compiler waits for them once:
+  // left to their first use in the loop, its vmcnt waits would run in every iteration and also
+  // wait for the untracked prefetch copies in flight.  Here they have all landed: the barrier
+  // waited.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    pin_in_registers(qf[s]);
+    pin_in_registers(df[s]);
+  }
+  float bias_pinned = bias;
+  asm volatile("" : "+v"(bias_pinned));
 
   f32x16_t dqacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
@@ -1282,7 +1311,7 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tt = s >> 1, r = 8 * (s & 1) + e;
-        const float pw = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias));
+        const float pw = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias_pinned));
         x[e] = pw * (pacc[tt][r] - D);
       }
       zf[s].set(x);
@@ -1416,6 +1445,15 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
   };
   fill(kt, buf0);
   barrier_copies_landed_reads_done<0>();
+  // The loads above are pinned here, before the loop, so that the compiler waits for them once:
+  // left to their first use in the loop, its vmcnt waits would run in every iteration and also
+  // wait for the untracked prefetch copies in flight.  Here they have all landed: the barrier
+  // waited.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    pin_in_registers(kf[s]);
+    pin_in_registers(vf[s]);
+  }
   for (int n = 0; n < count; n += 2) {
     body(n, buf0, buf1);
     if (n + 1 < count) body(n + 1, buf1, buf0);
@@ -1906,6 +1944,14 @@ __global__ __launch_bounds__(64) void fused_fwd_kernel(AttendParams p) {
   };
   off.copy_at(item_tile(p.k_sw, p.k, 0, rem_k), ks_addr, 0);
   off.copy_at(item_tile(p.v_sw, p.v, 0, rem_v), vs_addr, 0);
+  // The loads above are pinned here, before the loop, so that the compiler waits for them once:
+  // left to their first use in the loop, its vmcnt waits would run in every iteration and also
+  // wait for the untracked prefetch copies in flight.  The first item's tiles are needed at once
+  // anyway.
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pin_in_registers(qf[qh][s]);
 
   f32x16_t oacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
@@ -2286,6 +2332,18 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
   off.copy(item_tile(p.v, p.v_sw, 0), Vs, wave);
   if (nslots > 0) lse_cur = lse_q[slot_of(0) * kChunk];
   barrier_copies_landed<0>();
+  // The loads above are pinned here, before the loop, so that the compiler waits for them once:
+  // left to their first use in the loop, its vmcnt waits would run in every iteration and also
+  // wait for the untracked prefetch copies in flight.  Here they have all landed: the barrier
+  // waited.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    pin_in_registers(qf[s]);
+    pin_in_registers(df[s]);
+  }
+  asm volatile("" : "+v"(lse_cur));
+  float bias_sw_pinned = bias_sw;
+  asm volatile("" : "+v"(bias_sw_pinned));
 
   f32x16_t dqacc[2] = {zero16(), zero16()};
   float d_gca = 0.f;  // sum over the slots of w_k e_k (this lane's query)
@@ -2352,7 +2410,7 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
 #pragma unroll
         for (int ee = 0; ee < 8; ++ee) {
           const int tt = s >> 1, r = 8 * (s & 1) + ee;
-          const float pw = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias_sw));
+          const float pw = fast_exp2(__builtin_fmaf(sacc[tt][r], c2, bias_sw_pinned));
           x[ee] = pw * (pacc[tt][r] - d_sw);
         }
         zf[s].set(x);
@@ -2362,13 +2420,16 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) dqacc[dt] = mma(off.vfrag(Kc, s, dt), zf[s], dqacc[dt]);
-    lse_cur = lse_nxt;
     // K(i + 1), its lse and V(i + 1) landed (a slot's delta store may not have); every wave has
     // also read K(i), whose buffer the next item refills
     if (more) {
       if (is_gca) barrier_copies_landed_reads_done<1>();
       else barrier_copies_landed_reads_done<0>();
     }
+    // lse_nxt has landed (the barrier's wait): the compiler's wait for it goes here, not later
+    // (it also waits for the slot's delta store, which the barrier left in flight)
+    asm volatile("" : "+v"(lse_nxt));
+    lse_cur = lse_nxt;
   };
   for (int i = 0; i < n_items; i += 2) {
     step(i, Ka, Kb);
