@@ -111,11 +111,65 @@ def untracked_copy_violations(asm: str) -> list[str]:
     return sorted(set(bad))
 
 
+def loop_vmcnt_waits(asm: str) -> list[str]:
+    """Compiler-placed vmcnt waits in the matrix-core blocks of loops (empty list: none).
+
+    A vmcnt wait counts the untracked prefetch copies too, so one that the compiler places
+    inside a pipelined loop (typically for a value loaded before the loop, at its first use)
+    runs in every iteration and waits for the next tile's copies: the prefetch is lost.  Waits
+    written in the kernels' inline assembly are the counted ones and are not reported, nor is
+    the wait of a workgroup barrier (followed by s_barrier).  Only functions that issue copies
+    from inline assembly are checked (a kernel whose copies the compiler tracks needs its waits)."""
+    bad = []
+    fn = block = None
+    in_loop = in_asm = False
+    pending = []  # (block, wait) of the current block, reported if the block issues a product
+    mfma = False
+    found = []  # (function, block, wait) candidates
+    untracked = set()  # functions with copies issued from inline assembly
+
+    def flush():
+        if mfma and in_loop:
+            found.extend((fn, b, w) for b, w in pending)
+
+    lines = asm.splitlines()
+    for n, line in enumerate(lines):
+        t = line.strip()
+        func = re.match(r"([A-Za-z_][\w$]*):", line)
+        blk = re.match(r"(\.LBB\d+_\d+):(.*)", line)
+        if func or blk:
+            flush()
+            pending, mfma = [], False
+            if func:
+                fn, block, in_loop = func.group(1), "entry", False
+            else:
+                block, in_loop = blk.group(1), "Loop" in blk.group(2)
+            continue
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif t.startswith(";;#ASMEND"):
+            in_asm = False
+        elif in_asm and t.startswith("global_load_lds"):
+            untracked.add(fn)
+        elif t.startswith("v_mfma"):
+            mfma = True
+        elif t.startswith("s_waitcnt") and "vmcnt" in t and not in_asm:
+            nxt = next((x.strip() for x in lines[n + 1:] if x.strip() and not x.strip().startswith(";")), "")
+            if not nxt.startswith("s_barrier"):
+                pending.append((block, t.split(";")[0].strip()))
+    flush()
+    bad = [f"{f} {b}: {w}" for f, b, w in found if f in untracked]
+    return sorted(set(bad))
+
+
 def guard_untracked_copies() -> None:
-    """Fail if a file using untracked LDS copies compiles to code that breaks their waits."""
+    """Fail if a file using untracked LDS copies compiles to code that breaks their waits, or
+    that waits for them by accident inside a pipelined loop."""
     bad = []
     for src in UNTRACKED_COPY_SOURCES:
-        bad += [f"{src}: {b}" for b in untracked_copy_violations(_device_asm(src))]
+        asm = _device_asm(src)
+        bad += [f"{src}: {b}" for b in untracked_copy_violations(asm)]
+        bad += [f"{src}: compiler vmcnt wait in a loop: {b}" for b in loop_vmcnt_waits(asm)]
     if bad:
         raise RuntimeError("untracked LDS copies with compiler-issued memory operations:\n  " + "\n  ".join(bad))
 

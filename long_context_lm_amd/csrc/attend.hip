@@ -291,6 +291,11 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
     off.copy(kv_tile<T>(p.v, p, c.b, c.h, j), Vs, wave);
     barrier_copies_landed<kC>();  // K(0) landed and visible; V(0) may still be in flight
   }
+  // The query fragments are pinned here, before the loop, so that the compiler waits for them
+  // once (left to their first use in the loop, its vmcnt waits would run in every iteration and
+  // also wait for the prefetch copies in flight).
+#pragma unroll
+  for (int s = 0; s < 4; ++s) pin_in_registers(qf[s]);
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
@@ -871,6 +876,11 @@ __global__ __launch_bounds__(kThreads) void sw_fwd2_kernel(SwParams p) {
   off.copy(tile(p.k, kt0), Ks, wave);
   off.copy(tile(p.v, kt0), Vs, wave);
   barrier_copies_landed<kC>();  // K(kt0) landed and visible; V(kt0) may still be in flight
+  // The query fragments are pinned here, before the loop, so that the compiler waits for them
+  // once (left to their first use in the loop, its vmcnt waits would run in every iteration and
+  // also wait for the prefetch copies in flight).
+#pragma unroll
+  for (int s = 0; s < 4; ++s) pin_in_registers(qf[s]);
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -2161,6 +2171,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd2_kernel(AttendParams p) {
   off.copy(item_tile(p.k_sw, p.k, 0), Ks, wave);
   off.copy(item_tile(p.v_sw, p.v, 0), Vs, wave);
   barrier_copies_landed<kC>();  // K(0) landed and visible; V(0) may still be in flight
+  // The query fragments are pinned here, before the loop, so that the compiler waits for them
+  // once (left to their first use in the loop, its vmcnt waits would run in every iteration and
+  // also wait for the prefetch copies in flight).
+#pragma unroll
+  for (int s = 0; s < 4; ++s) pin_in_registers(qf[s]);
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   float m_run = -__builtin_inff(), l_run = 0.f;
