@@ -134,3 +134,35 @@ def test_caller_indices_at_or_after_the_row(dtype):
     # chunks 64..99 are only reachable through rows below 64 and through later rows alike
     assert_close("dk[chunks 64..99]", I.as_f64(grads[1])[:, :, 64 * 64:], r_g[1][:, :, 64 * 64:], dtype)
     assert_close("dv[chunks 64..99]", I.as_f64(grads[2])[:, :, 64 * 64:], r_g[2][:, :, 64 * 64:], dtype)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_lists_odd_shapes(dtype):
+    """Three groups, three batch rows, K = 16, a history longer than the query chunks, and a hub
+    chunk named by more than 128 entries (G (n_q - 1) = 147): its list is split into two
+    segments, while the other chunks' lists are walked whole.  Against the oracle backward, and
+    a second call must give the same bits."""
+    shape = I.Shape(B=3, G=3, H=2, n_q=50, n_kv=60, topk=16)
+    cfg = config_for(shape, dtype, use_gumbel=True, seed=7)
+    say("case split lists", shape, dtype)
+    host = _hub_inputs(shape, dtype, seed=17)
+    x = {k: I.as_f64(v) for k, v in host.items()}
+    dev = upload(host)
+    idx, sc = gca.retrieve(cfg, dev["lq"], dev["lk"])
+    o, lse = gca.forward(cfg, dev["q"], dev["k"], dev["v"], idx, sc)
+    grads = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
+    again = gca.backward(cfg, dev["q"], dev["k"], dev["v"], idx, sc, lse, dev["dout"])
+    torch.cuda.synchronize()
+    r_idx, r_sc = O.retrieve(x["lq"], x["lk"], 16, use_gumbel=True, seed=7)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r_idx)
+    feeds = r_idx[:, :, : shape.n_q - 1]
+    longest = max(int((feeds[:, b] == j).sum()) for b in range(shape.B) for j in range(shape.n_kv))
+    say(f"  longest list {longest} entries")
+    assert longest > 128, "a list must exceed one segment"
+    r_g = O.backward(x["q"], x["k"], x["v"], r_idx, r_sc, x["dout"])
+    for name, got, ref, rep in zip(("dq", "dk", "dv", "dscore"), grads, r_g, again):
+        assert torch.equal(got, rep), f"{name}: second call differs"
+        assert_close(name, I.as_f64(got), ref, dtype)
+        if dtype == "bf16" and name in ("dk", "dv"):
+            assert_tiles_close(name, I.as_f64(got), ref)
