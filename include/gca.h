@@ -207,8 +207,8 @@ gca_status gca_sw_forward(const gca_problem* problem, int32_t window, const void
  *   dS = P (dP - D),  dq = attn_scale dS k,  dk = attn_scale dS^T q,  dv = P^T dout,
  * in fp32 over fixed orders without atomics (bit-identical from run to run), rounded once to dtype.
  * q, k, v, o and lse (from gca_sw_forward), dout: inputs [B,H,L,64] (lse [B,H,L] fp32); dq, dk, dv:
- * outputs like q.  ws: >= gca_workspace_size(SW_BACKWARD) = B*H*L*8 bytes (per-token
- * {-lse log2 e, D}; contents need no setup).  Same problem rules as gca_sw_forward.
+ * outputs like q.  ws: >= gca_workspace_size(SW_BACKWARD) = B*H*L*8 bytes (per token
+ * -lse log2 e and -D; contents need no setup).  Same problem rules as gca_sw_forward.
  */
 gca_status gca_sw_backward(const gca_problem* problem, int32_t window, const void* q, const void* k,
                            const void* v, const void* o, const float* lse, const void* dout,

@@ -1212,9 +1212,9 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
 // then dQ = scale dS K query-major and dK = scale dS^T Q, dV = P^T dO key-major, without atomics.
 // The query-major pass walks key tiles t - m .. t exactly as the GCA query-major pass walks its
 // slots (double-buffered K, single V, two waves of 32 queries); it first computes D from the
-// stored output and writes {-lse log2 e, D} per query, which the key-major pass reads as the GCA
-// key-major pass reads its {bias, e} vectors.  Masked scores become -inf before the exp, so their
-// P and dS are exactly 0.
+// stored output and writes -lse log2 e and -D per query (per query tile: 64 of each), which the
+// key-major pass reads as the GCA key-major pass reads its biases and -e.  Masked scores become
+// -inf before the exp, so their P and dS are exactly 0.
 
 // <a, b> over one lane's eight fragment elements
 __device__ __forceinline__ float frag_dot(const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
@@ -1269,7 +1269,8 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
   for (int s = 0; s < 4; ++s) dd += frag_dot(df[s], of[s]);
   const float D = xor32_sum(dd);
   const float bias = -p.lse_in[my_row] * kLog2e;
-  if (hl == 0) reinterpret_cast<f32x2_t*>(p.stats)[my_row] = f32x2_t{bias, D};
+  // per query tile: 64 biases, then the 64 negated D (one store: each lane half writes one)
+  p.stats[2 * qrow0 + 64 * hl + my_q] = hl ? -D : bias;
   Off off;
   off.init(wave);
 
@@ -1351,7 +1352,7 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
 
 // Key-major pass: one workgroup of two waves (32 keys each) per key tile kt walks the query tiles
 // kt .. kt + m whose windows reach it, double-buffered like the GCA key-major pass (Q tile, dO
-// tile and the 64 {bias, D} pairs of the next query tile copied in at the start of the current).
+// tile and the 64 biases and 64 -D of the next query tile copied in at the start of the current).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
   using TL = Tile<T>;
@@ -1388,22 +1389,27 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
     const int64_t qrow0 = row0 + qt * kChunk;
     off.copy(static_cast<const T*>(p.q) + qrow0 * kDim, buf, wave);
     off.copy(static_cast<const T*>(p.dout) + qrow0 * kDim, buf + TL::kBytes, wave);
-    // wave w copies the pairs of queries 32 w .. 32 w + 31 (16 bytes per lane, lanes < 16)
-    const float* src = p.stats + 2 * (qrow0 + 32 * wave);
-    if (lane < 16) copy16_async_untracked(src, 16u * lane, buf + 2 * TL::kBytes + 256 * wave);
+    // wave w copies the biases and the -D of queries 32 w .. 32 w + 31 (16 bytes per lane,
+    // lanes < 16): lanes 0-7 the biases, lanes 8-15 the -D, to [32 biases, 32 -D] at 256 w
+    const float* src = p.stats + 2 * qrow0 + 32 * wave;
+    if (lane < 16)
+      copy16_async_untracked(src, 256u * (lane >> 3) + 16u * (lane & 7), buf + 2 * TL::kBytes + 256 * wave);
   };
   auto body = [&](int n, const char* cur, char* nxt) {
     const int64_t qt = kt + n;
     if (n + 1 < count) fill(qt + 1, nxt);
     const char* Qs = cur;
     const char* Ds = cur + TL::kBytes;
-    const f32x4_t* vec = reinterpret_cast<const f32x4_t*>(cur + 2 * TL::kBytes);  // {b, D, b, D}
+    // [32 biases, 32 -D] of queries 0-31, then of queries 32-63; the dP products start from -D
+    // of their queries, so they leave dP - D
+    const float* vec = reinterpret_cast<const float*>(cur + 2 * TL::kBytes);
     const bool diagonal = qt == kt, lower_edge = qt == kt + p.m;
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
+    for (int qh = 0; qh < 2; ++qh) pacc[qh] = *reinterpret_cast<const f32x16_t*>(vec + 64 * qh + 32 + 16 * hl);
+#pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       sacc[qh] = zero16();
-      pacc[qh] = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         sacc[qh] = mma(off.kfrag(Qs, qh, s), kf[s], sacc[qh]);
@@ -1426,18 +1432,15 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
       Frag<T> pf[2], zf[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int q0 = 32 * qh + 16 * hl + 8 * half;
-        f32x4_t be[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) be[i] = vec[q0 / 2 + i];
+        const f32x4_t* bq = reinterpret_cast<const f32x4_t*>(vec + 64 * qh + 16 * hl + 8 * half);
+        const f32x4_t b0 = bq[0], b1 = bq[1];
         float xp[8], xz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const float bias_q = be[e >> 1][2 * (e & 1)], d_q = be[e >> 1][2 * (e & 1) + 1];
-          const float pw = fast_exp2(__builtin_fmaf(sacc[qh][r], c2, bias_q));
+          const float pw = fast_exp2(__builtin_fmaf(sacc[qh][r], c2, e < 4 ? b0[e] : b1[e - 4]));
           xp[e] = pw;
-          xz[e] = pw * (pacc[qh][r] - d_q);
+          xz[e] = pw * pacc[qh][r];
         }
         pf[half].set(xp);
         zf[half].set(xz);
@@ -2285,7 +2288,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd2_kernel(AttendParams p) {
 // sum is <dO, o_gca>, so the window's D = <dO, o_window> = <dO, o> - sum_k w_k e_k comes from the
 // stored fused output o without the window's own output.  Then the window's key tiles, as in
 // sw_bwd_query_kernel, add dS K with dS = P (dP - D).  The window's key-major pass reads the
-// {-lse_sw log2 e, D} pairs written at the end.
+// biases -lse_sw log2 e and the -D written at the end.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams p) {
   // the split-list counters of the key-major pass that follows start at zero
@@ -2459,7 +2462,7 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
     for (int a = 0; a < 4; ++a)
       store4(dq + 32 * dt + 8 * a + 4 * hl, sc * dqacc[dt][4 * a], sc * dqacc[dt][4 * a + 1],
              sc * dqacc[dt][4 * a + 2], sc * dqacc[dt][4 * a + 3]);
-  if (hl == 0) reinterpret_cast<f32x2_t*>(p.sw_stats)[my_row] = f32x2_t{bias_sw, d_all - d_gca};
+  p.sw_stats[2 * qrow0 + 64 * hl + my_q] = hl ? -(d_all - d_gca) : bias_sw;  // as the window pass
   __syncthreads();
   if (row >= 0 && tid < p.K) {
     const int64_t o = (((static_cast<int64_t>(c.g) * p.B + c.b) * p.n_q + row) * p.H + c.h) * p.K + tid;

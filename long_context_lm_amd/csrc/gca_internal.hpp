@@ -76,7 +76,8 @@ struct AttendParams {
   const void* k_sw;     // [B, H, n_q * 64, 64] the window's keys and values
   const void* v_sw;
   float* lse_sw;        // forward output / backward input [B, H, n_q * 64] (may be null in the forward)
-  float* sw_stats;      // backward: [B, H, n_q * 64, 2] {-lse_sw log2 e, D_sw} for the window's key pass
+  float* sw_stats;      // backward: [B, H, n_q][2][64] per query tile: 64 biases -lse_sw log2 e,
+                        // then the 64 negated D_sw, for the window's key pass
   int32_t m;            // window in chunks (W = 64 m); 0 = no window
   int32_t entry_decoded;  // inverse index entries for the key-major pass (see pairs)
   int32_t causal_rows;  // inverse index: 1 = list only rows whose global chunk lies after the key
@@ -122,7 +123,8 @@ struct FetchParams {
 
 // Sliding-window attention over one sequence of n_c chunks: q, k, v, o, dout, dq, dk, dv are
 // [B, H, n_c * 64, 64]; lse [B, H, n_c * 64] (natural log-sum-exp of attn_scale q.k over the window);
-// stats [B, H, n_c * 64, 2] {-lse log2 e, D = <dout, o>} for the key-major pass.
+// stats [B, H, n_c][2][64] per query tile: 64 biases -lse log2 e, then the 64 negated
+// D = <dout, o>, for the key-major pass.
 struct SwParams {
   const void* q;
   const void* k;
