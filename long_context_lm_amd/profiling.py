@@ -239,10 +239,12 @@ def infer_traffic(dir_fetch: str, dir_write: str, out_md: str, commands) -> None
         fh.write("\n".join(lines) + "\n")
 
 
-def _per_kernel(directory: str, counter: str):
-    """Counter values per kernel, in dispatch order.  A kernel that also runs at other launch shapes
-    later in the run (the forward-only workload, the context-length sweep) keeps only the dispatches
-    with the grid of its first one: the training step, which bench.py runs first."""
+def _per_kernel(directory: str, counter: str, warmup: int, steps: int):
+    """Counter values per kernel, in dispatch order, of the timed training steps: dispatches
+    [warmup, warmup + steps) of each kernel at the grid of its first dispatch (bench.py runs the
+    training step first, one launch of each kernel per step).  Later runs at the same grid (the
+    skewed-retrieval steps, whose hub lists change the key-major work) and at other launch shapes
+    (the forward-only workload, the context-length sweep) are left out."""
     rows = []
     for r in _rows(directory, "counter_collection.csv"):
         if r["Counter_Name"] != counter:
@@ -256,17 +258,18 @@ def _per_kernel(directory: str, counter: str):
         grid.setdefault(s, g)
         if s == "copy" or g == grid[s]:
             per.setdefault(s, []).append(v)
-    return per
+    return {s: (v if s == "copy" else v[warmup:warmup + steps]) for s, v in per.items()}
 
 
-def traffic(dir_fetch: str, dir_write: str, out_json: str, commands) -> None:
-    fetch = _per_kernel(dir_fetch, "FETCH_SIZE")
-    write = _per_kernel(dir_write, "WRITE_SIZE")
+def traffic(dir_fetch: str, dir_write: str, out_json: str, commands, warmup: int = 1, steps: int = 2) -> None:
+    fetch = _per_kernel(dir_fetch, "FETCH_SIZE", warmup, steps)
+    write = _per_kernel(dir_write, "WRITE_SIZE", warmup, steps)
     # the calibration copy reads and writes COPY_BYTES
     f_scale = _copy_calibration(dir_fetch, "FETCH_SIZE")
     w_scale = _copy_calibration(dir_write, "WRITE_SIZE")
     out = {"source_hash": source_hash(), "fetch_bytes_per_kib": f_scale, "write_bytes_per_kib": w_scale,
-           "copy_bytes": COPY_BYTES, "commands": commands, "kernels": {}}
+           "copy_bytes": COPY_BYTES, "commands": commands,
+           "dispatches": f"{warmup}..{warmup + steps - 1} of each kernel (the timed training steps)", "kernels": {}}
     for k in SHORT:
         if k in fetch and k in write:
             fk = sum(fetch[k]) / len(fetch[k])
