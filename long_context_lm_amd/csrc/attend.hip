@@ -59,36 +59,57 @@ struct SlotTable {
   int n;
 };
 
-__device__ void build_slot_table(SlotTable& st, const AttendParams& p, int g, int b, int64_t row) {
-  st.n = 0;
-  st.valid_mask = 0;
-  for (int k = 0; k < kMaxTopk; ++k) st.w_all[k] = 0.f;
-  if (row < 0) return;
+struct WaveSlots {
+  int32_t j;        // lane k: chunk of slot k
+  float w;          // lane k: fusion weight of slot k (0 if invalid)
+  uint32_t valid;   // bit k: slot k valid
+};
+
+// Slots of one retrieval row, computed lane-parallel by one wave: lanes < K load the row's index
+// and score together (one memory round trip), the maximum over the valid slots is a butterfly
+// (exact, so its order does not matter), and the exponentials are summed in slot order.
+__device__ __forceinline__ WaveSlots wave_slots(const AttendParams& p, int g, int b, int64_t row) {
+  const int lane = threadIdx.x & 63;
+  WaveSlots ws{-1, 0.f, 0u};
+  if (row < 0) return ws;
   const int64_t base = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K;
-  const int32_t* ir = p.idx + base;
-  const float* sr = p.score + base;
-  float mx = -__builtin_inff();
-  for (int k = 0; k < p.K; ++k) {
-    const int32_t j = ir[k];
-    if (j >= 0 && j < p.n_kv) {
-      st.valid_mask |= 1u << k;
-      mx = fmaxf(mx, sr[k]);
+  float sc = -__builtin_inff();
+  if (lane < p.K) {
+    ws.j = p.idx[base + lane];
+    sc = p.score[base + lane];
+  }
+  const bool v = lane < p.K && ws.j >= 0 && ws.j < p.n_kv;
+  ws.valid = static_cast<uint32_t>(__ballot(v));
+  float mx = v ? sc : -__builtin_inff();
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+  mx = __shfl(mx, 0, 64);
+  const float e = v ? expf(sc - mx) : 0.f;
+  float sum = 0.f;
+  for (int k = 0; k < p.K; ++k)
+    if ((ws.valid >> k) & 1u) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), k));
+  ws.w = v ? e / sum : 0.f;
+  return ws;
+}
+
+// The slot table of one retrieval row in LDS, filled by every lane of one wave from wave_slots:
+// valid slot k goes to position popcount(valid below k), so the table keeps slot order.  The
+// caller publishes it with a barrier.
+__device__ __forceinline__ void fill_slot_table(SlotTable& st, const AttendParams& p, int g, int b, int64_t row) {
+  const int lane = threadIdx.x & 63;
+  const WaveSlots ws = wave_slots(p, g, b, row);
+  if (lane < kMaxTopk) {
+    st.w_all[lane] = ws.w;
+    if ((ws.valid >> lane) & 1u) {
+      const int pos = __popc(ws.valid & ((1u << lane) - 1u));
+      st.j[pos] = ws.j;
+      st.slot[pos] = lane;
+      st.w[pos] = ws.w;
     }
   }
-  float sum = 0.f;
-  for (int k = 0; k < p.K; ++k) {
-    if (!((st.valid_mask >> k) & 1u)) continue;
-    const float e = expf(sr[k] - mx);
-    st.w_all[k] = e;
-    sum += e;
-  }
-  for (int k = 0; k < p.K; ++k) {
-    if (!((st.valid_mask >> k) & 1u)) continue;
-    st.w_all[k] = st.w_all[k] / sum;
-    st.j[st.n] = ir[k];
-    st.slot[st.n] = k;
-    st.w[st.n] = st.w_all[k];
-    ++st.n;
+  if (lane == 0) {
+    st.n = __popc(ws.valid);
+    st.valid_mask = ws.valid;
   }
 }
 
@@ -100,15 +121,18 @@ struct QTileCoord {
 
 // Group fastest, then query chunk: both groups' tiles of one (batch row, head) and chunk run side
 // by side and share each K/V tile while it is in L2.
+// The grid has G B H n_q < 2^31 blocks (checked on the host), so 32-bit divisions suffice.
 __device__ __forceinline__ QTileCoord query_tile_coord(const AttendParams& p) {
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const uint32_t lid = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const uint32_t G = static_cast<uint32_t>(p.G), H = static_cast<uint32_t>(p.H);
+  const uint32_t nq = static_cast<uint32_t>(p.n_q);
   QTileCoord c;
-  c.g = static_cast<int>(lid % p.G);
-  int64_t rest = lid / p.G;
-  c.t = rest % p.n_q;
-  rest /= p.n_q;
-  c.h = static_cast<int>(rest % p.H);
-  c.b = static_cast<int>(rest / p.H);
+  uint32_t rest = lid / G;
+  c.g = static_cast<int>(lid - rest * G);
+  const uint32_t bh = rest / nq;
+  c.t = rest - bh * nq;
+  c.b = static_cast<int>(bh / H);
+  c.h = static_cast<int>(bh - static_cast<uint32_t>(c.b) * H);
   c.gbh = (static_cast<int64_t>(c.g) * p.B + c.b) * p.H + c.h;
   return c;
 }
@@ -269,11 +293,11 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
   const int64_t qrow0 = c.gbh * Lq + c.t * kChunk;
   const int my_q = 32 * wave + li;
 
-  if (tid == 0) build_slot_table(st, p, c.g, c.b, c.t - p.shift);
   Frag<T> qf[4];
   const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s].load(q + 16 * s + 8 * hl);
+  if (wave == 0) fill_slot_table(st, p, c.g, c.b, c.t - p.shift);  // its loads beside the query's
   Off off;
   off.init(wave);
   __syncthreads();
@@ -353,38 +377,6 @@ __global__ __launch_bounds__(kThreads) void attend_fwd_kernel(AttendParams p) {
 // workgroup needs no barriers.  The slot list lives in registers (lane k < K holds slot k).  The
 // same one-buffer pipeline as above: K(next) is copied in once K(n) is in registers, V(next)
 // once V(n) is, each wait counted in vector memory operations (in issue order).
-struct WaveSlots {
-  int32_t j;        // lane k: chunk of slot k
-  float w;          // lane k: fusion weight of slot k (0 if invalid)
-  uint32_t valid;   // bit k: slot k valid
-};
-
-// Fusion weights of one retrieval row, as build_slot_table computes them (maximum over the
-// valid slots, exp, then the sum in slot order).
-__device__ __forceinline__ WaveSlots wave_slots(const AttendParams& p, int g, int b, int64_t row) {
-  const int lane = threadIdx.x & 63;
-  WaveSlots ws{-1, 0.f, 0u};
-  if (row < 0) return ws;
-  const int64_t base = ((static_cast<int64_t>(g) * p.B + b) * p.n_q + row) * p.K;
-  float sc = -__builtin_inff();
-  if (lane < p.K) {
-    ws.j = p.idx[base + lane];
-    sc = p.score[base + lane];
-  }
-  const bool v = lane < p.K && ws.j >= 0 && ws.j < p.n_kv;
-  ws.valid = static_cast<uint32_t>(__ballot(v));
-  float mx = v ? sc : -__builtin_inff();
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-  mx = __shfl(mx, 0, 64);
-  const float e = v ? expf(sc - mx) : 0.f;
-  float sum = 0.f;
-  for (int k = 0; k < p.K; ++k)
-    if ((ws.valid >> k) & 1u) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), k));
-  ws.w = v ? e / sum : 0.f;
-  return ws;
-}
-
 template <bool kLse>
 __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
   using T = bf16_t;
@@ -674,6 +666,16 @@ __global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(Atte
 // sacc[qh][tt][r] = S[query 32 qh + li][key 32 tt + 16 hl + r], so the masks are per-register
 // comparisons.  Masked scores are -inf; a query whose keys in a tile are all masked keeps its
 // running maximum (the guards below avoid -inf - -inf).
+// (batch row and head, tile) of a sliding-window workgroup; B H n_c < 2^31 blocks (checked on
+// the host), so 32-bit divisions suffice.
+__device__ __forceinline__ void window_tile(const SwParams& p, int64_t& bh, int64_t& t) {
+  const uint32_t lid = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const uint32_t n = static_cast<uint32_t>(p.n_c);
+  const uint32_t q = lid / n;
+  bh = q;
+  t = lid - q * n;
+}
+
 __device__ __forceinline__ void sw_mask(f32x16_t (&sacc)[2][2], bool lower_edge, bool diagonal) {
   const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
 #pragma unroll
@@ -714,9 +716,8 @@ __global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
   __shared__ __align__(1024) char Vs[TL::kBytes];
 
   const int lane = threadIdx.x, li = lane & 31, hl = lane >> 5;
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t t = lid % p.n_c;
-  const int64_t bh = lid / p.n_c;
+  int64_t bh, t;
+  window_tile(p, bh, t);
   const int64_t row0 = bh * p.n_c * kChunk;  // first token of this (batch row, head)
   const int64_t qrow0 = row0 + t * kChunk;
 
@@ -857,9 +858,8 @@ __global__ __launch_bounds__(kThreads) void sw_fwd2_kernel(SwParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t t = lid % p.n_c;
-  const int64_t bh = lid / p.n_c;
+  int64_t bh, t;
+  window_tile(p, bh, t);
   const int64_t row0 = bh * p.n_c * kChunk;
   const int64_t qrow0 = row0 + t * kChunk;
   const int my_q = 32 * wave + li;
@@ -1085,7 +1085,6 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
   const int my_q = 32 * wave + li;
   const int64_t row = c.t - p.shift;
 
-  if (tid == 0) build_slot_table(st, p, c.g, c.b, row);
   if (tid < 2 * kMaxTopk) dw_s[tid / kMaxTopk][tid % kMaxTopk] = 0.f;
   Frag<T> qf[4], df[4];
   const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
@@ -1095,6 +1094,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(AttendParams p) {
     qf[s].load(q + 16 * s + 8 * hl);
     df[s].load(dout + 16 * s + 8 * hl);
   }
+  if (wave == 0) fill_slot_table(st, p, c.g, c.b, row);  // its loads beside the query's and dO's
   Off off;
   off.init(wave);
   __syncthreads();
@@ -1248,9 +1248,8 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t t = lid % p.n_c;
-  const int64_t bh = lid / p.n_c;
+  int64_t bh, t;
+  window_tile(p, bh, t);
   const int64_t row0 = bh * p.n_c * kChunk;
   const int64_t qrow0 = row0 + t * kChunk;
   const int my_q = 32 * wave + li;
@@ -1364,9 +1363,8 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t kt = lid % p.n_c;
-  const int64_t bh = lid / p.n_c;
+  int64_t bh, kt;
+  window_tile(p, bh, kt);
   const int64_t row0 = bh * p.n_c * kChunk;
   const int my_u = 32 * wave + li;
   const int64_t krow = row0 + kt * kChunk + my_u;
@@ -1517,8 +1515,9 @@ __device__ __forceinline__ void key_walk(const AttendParams& p, int64_t bh, int6
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
-  const int h = static_cast<int>(bh % p.H);
-  const int b = static_cast<int>(bh / p.H);
+  const uint32_t H = static_cast<uint32_t>(p.H);
+  const int b = static_cast<int>(static_cast<uint32_t>(bh) / H);  // bh < B H < 2^31
+  const int h = static_cast<int>(static_cast<uint32_t>(bh) - static_cast<uint32_t>(b) * H);
   const int my_u = 32 * wave + li;
 
   const int64_t krow = (bh * p.n_kv + j) * kChunk + my_u;
@@ -1668,10 +1667,13 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
   __shared__ i32x2_t ents[kEntRound];
   const int my_u = 32 * (threadIdx.x >> 6) + (threadIdx.x & 31);
-  const int64_t lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t j = lid % p.n_kv;
-  const int64_t bh = lid / p.n_kv;
-  const int32_t count = p.counts[(bh / p.H) * p.n_kv + j];
+  // B H n_kv < 2^31 blocks (checked on the host): 32-bit divisions
+  const uint32_t lid = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const uint32_t nkv = static_cast<uint32_t>(p.n_kv);
+  const uint32_t bh32 = lid / nkv;
+  const int64_t j = lid - bh32 * nkv;
+  const int64_t bh = bh32;
+  const int32_t count = p.counts[static_cast<int64_t>(bh32 / static_cast<uint32_t>(p.H)) * p.n_kv + j];
   // a split list is bwd_key_split_kernel's work: walk nothing and write nothing (not an early
   // return, which would hold the walk's K/V loads back behind the count's)
   const bool split = p.long_ctl != nullptr && count > kSegEntries;
@@ -2150,11 +2152,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd2_kernel(AttendParams p) {
   const int64_t qrow0 = row0 + c.t * kChunk;
   const int my_q = 32 * wave + li;
 
-  if (tid == 0) build_slot_table(st, p, c.g, c.b, c.t - p.shift);
   Frag<T> qf[4];
   const T* q = static_cast<const T*>(p.q) + (qrow0 + my_q) * kDim;
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s].load(q + 16 * s + 8 * hl);
+  if (wave == 0) fill_slot_table(st, p, c.g, c.b, c.t - p.shift);  // its loads beside the query's
   Off off;
   off.init(wave);
   __syncthreads();
@@ -2312,7 +2314,6 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
   const int64_t my_row = qrow0 + my_q;
   const int64_t row = c.t - p.shift;
 
-  if (tid == 0) build_slot_table(st, p, c.g, c.b, row);
   if (tid < 2 * kMaxTopk) dw_s[tid / kMaxTopk][tid % kMaxTopk] = 0.f;
   Frag<T> qf[4], df[4];
   float dd = 0.f;
@@ -2324,6 +2325,7 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
       df[s].load(static_cast<const T*>(p.dout) + my_row * kDim + 16 * s + 8 * hl);
       of[s].load(static_cast<const T*>(p.o) + my_row * kDim + 16 * s + 8 * hl);
     }
+    if (wave == 0) fill_slot_table(st, p, c.g, c.b, row);  // its loads beside the tiles'
 #pragma unroll
     for (int s = 0; s < 4; ++s) dd += frag_dot(df[s], of[s]);
   }
