@@ -80,10 +80,18 @@ __device__ __forceinline__ WaveSlots wave_slots(const AttendParams& p, int g, in
   }
   const bool v = lane < p.K && ws.j >= 0 && ws.j < p.n_kv;
   ws.valid = static_cast<uint32_t>(__ballot(v));
+  // maximum over lanes 0..15 (K <= 16): four DPP steps inside the 16-lane row (the swaps of
+  // neighbours and of pairs, then the mirrors of each half and of the row), exact in any order
   float mx = v ? sc : -__builtin_inff();
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-  mx = __shfl(mx, 0, 64);
+  auto row_max = [](float x, auto ctrl) {
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, true);
+    return fmaxf(x, __int_as_float(y));
+  };
+  mx = row_max(mx, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  mx = row_max(mx, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  mx = row_max(mx, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  mx = row_max(mx, std::integral_constant<int, 0x140>{});  // row_mirror
+  mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));  // lane 0: slots 0..15
   const float e = v ? expf(sc - mx) : 0.f;
   float sum = 0.f;
   for (int k = 0; k < p.K; ++k)
@@ -391,7 +399,6 @@ __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
   const int64_t Lq = p.n_q * kChunk;
   const int64_t qrow0 = c.gbh * Lq + c.t * kChunk;
 
-  const WaveSlots sl = wave_slots(p, c.g, c.b, c.t - p.shift);
   Frag<T> qf[2][4];
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
@@ -399,6 +406,8 @@ __global__ __launch_bounds__(64) void attend_fwd_wave_kernel(AttendParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[qh][s].load(q + 16 * s + 8 * hl);
   }
+  // after the query loads, so that one memory round trip covers both
+  const WaveSlots sl = wave_slots(p, c.g, c.b, c.t - p.shift);
   Off off;
   off.init(0);
 
@@ -1927,7 +1936,6 @@ __global__ __launch_bounds__(64) void fused_fwd_kernel(AttendParams p) {
   const int64_t Lq = p.n_q * kChunk;
   const int64_t row0 = (static_cast<int64_t>(c.b) * p.H + c.h) * Lq;  // this (batch row, head)
   const int64_t qrow0 = row0 + c.t * kChunk;
-  const WaveSlots sl = wave_slots(p, c.g, c.b, c.t - p.shift);
   Frag<T> qf[2][4];
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
@@ -1935,6 +1943,8 @@ __global__ __launch_bounds__(64) void fused_fwd_kernel(AttendParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[qh][s].load(q + 16 * s + 8 * hl);
   }
+  // after the query loads, so that one memory round trip covers both
+  const WaveSlots sl = wave_slots(p, c.g, c.b, c.t - p.shift);
   Off off;
   off.init(0);
   // copies address the buffers by their LDS addresses: with the two item loops below, the
