@@ -4,12 +4,12 @@ A hub chunk: when every retrieval row's query landmark shares a direction with o
 that chunk enters the top-k of nearly every row [Notes, Key designs: causal retrieval: the top-k
 runs over all earlier chunks, so one salient chunk can be selected by many rows].  Its key-side
 sums then run over the longest entry lists the inverse retrieval index can hold: here more than
-512 (group, row, slot) entries, so the key-major pass stages its list in more than one round and
-the landmark key pass walks it in more than eight 64-entry pieces.
+512 (group, row, slot) entries, which the landmark key pass walks in more than eight 64-entry
+pieces.
 
 The key-major pass splits a list longer than 128 entries into segments that separate workgroups
-walk, and sums their partials in segment order; the hub's list takes that path, and its result
-must not change from one call to the next.
+walk (here more than four), and sums their partials in segment order; the hub's list takes that
+path, and its result must not change from one call to the next.
 
 Caller-built indices: gca_forward and gca_backward count every slot with 0 <= idx < n_kv, also
 chunks at or after the row's own chunk (a caller's own selection, or the compact buffers of
@@ -81,7 +81,7 @@ def test_hub_chunk_backward_and_landmarks(dtype):
     feeds = r_idx[:, :, : shape.n_q - 1]
     n_bwd, n_lmk = int((feeds == 0).sum()), int((r_idx == 0).sum())
     say(f"  chunk 0 named by {n_bwd} backward entries, {n_lmk} landmark entries")
-    assert n_bwd > 512 and n_lmk > 512, "the hub must need more than one staging round"
+    assert n_bwd > 512 and n_lmk > 512, "the hub list must exceed four segments and eight landmark pieces"
     r_o, r_lse = O.forward(x["q"], x["k"], x["v"], r_idx, r_sc)
     r_g = O.backward(x["q"], x["k"], x["v"], r_idx, r_sc, x["dout"])
     errs = {"o": assert_close("o", I.as_f64(o), r_o, dtype), "lse": lse_compare("lse", lse, r_lse, dtype)}
