@@ -174,12 +174,12 @@ gca_status gca_forward(const gca_problem* problem, const void* q, const void* k,
  * gca_fetch_chunks, is differentiated as the forward used it).
  * q, k, v, idx, score, lse (from gca_forward), dout: inputs; dq, dk, dv, dscore: outputs.
  * dk and dv are accumulated in fp32 in a fixed order and rounded once to dtype.  A chunk
- * retrieved by more than 128 (group, row) entries has its sums split into segments of 128
+ * retrieved by more than 128 (group, row) entries has its sums split into segments of 64
  * entries, each summed by its own workgroup; the segments' fp32 partials are then added in
  * segment order, so the result is the same on every run.
  * ws: >= gca_workspace_size(BACKWARD); it holds, among others, an inverse retrieval index of
  * B * n_kv * G * n_q int32 entries and room for the split chunks' partials (up to
- * B * (ceil(L / 128) + floor(L / 129)) segments of H * 32 KiB, L = G * n_q * topk).  Contents
+ * B * (ceil(L / 64) + floor(L / 129)) segments of H * 32 KiB, L = G * n_q * topk).  Contents
  * need no setup.
  */
 gca_status gca_backward(const gca_problem* problem, const void* q, const void* k, const void* v,

@@ -43,7 +43,6 @@ namespace {
 constexpr int kThreads = 128;  // two waves
 constexpr int kWaves = 2;
 constexpr int kEntRound = 512;  // inverse-index entries staged in LDS at a time
-constexpr int kSegEntries = 128;  // longest list one key-major workgroup walks when lists are split
 constexpr int64_t kWideMaxTiles = 256;  // query tiles up to which the forward runs one slot per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2f = 0.6931471805599453f;
@@ -177,9 +176,12 @@ struct TileOffsets {
   static constexpr int kCopies = Tile<T>::kChunks / 64 / kWaves;
   uint32_t k[4], v[8], cp[kCopies];
 
-  __device__ __forceinline__ void init(int wave) {
+  __device__ __forceinline__ void init(int wave) { init(wave, static_cast<int>(threadIdx.x)); }
+  // the same with the thread index given (an opaque copy keeps the offsets from being hoisted
+  // out of a loop of walks, where they would stay live across the loop)
+  __device__ __forceinline__ void init(int wave, int tid) {
     using TL = Tile<T>;
-    const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
+    const int lane = tid & 63, li = lane & 31, hl = lane >> 5;
 #pragma unroll
     for (int n = 0; n < kCopies; ++n) {
       const int pos = (n * kWaves + wave) * 64 + lane;
@@ -1518,10 +1520,10 @@ __device__ __forceinline__ PairRef decode_pair(const i32x2_t ent) {
 template <typename T>
 __device__ __forceinline__ void key_walk(const AttendParams& p, int64_t bh, int64_t j, int32_t e0, int32_t e1,
                                          char* buf0, char* buf1, i32x2_t* ents, f32x16_t (&dkacc)[2],
-                                         f32x16_t (&dvacc)[2]) {
+                                         f32x16_t (&dvacc)[2], int tid) {
   using TL = Tile<T>;
   using Off = TileOffsets<T, kWaves>;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hl = lane >> 5;
   const uint32_t H = static_cast<uint32_t>(p.H);
@@ -1539,7 +1541,7 @@ __device__ __forceinline__ void key_walk(const AttendParams& p, int64_t bh, int6
     vf[s].load(vp + 16 * s + 8 * hl);
   }
   Off off;
-  off.init(wave);
+  off.init(wave, tid);
   dkacc[0] = dkacc[1] = dvacc[0] = dvacc[1] = zero16();
   const float c2 = p.attn_scale * kLog2e;
   const int64_t Lq = p.n_q * kChunk;
@@ -1666,7 +1668,7 @@ __device__ __forceinline__ void store_key_grads(D* dk, D* dv, float sc, const f3
 }
 
 // One workgroup of two waves per (batch row, head, key chunk) walks the chunk's entries and
-// writes its dK, dV.  With long lists split (long_ctl set), a chunk of more than kSegEntries
+// writes its dK, dV.  With long lists split (long_ctl set), a chunk of more than kSplitMin
 // entries is left to bwd_key_split_kernel, which runs just before.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
@@ -1685,9 +1687,9 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   const int32_t count = p.counts[static_cast<int64_t>(bh32 / static_cast<uint32_t>(p.H)) * p.n_kv + j];
   // a split list is bwd_key_split_kernel's work: walk nothing and write nothing (not an early
   // return, which would hold the walk's K/V loads back behind the count's)
-  const bool split = p.long_ctl != nullptr && count > kSegEntries;
+  const bool split = p.long_ctl != nullptr && count > kSplitMin;
   f32x16_t dkacc[2], dvacc[2];
-  key_walk<T>(p, bh, j, 0, split ? 0 : count, buf0, buf1, ents, dkacc, dvacc);
+  key_walk<T>(p, bh, j, 0, split ? 0 : count, buf0, buf1, ents, dkacc, dvacc, static_cast<int>(threadIdx.x));
   if (split) return;
   const int64_t krow = (bh * p.n_kv + j) * kChunk + my_u;
   store_key_grads(static_cast<T*>(p.dk) + krow * kDim, static_cast<T*>(p.dv) + krow * kDim, p.attn_scale, dkacc,
@@ -1722,8 +1724,13 @@ __global__ __launch_bounds__(kThreads) void bwd_key_split_kernel(AttendParams p)
     const int32_t e0 = (q - __builtin_amdgcn_readfirstlane(ent[3])) * kSegEntries;
     const int32_t e1 = count - e0 < kSegEntries ? count : e0 + kSegEntries;
     if (e0 < 0 || e0 >= e1) return;
+    // the thread index, opaque in every item: the walk's per-lane set-up is then recomputed for
+    // each walk instead of hoisted out of the loop and held live across it (which costs the
+    // second wave per SIMD)
+    int tid = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid));
     f32x16_t dkacc[2], dvacc[2];
-    key_walk<T>(p, static_cast<int64_t>(b) * p.H + h, j, e0, e1, buf0, buf1, ents, dkacc, dvacc);
+    key_walk<T>(p, static_cast<int64_t>(b) * p.H + h, j, e0, e1, buf0, buf1, ents, dkacc, dvacc, tid);
     float* part = p.long_part + f * (2 * kChunk * kDim) + my_u * kDim;
     store_key_grads(part, part + kChunk * kDim, 1.f, dkacc, dvacc);
   }
@@ -1841,11 +1848,11 @@ __global__ __launch_bounds__(kIdxThreads) void inverse_index_kernel(AttendParams
   if (tid < 64 && j < p.n_kv) {
     const int32_t c = total[tid];
     p.counts[static_cast<int64_t>(b) * p.n_kv + j] = c;
-    // A list longer than kSegEntries is split for the key-major pass: one 64-bit atomic takes its
+    // A list longer than kSplitMin is split for the key-major pass: one 64-bit atomic takes its
     // place in the list of long chunks (high word) and its segment slots (low word), so the
     // list stays in slot order.  The order of the chunks in it varies from run to run; what is
     // computed for each chunk and segment does not.
-    if (p.long_ctl != nullptr && c > kSegEntries) {
+    if (p.long_ctl != nullptr && c > kSplitMin) {
       const int32_t nseg = (c + kSegEntries - 1) / kSegEntries;
       const unsigned long long old =
           atomicAdd(reinterpret_cast<unsigned long long*>(p.long_ctl), (1ull << 32) | static_cast<unsigned long long>(nseg));

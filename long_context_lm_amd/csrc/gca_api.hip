@@ -99,8 +99,9 @@ gca_status validate_problem(const gca_problem* p) {
   if (p->n_kv_chunks > 0 && static_cast<int64_t>(p->B) * p->H > big / p->n_kv_chunks) return GCA_ERR_UNSUPPORTED;
   // (group, row, slot) codes of the inverse index travel as int32
   if (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk > big) return GCA_ERR_UNSUPPORTED;
-  // so do the split lists' segment slots (at most B (G n_q K / 64 + 2) of them)
-  if (static_cast<int64_t>(p->B) * (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk / 64 + 2) > big)
+  // so do the split lists' segment slots: at most B (ceil(L / kSegEntries) + L / (kSplitMin + 1)),
+  // L = G n_q K, which is below B (L / 32 + 2)
+  if (static_cast<int64_t>(p->B) * (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk / 32 + 2) > big)
     return GCA_ERR_UNSUPPORTED;
   return GCA_OK;
 }
@@ -153,10 +154,6 @@ LandmarkLayout plan_landmark(const gca_problem* p) {
   return l;
 }
 
-// Lists longer than this many entries are split over several key-major workgroups (the
-// kernels' kSegEntries).
-constexpr int64_t kSegEntries = 128;
-
 struct BackwardLayout {
   size_t delta, dw_part, wts, pairs, counts, long_ctl, long_list, long_seg, long_part, total;
   int64_t long_cap, seg_cap;  // 0: no list can be long, nothing is split
@@ -179,12 +176,12 @@ BackwardLayout plan_backward(const gca_problem* p) {
   l.counts = off;
   off += align_up(B * nkv * sizeof(int32_t));
   // Split lists.  A batch row holds at most L = G n_q K entries (each retrieval row names at most
-  // K chunks), so at most floor(L / (E + 1)) of its chunks exceed E = kSegEntries entries, and
-  // their segments number at most ceil(L / E) + that many.
+  // K chunks), so at most floor(L / (T + 1)) of its chunks exceed T = kSplitMin entries, and their
+  // segments of E = kSegEntries number at most ceil(L / E) + that many.
   const int64_t L = static_cast<int64_t>(G * nq * K);
-  if (nkv > 0 && L > kSegEntries) {
-    l.long_cap = static_cast<int64_t>(B) * (L / (kSegEntries + 1));
-    l.seg_cap = static_cast<int64_t>(B) * ((L + kSegEntries - 1) / kSegEntries + L / (kSegEntries + 1));
+  if (nkv > 0 && L > kSplitMin) {
+    l.long_cap = static_cast<int64_t>(B) * (L / (kSplitMin + 1));
+    l.seg_cap = static_cast<int64_t>(B) * ((L + kSegEntries - 1) / kSegEntries + L / (kSplitMin + 1));
     l.long_ctl = off;
     off += align_up(sizeof(uint64_t));
     l.long_list = off;
@@ -209,7 +206,7 @@ void set_long_lists(AttendParams& a, const BackwardLayout& L, char* w, bool any)
   a.long_cap = static_cast<int32_t>(L.long_cap);
   a.seg_cap = static_cast<int32_t>(L.seg_cap);
   const int64_t items = L.seg_cap * a.H;  // the most segment walks a call can have
-  a.n_help = static_cast<int32_t>(items < 512 ? items : 512);
+  a.n_help = static_cast<int32_t>(items < 1024 ? items : 1024);
 }
 
 gca_status check_ws(size_t need, const void* ws, size_t ws_bytes) {

@@ -29,6 +29,12 @@ enum KernelId {
 };
 const char* kernel_name(int id);
 
+// Key-major backward: a key chunk's inverse-index list of more than kSplitMin entries is split
+// into segments of at most kSegEntries entries that bwd_key_split_kernel walks in parallel (the
+// plain pass then walks at most kSplitMin entries per chunk).
+constexpr int kSplitMin = 128;
+constexpr int kSegEntries = 64;
+
 struct RetrieveParams {
   const void* lq;
   const void* lk;

@@ -7,9 +7,9 @@ sums then run over the longest entry lists the inverse retrieval index can hold:
 512 (group, row, slot) entries, which the landmark key pass walks in more than eight 64-entry
 pieces.
 
-The key-major pass splits a list longer than 128 entries into segments that separate workgroups
-walk (here more than four), and sums their partials in segment order; the hub's list takes that
-path, and its result must not change from one call to the next.
+The key-major pass splits a list longer than 128 entries into segments of 64 that separate
+workgroups walk (here more than eight), and sums their partials in segment order; the hub's list
+takes that path, and its result must not change from one call to the next.
 
 Caller-built indices: gca_forward and gca_backward count every slot with 0 <= idx < n_kv, also
 chunks at or after the row's own chunk (a caller's own selection, or the compact buffers of
@@ -81,7 +81,7 @@ def test_hub_chunk_backward_and_landmarks(dtype):
     feeds = r_idx[:, :, : shape.n_q - 1]
     n_bwd, n_lmk = int((feeds == 0).sum()), int((r_idx == 0).sum())
     say(f"  chunk 0 named by {n_bwd} backward entries, {n_lmk} landmark entries")
-    assert n_bwd > 512 and n_lmk > 512, "the hub list must exceed four segments and eight landmark pieces"
+    assert n_bwd > 512 and n_lmk > 512, "the hub list must exceed eight segments and eight landmark pieces"
     r_o, r_lse = O.forward(x["q"], x["k"], x["v"], r_idx, r_sc)
     r_g = O.backward(x["q"], x["k"], x["v"], r_idx, r_sc, x["dout"])
     errs = {"o": assert_close("o", I.as_f64(o), r_o, dtype), "lse": lse_compare("lse", lse, r_lse, dtype)}
@@ -140,9 +140,9 @@ def test_caller_indices_at_or_after_the_row(dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_split_lists_odd_shapes(dtype):
     """Three groups, three batch rows, K = 16, a history longer than the query chunks, and a hub
-    chunk named by more than 128 entries (G (n_q - 1) = 147): its list is split into two
-    segments, while the other chunks' lists are walked whole.  Against the oracle backward, and
-    a second call must give the same bits."""
+    chunk named by more than 128 entries (G (n_q - 1) = 147): its list is split into three
+    segments of at most 64, while the other chunks' lists are walked whole.  Against the oracle
+    backward, and a second call must give the same bits."""
     shape = I.Shape(B=3, G=3, H=2, n_q=50, n_kv=60, topk=16)
     cfg = config_for(shape, dtype, use_gumbel=True, seed=7)
     say("case split lists", shape, dtype)
@@ -159,7 +159,7 @@ def test_split_lists_odd_shapes(dtype):
     feeds = r_idx[:, :, : shape.n_q - 1]
     longest = max(int((feeds[:, b] == j).sum()) for b in range(shape.B) for j in range(shape.n_kv))
     say(f"  longest list {longest} entries")
-    assert longest > 128, "a list must exceed one segment"
+    assert longest > 128, "a list must be split"
     r_g = O.backward(x["q"], x["k"], x["v"], r_idx, r_sc, x["dout"])
     for name, got, ref, rep in zip(("dq", "dk", "dv", "dscore"), grads, r_g, again):
         assert torch.equal(got, rep), f"{name}: second call differs"
