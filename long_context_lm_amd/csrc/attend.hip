@@ -1906,8 +1906,18 @@ __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
     const f32x4_t* part = reinterpret_cast<const f32x4_t*>(p.long_part + (static_cast<int64_t>(ent[3]) * p.H + h) * kPart);
     const int64_t stride = static_cast<int64_t>(p.H) * kPart / 4;
     for (int e = threadIdx.x; e < kPart / 4; e += 256) {
+      // the segments' loads eight at a time, all in flight, then added in segment order
+      constexpr int kBatch = 8;
       f32x4_t acc = part[e];
-      for (int32_t sg = 1; sg < ent[2]; ++sg) acc += part[sg * stride + e];
+      for (int32_t s0 = 1; s0 < ent[2]; s0 += kBatch) {
+        f32x4_t v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+          if (s0 + b < ent[2]) v[b] = part[(s0 + b) * stride + e];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+          if (s0 + b < ent[2]) acc += v[b];
+      }
       const bool is_v = e >= kPart / 8;
       const float sc = is_v ? 1.f : p.attn_scale;
       T* dst = static_cast<T*>(is_v ? p.dv : p.dk) + tile + 4 * (e & (kPart / 8 - 1));
