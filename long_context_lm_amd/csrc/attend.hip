@@ -1882,7 +1882,18 @@ __global__ __launch_bounds__(256) void score_grad_kernel(AttendParams p) {
     valid = row + p.shift < p.n_q && jj >= 0 && jj < p.n_kv;
     if (valid) {
       w = p.wts[gid * p.K + k];
-      for (int h = 0; h < p.H; ++h) dw += p.dw_part[(gid * p.H + h) * p.K + k];
+      // eight heads' loads in flight at a time, added in head order
+      constexpr int kBatch = 8;
+      const float* dp = p.dw_part + gid * p.H * p.K + k;
+      for (int h0 = 0; h0 < p.H; h0 += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+          if (h0 + b < p.H) v[b] = dp[(h0 + b) * p.K];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+          if (h0 + b < p.H) dw += v[b];
+      }
     }
   }
   float wdw = w * dw;
