@@ -1413,16 +1413,27 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
     // of their queries, so they leave dP - D
     const float* vec = reinterpret_cast<const float*>(cur + 2 * TL::kBytes);
     const bool diagonal = qt == kt, lower_edge = qt == kt + p.m;
+    // every row fragment of the query tile is read before the first product, so the products
+    // wait once for the LDS reads instead of once per product
+    Frag<T> qr[2][4], dr[2][4];
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) pacc[qh] = *reinterpret_cast<const f32x16_t*>(vec + 64 * qh + 32 + 16 * hl);
+    for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        qr[qh][s] = off.kfrag(Qs, qh, s);
+        dr[qh][s] = off.kfrag(Ds, qh, s);
+      }
+      pacc[qh] = *reinterpret_cast<const f32x16_t*>(vec + 64 * qh + 32 + 16 * hl);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       sacc[qh] = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sacc[qh] = mma(off.kfrag(Qs, qh, s), kf[s], sacc[qh]);
-        pacc[qh] = mma(off.kfrag(Ds, qh, s), vf[s], pacc[qh]);
+        sacc[qh] = mma(qr[qh][s], kf[s], sacc[qh]);
+        pacc[qh] = mma(dr[qh][s], vf[s], pacc[qh]);
       }
     }
     if (lower_edge || diagonal) {  // wave-uniform: only the two edge query tiles are masked
