@@ -393,7 +393,7 @@ def skewed_retrieval_timing(shape, dev, bufs, step, iters=10):
     chunk: every query landmark of a (group, batch row) shares a direction with key landmark 0,
     which then enters nearly every row's top-k (about 500 of the 512 (group, row) entries of a
     batch row).  Same q, k, v, dout as the headline step; the step's landmarks are overwritten.
-    The hub's list is split over several key-major workgroups (bwd_key_split)."""
+    The hub's list is split into segments that helper workgroups of the key-major pass walk."""
     import numpy as np
 
     from long_context_lm_amd import inputs as I

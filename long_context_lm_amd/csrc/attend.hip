@@ -1680,7 +1680,12 @@ __device__ __forceinline__ void store_key_grads(D* dk, D* dv, float sc, const f3
 
 // One workgroup of two waves per (batch row, head, key chunk) walks the chunk's entries and
 // writes its dK, dV.  With long lists split (long_ctl set), a chunk of more than kSplitMin
-// entries is left to bwd_key_split_kernel, which runs just before.
+// entries is walked in segments instead: the first n_help workgroups of the launch take the work
+// items f = q * H + h (the walk of segment slot q, at most kSegEntries entries of one long chunk,
+// for head h) in turn and write float partials, which score_grad_kernel sums in segment order;
+// with no long list they end at once.  Both kinds run side by side (they write disjoint outputs
+// and only read the inverse index).  n_help is a multiple of 8, so the other workgroups keep the
+// XCD order of xcd_logical_block.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   using TL = Tile<T>;
@@ -1689,15 +1694,44 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
   __shared__ i32x2_t ents[kEntRound];
   const int my_u = 32 * (threadIdx.x >> 6) + (threadIdx.x & 31);
+  if (static_cast<int32_t>(blockIdx.x) < p.n_help) {
+    const uint64_t ctl = *p.long_ctl;
+    const int32_t n_long = min(static_cast<int32_t>(ctl >> 32), p.long_cap);
+    const int32_t n_seg = min(static_cast<int32_t>(ctl & 0xffffffffu), p.seg_cap);
+    const int64_t items = static_cast<int64_t>(n_seg) * p.H;
+    for (int64_t f = blockIdx.x; f < items; f += p.n_help) {
+      const int32_t q = static_cast<int32_t>(f / p.H);
+      const int h = static_cast<int>(f - static_cast<int64_t>(q) * p.H);
+      const int32_t at = __builtin_amdgcn_readfirstlane(p.long_seg[q]);
+      if (at < 0 || at >= n_long) return;  // never, by the capacities' bound (see inverse_index_kernel)
+      const i32x4_t ent = reinterpret_cast<const i32x4_t*>(p.long_list)[at];  // {b, j, segments, first slot}
+      const int32_t b = __builtin_amdgcn_readfirstlane(ent[0]);
+      const int32_t j = __builtin_amdgcn_readfirstlane(ent[1]);
+      const int32_t count = p.counts[static_cast<int64_t>(b) * p.n_kv + j];
+      const int32_t e0 = (q - __builtin_amdgcn_readfirstlane(ent[3])) * kSegEntries;
+      const int32_t e1 = count - e0 < kSegEntries ? count : e0 + kSegEntries;
+      if (e0 < 0 || e0 >= e1) return;
+      // the thread index, opaque in every item: the walk's per-lane set-up is then recomputed for
+      // each walk instead of hoisted out of the loop and held live across it (which costs the
+      // second wave per SIMD)
+      int tid = static_cast<int>(threadIdx.x);
+      asm volatile("" : "+v"(tid));
+      f32x16_t dkacc[2], dvacc[2];
+      key_walk<T>(p, static_cast<int64_t>(b) * p.H + h, j, e0, e1, buf0, buf1, ents, dkacc, dvacc, tid);
+      float* part = p.long_part + f * (2 * kChunk * kDim) + my_u * kDim;
+      store_key_grads(part, part + kChunk * kDim, 1.f, dkacc, dvacc);
+    }
+    return;
+  }
   // B H n_kv < 2^31 blocks (checked on the host): 32-bit divisions
-  const uint32_t lid = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const uint32_t lid = static_cast<uint32_t>(xcd_logical_block(blockIdx.x - p.n_help, gridDim.x - p.n_help));
   const uint32_t nkv = static_cast<uint32_t>(p.n_kv);
   const uint32_t bh32 = lid / nkv;
   const int64_t j = lid - bh32 * nkv;
   const int64_t bh = bh32;
   const int32_t count = p.counts[static_cast<int64_t>(bh32 / static_cast<uint32_t>(p.H)) * p.n_kv + j];
-  // a split list is bwd_key_split_kernel's work: walk nothing and write nothing (not an early
-  // return, which would hold the walk's K/V loads back behind the count's)
+  // a split list is the helpers' work: walk nothing and write nothing (not an early return,
+  // which would hold the walk's K/V loads back behind the count's)
   const bool split = p.long_ctl != nullptr && count > kSplitMin;
   f32x16_t dkacc[2], dvacc[2];
   key_walk<T>(p, bh, j, 0, split ? 0 : count, buf0, buf1, ents, dkacc, dvacc, static_cast<int>(threadIdx.x));
@@ -1705,46 +1739,6 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(AttendParams p) {
   const int64_t krow = (bh * p.n_kv + j) * kChunk + my_u;
   store_key_grads(static_cast<T*>(p.dk) + krow * kDim, static_cast<T*>(p.dv) + krow * kDim, p.attn_scale, dkacc,
                   dvacc);
-}
-
-// The long lists' segments: work item f = q * H + h is the walk of segment slot q (at most
-// kSegEntries entries of one long chunk) for head h, taken round-robin by the workgroups, and
-// writes a float partial; score_grad_kernel sums each chunk's partials in segment order.  With
-// no long list, every workgroup ends at once.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_key_split_kernel(AttendParams p) {
-  using TL = Tile<T>;
-  constexpr int kVecBytes = kChunk * 8;
-  __shared__ __align__(1024) char buf0[2 * TL::kBytes + kVecBytes];
-  __shared__ __align__(1024) char buf1[2 * TL::kBytes + kVecBytes];
-  __shared__ i32x2_t ents[kEntRound];
-  const int my_u = 32 * (threadIdx.x >> 6) + (threadIdx.x & 31);
-  const uint64_t ctl = *p.long_ctl;
-  const int32_t n_long = min(static_cast<int32_t>(ctl >> 32), p.long_cap);
-  const int32_t n_seg = min(static_cast<int32_t>(ctl & 0xffffffffu), p.seg_cap);
-  const int64_t items = static_cast<int64_t>(n_seg) * p.H;
-  for (int64_t f = blockIdx.x; f < items; f += gridDim.x) {
-    const int32_t q = static_cast<int32_t>(f / p.H);
-    const int h = static_cast<int>(f - static_cast<int64_t>(q) * p.H);
-    const int32_t at = __builtin_amdgcn_readfirstlane(p.long_seg[q]);
-    if (at < 0 || at >= n_long) return;  // never, by the capacities' bound (see inverse_index_kernel)
-    const i32x4_t ent = reinterpret_cast<const i32x4_t*>(p.long_list)[at];  // {b, j, segments, first slot}
-    const int32_t b = __builtin_amdgcn_readfirstlane(ent[0]);
-    const int32_t j = __builtin_amdgcn_readfirstlane(ent[1]);
-    const int32_t count = p.counts[static_cast<int64_t>(b) * p.n_kv + j];
-    const int32_t e0 = (q - __builtin_amdgcn_readfirstlane(ent[3])) * kSegEntries;
-    const int32_t e1 = count - e0 < kSegEntries ? count : e0 + kSegEntries;
-    if (e0 < 0 || e0 >= e1) return;
-    // the thread index, opaque in every item: the walk's per-lane set-up is then recomputed for
-    // each walk instead of hoisted out of the loop and held live across it (which costs the
-    // second wave per SIMD)
-    int tid = static_cast<int>(threadIdx.x);
-    asm volatile("" : "+v"(tid));
-    f32x16_t dkacc[2], dvacc[2];
-    key_walk<T>(p, static_cast<int64_t>(b) * p.H + h, j, e0, e1, buf0, buf1, ents, dkacc, dvacc, tid);
-    float* part = p.long_part + f * (2 * kChunk * kDim) + my_u * kDim;
-    store_key_grads(part, part + kChunk * kDim, 1.f, dkacc, dvacc);
-  }
 }
 
 // ------------------------------------------------------------- inverse retrieval index
@@ -2607,16 +2601,9 @@ hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_key_split(const AttendParams& p, bool f32, hipStream_t s) {
-  if (f32)
-    hipLaunchKernelGGL(bwd_key_split_kernel<float>, dim3(static_cast<uint32_t>(p.n_help)), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(bwd_key_split_kernel<bf16_t>, dim3(static_cast<uint32_t>(p.n_help)), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
-
 hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.n_kv;
+  // the n_help segment walkers first, then one workgroup per (batch row, head, key chunk)
+  const int64_t blocks = (p.long_ctl != nullptr ? p.n_help : 0) + static_cast<int64_t>(p.B) * p.H * p.n_kv;
   if (f32)
     hipLaunchKernelGGL(bwd_key_kernel<float>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p);
   else

@@ -16,8 +16,7 @@ const char* kernel_name(int id) {
   static const char* names[kNumKernels] = {"score_topk", "topk_merge", "attend_fwd",     "inverse_index",
                                            "bwd_query",  "bwd_key",    "score_grad",     "lmk_query_grad",
                                            "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd",
-                                           "sw_bwd_query", "sw_bwd_key", "fused_fwd", "fused_bwd_query",
-                                           "bwd_key_split"};
+                                           "sw_bwd_query", "sw_bwd_key", "fused_fwd", "fused_bwd_query"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 
@@ -96,7 +95,9 @@ gca_status validate_problem(const gca_problem* p) {
   if (p->n_kv_chunks > big || p->q_chunk_base + p->n_q_chunks > big) return GCA_ERR_UNSUPPORTED;
   const int64_t gbh = static_cast<int64_t>(p->G) * p->B * p->H;
   if (p->n_q_chunks > 0 && gbh > big / p->n_q_chunks) return GCA_ERR_UNSUPPORTED;
-  if (p->n_kv_chunks > 0 && static_cast<int64_t>(p->B) * p->H > big / p->n_kv_chunks) return GCA_ERR_UNSUPPORTED;
+  // (the key-major pass launches up to 1024 more workgroups than B H n_kv)
+  if (p->n_kv_chunks > 0 && static_cast<int64_t>(p->B) * p->H > (big - 1024) / p->n_kv_chunks)
+    return GCA_ERR_UNSUPPORTED;
   // (group, row, slot) codes of the inverse index travel as int32
   if (static_cast<int64_t>(p->G) * p->n_q_chunks * p->topk > big) return GCA_ERR_UNSUPPORTED;
   // so do the split lists' segment slots: at most B (ceil(L / kSegEntries) + L / (kSplitMin + 1)),
@@ -206,7 +207,8 @@ void set_long_lists(AttendParams& a, const BackwardLayout& L, char* w, bool any)
   a.long_cap = static_cast<int32_t>(L.long_cap);
   a.seg_cap = static_cast<int32_t>(L.seg_cap);
   const int64_t items = L.seg_cap * a.H;  // the most segment walks a call can have
-  a.n_help = static_cast<int32_t>(items < 1024 ? items : 1024);
+  const int64_t help = items < 1024 ? items : 1024;
+  a.n_help = static_cast<int32_t>((help + 7) / 8 * 8);  // a multiple of 8: see bwd_key_kernel
 }
 
 gca_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
@@ -461,7 +463,6 @@ gca_status gca_backward(const gca_problem* problem, const void* q, const void* k
   // writes zero dk, dv for chunks nobody retrieved) run.
   if (any) GCA_TRY(launch(kBwdQuery, s, [&] { return launch_bwd_query(a, f32, s); }));
   if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
-  if (kv && a.long_ctl) GCA_TRY(launch(kBwdKeySplit, s, [&] { return launch_bwd_key_split(a, f32, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
   if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, f32, s); }));
   return GCA_OK;
@@ -721,7 +722,6 @@ gca_status gca_fused_backward(const gca_problem* problem, int32_t window, const 
     GCA_TRY(launch(kSwBwdKey, s, [&] { return launch_sw_bwd_key(sw, f32, s); }));
   }
   if (kv) GCA_TRY(launch(kInverseIndex, s, [&] { return launch_inverse_index(a, s); }));
-  if (kv && a.long_ctl) GCA_TRY(launch(kBwdKeySplit, s, [&] { return launch_bwd_key_split(a, f32, s); }));
   if (kv) GCA_TRY(launch(kBwdKey, s, [&] { return launch_bwd_key(a, f32, s); }));
   if (any) GCA_TRY(launch(kScoreGrad, s, [&] { return launch_score_grad(a, f32, s); }));
   return GCA_OK;

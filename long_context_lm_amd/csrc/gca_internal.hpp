@@ -24,14 +24,13 @@ enum KernelId {
   kSwBwdKey,
   kFusedFwd,
   kFusedBwdQuery,
-  kBwdKeySplit,
   kNumKernels
 };
 const char* kernel_name(int id);
 
 // Key-major backward: a key chunk's inverse-index list of more than kSplitMin entries is split
-// into segments of at most kSegEntries entries that bwd_key_split_kernel walks in parallel (the
-// plain pass then walks at most kSplitMin entries per chunk).
+// into segments of at most kSegEntries entries that the key-major pass's helper workgroups walk
+// in parallel (its other workgroups then walk at most kSplitMin entries per chunk).
 constexpr int kSplitMin = 128;
 constexpr int kSegEntries = 64;
 
@@ -91,8 +90,8 @@ struct AttendParams {
                         // (the GCA backward, whose other passes count every 0 <= j < n_kv)
   // key-major pass with long lists split (null: no split): {long chunks, segment slots} counter,
   // long chunks [long_cap][4] {b, j, segments, first slot}, the long chunk of each segment slot
-  // [seg_cap], float partials [seg_cap * H][2][64][64]; n_help workgroups walk the segments
-  // (bwd_key_split_kernel)
+  // [seg_cap], float partials [seg_cap * H][2][64][64]; the first n_help (a multiple of 8)
+  // workgroups of the key-major pass walk the segments
   uint64_t* long_ctl;
   int32_t* long_list;
   int32_t* long_seg;
@@ -157,7 +156,6 @@ hipError_t launch_attend_fwd(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_inverse_index(const AttendParams& p, hipStream_t s);
 hipError_t launch_bwd_query(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_bwd_key(const AttendParams& p, bool f32, hipStream_t s);
-hipError_t launch_bwd_key_split(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_score_grad(const AttendParams& p, bool f32, hipStream_t s);
 hipError_t launch_lmk_query_grad(const LandmarkParams& p, bool f32, hipStream_t s);
 hipError_t launch_lmk_key_grad(const LandmarkParams& p, bool f32, hipStream_t s);

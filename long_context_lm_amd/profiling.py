@@ -29,7 +29,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/attend.hip", "csrc/retrieve.hip", "csrc/gca_device.hpp", "csrc/gca_internal.hpp"]
-SHORT = ["score_topk", "topk_merge", "attend_fwd", "inverse_index", "bwd_query", "bwd_key_split", "bwd_key", "score_grad",
+SHORT = ["score_topk", "topk_merge", "attend_fwd", "inverse_index", "bwd_query", "bwd_key", "score_grad",
          "lmk_query_grad", "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd", "sw_bwd_query",
          "sw_bwd_key", "fused_fwd", "fused_bwd_query"]
 COPY_BYTES = 1 << 30
