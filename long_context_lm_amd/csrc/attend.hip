@@ -1527,7 +1527,8 @@ __device__ __forceinline__ PairRef decode_pair(const i32x2_t ent) {
 // each wave owns 32 of the chunk's keys and accumulates their dK (unscaled) and dV over the
 // entries, double-buffered: the next entry's Q and dO tiles and its 64 biases and 64 -e are
 // copied in at the start of the current one.  Every copy has landed and every LDS read is done
-// when it returns, so walks can follow one another in the same workgroup.
+// when it returns, so walks can follow one another in the same workgroup.  tid is the thread
+// index (threadIdx.x, or an opaque copy of it in a loop of walks).
 template <typename T>
 __device__ __forceinline__ void key_walk(const AttendParams& p, int64_t bh, int64_t j, int32_t e0, int32_t e1,
                                          char* buf0, char* buf1, i32x2_t* ents, f32x16_t (&dkacc)[2],

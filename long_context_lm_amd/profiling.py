@@ -28,18 +28,30 @@ import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/attend.hip", "csrc/retrieve.hip", "csrc/gca_device.hpp", "csrc/gca_internal.hpp"]
+KERNEL_SOURCES = ["csrc/attend.hip", "csrc/retrieve.hip", "csrc/landmark.hip", "csrc/fetch.hip", "csrc/gca_api.hip",
+                  "csrc/gca_device.hpp", "csrc/gca_internal.hpp"]
 SHORT = ["score_topk", "topk_merge", "attend_fwd", "inverse_index", "bwd_query", "bwd_key", "score_grad",
          "lmk_query_grad", "lmk_key_grad", "fetch_chunks", "decode_tokens", "sw_fwd", "sw_bwd_query",
          "sw_bwd_key", "fused_fwd", "fused_bwd_query"]
 COPY_BYTES = 1 << 30
 
 
+def code_text(src: str) -> str:
+    """The code of a C++/HIP source: comments removed and whitespace runs collapsed, so that an
+    edit of comments or layout alone leaves it unchanged (the sources hold no string literal with
+    a comment marker in it)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout excluded): profiles taken with
+    another hash describe other kernels."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(HERE, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

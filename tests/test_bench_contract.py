@@ -64,3 +64,19 @@ def test_step_roofline_at_the_16k_training_shape():
     bwd_us = sr["backward"]["flops"] / 2.5e15 * 1e6
     assert abs(fwd_us - 163.6) < 0.1 and abs(bwd_us - 322.8) < 0.1
     assert abs(sr["floor_us"] - (fwd_us + bwd_us)) < 1e-6
+
+
+def test_profile_hash_ignores_comments_but_not_code():
+    """The profiles record a hash of the kernel sources; the bench reports their HBM traffic only
+    while it matches.  Comments and layout do not change the kernels, so they must not change the
+    hash; any code change must."""
+    from long_context_lm_amd import profiling as P
+
+    src = "int f(int a) {  // the sum\n  return a + 1; /* one\n more */\n}\n"
+    assert P.code_text(src) == P.code_text("int f(int a) {\n return a + 1;  // changed note\n}")
+    assert P.code_text(src) != P.code_text("int f(int a) { return a + 2; }")
+    assert "//" not in P.code_text(src) and "/*" not in P.code_text(src)
+    h = P.source_hash()
+    assert len(h) == 16 and h == P.source_hash()
+    for f in P.KERNEL_SOURCES:
+        assert os.path.exists(os.path.join(P.HERE, f)), f
