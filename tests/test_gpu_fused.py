@@ -25,10 +25,13 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _case(shape, dtype, window, seed, scale=1.0, alias=False):
-    say("case fused", shape, dtype, "window", window, "alias", alias)
+def _case(shape, dtype, window, seed, scale=1.0, alias=False, hub=False):
+    say("case fused", shape, dtype, "window", window, "alias", alias, "hub", hub)
     cfg = config_for(shape, dtype, use_gumbel=True, seed=seed)
     host = I.make_inputs(shape, dtype, seed=seed, scale=scale)
+    if hub:
+        lq, lk = I.hub_landmarks(shape, seed)
+        host["lq"], host["lk"] = I.to_dtype(lq, dtype), I.to_dtype(lk, dtype)
     extra = I.make_inputs(shape, dtype, seed=seed + 1000, scale=scale, names=("k", "v"))
     q = host["q"][0]  # [B, H, L, 64]: the layer's queries (one group)
     dout = host["dout"][0]
@@ -82,6 +85,29 @@ def test_fused_with_aliased_keys(dtype):
     shape = I.Shape(B=1, G=1, H=2, n_q=10, n_kv=10, topk=8)
     _, _, _, got, x, ref_sel = _case(shape, dtype, 192, seed=3, alias=True)
     _compare(dtype, got, x, ref_sel, 192)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_hub_chunk_splits_its_list(dtype):
+    """A hub chunk (every query landmark shares the direction of key landmark 0) at n_q = 200, K = 8,
+    window 128: chunk 0 is named by nearly all 199 rows that feed a query chunk, so the fused
+    backward's key-major pass splits its list into segments of 64.  Against the oracle's fused
+    backward, and a second call must give the same bits (the segments' partials are summed in
+    segment order whatever order the helper workgroups take them in)."""
+    shape = I.Shape(B=1, G=1, H=2, n_q=200, n_kv=200, topk=8)
+    cfg, d, (idx, sc), got, x, ref_sel = _case(shape, dtype, 128, seed=23, scale=0.5, hub=True)
+    o, lse_sw, lse, grads = got
+    again = gca.fused_backward(cfg, d["q"], d["k_sw"], d["v_sw"], d["k"], d["v"], idx, sc, o, lse_sw, lse,
+                               d["dout"], 128)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk_sw", "dv_sw", "dk", "dv", "dscore"), grads, again):
+        assert torch.equal(a, b), f"{name}: second call differs"
+    feeds = ref_sel[0][:, :, : shape.n_q - 1]
+    n_hub = int((feeds == 0).sum())
+    say(f"  chunk 0 named by {n_hub} backward entries")
+    assert n_hub > 128, "the hub list must be split"
+    _compare(dtype, got, x, ref_sel, 128)
 
 
 def test_fused_equals_the_two_separate_calls():
