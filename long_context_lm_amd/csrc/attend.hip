@@ -687,32 +687,37 @@ __device__ __forceinline__ void window_tile(const SwParams& p, int64_t& bh, int6
   t = lid - q * n;
 }
 
-__device__ __forceinline__ void sw_mask(f32x16_t (&sacc)[2][2], bool lower_edge, bool diagonal) {
+// Masks the 16 elements of one accumulator run in an edge tile of the window: per lane, the
+// elements r < t keep their value and the others become -inf when lo_keeps, and the other way
+// round otherwise (lo_keeps wave-uniform).  One comparison and one select per element.  t is
+// opaque, so the comparisons are made here on every call: hoisted out of the caller's loop, the
+// lane masks they give outgrow the scalar registers, and the compiler then parks them in vector
+// lanes and turns every select into a branch.
+template <bool kOpaque = true>
+__device__ __forceinline__ void mask_run(f32x16_t& x, int t, bool lo_keeps) {
+  if (kOpaque) asm volatile("" : "+v"(t));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = (r < t) == lo_keeps ? x[r] : -__builtin_inff();
+}
+
+// Edge tiles of a query-major pass (the diagonal tile or, exclusively since W >= 64, the tile at
+// the window's lower edge): sacc[qh][tt][r] = S[query 32 qh + li][key 32 tt + 16 hl + r].  The key
+// lies after the query (masked in the diagonal tile) exactly when r >= t = 32 (qh - tt) + li -
+// 16 hl + 1, and at or before it (masked at the lower edge) when r < t.
+__device__ __forceinline__ void sw_mask(f32x16_t (&sacc)[2][2], bool diagonal) {
   const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * tt + 16 * hl + r, query = 32 * qh + li;
-        const bool out = (lower_edge && key <= query) || (diagonal && key > query);
-        sacc[qh][tt][r] = out ? -__builtin_inff() : sacc[qh][tt][r];
-      }
+    for (int tt = 0; tt < 2; ++tt) mask_run<false>(sacc[qh][tt], 32 * (qh - tt) + li - 16 * hl + 1, diagonal);
 }
 
-__device__ __forceinline__ void sw_mask_keys_major(f32x16_t (&sacc)[2], int query_base, bool lower_edge,
-                                                   bool diagonal) {
-  // query-major accumulators: sacc[tt][r] = S[query query_base + li][key 32 tt + 16 hl + r]
+// The same for query-major accumulators of one 32-query half:
+// sacc[tt][r] = S[query query_base + li][key 32 tt + 16 hl + r].
+__device__ __forceinline__ void sw_mask_keys_major(f32x16_t (&sacc)[2], int query_base, bool diagonal) {
   const int lane = threadIdx.x & 63, li = lane & 31, hl = lane >> 5;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * tt + 16 * hl + r, query = query_base + li;
-      const bool out = (lower_edge && key <= query) || (diagonal && key > query);
-      sacc[tt][r] = out ? -__builtin_inff() : sacc[tt][r];
-    }
+  for (int tt = 0; tt < 2; ++tt) mask_run(sacc[tt], query_base + li - 32 * tt - 16 * hl + 1, diagonal);
 }
 
 // One wave per query tile, as the bf16 GCA forward: K and V tiles stream through single LDS
@@ -780,7 +785,7 @@ __global__ __launch_bounds__(64) void sw_fwd_kernel(SwParams p) {
         for (int s = 0; s < 4; ++s) sacc[qh][tt] = mma(kf[tt][s], qf[qh][s], sacc[qh][tt]);
       }
     const bool lower_edge = kt == t - p.m, diagonal = kt == t;
-    if (lower_edge || diagonal) sw_mask(sacc, lower_edge, diagonal);
+    if (lower_edge || diagonal) sw_mask(sacc, diagonal);
     Frag<T> pf[2][4];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -908,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void sw_fwd2_kernel(SwParams p) {
     barrier_lds_reads_done();  // every wave has read K(kt)
     if (more) off.copy(tile(p.k, kt + 1), Ks, wave);
     const bool lower_edge = kt == t - p.m, diagonal = kt == t;
-    if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+    if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, diagonal);
     float mx = -__builtin_inff();
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -1324,7 +1329,7 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_query_kernel(SwParams p) {
     barrier_lds_reads_done();  // every wave has read V(kt)
     if (more) off.copy(tile(p.v, kt + 1), Vs, wave);
     const bool lower_edge = kt == t - p.m, diagonal = kt == t;
-    if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+    if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, diagonal);
     Frag<T> zf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1437,14 +1442,10 @@ __global__ __launch_bounds__(kThreads) void sw_bwd_key_kernel(SwParams p) {
       }
     }
     if (lower_edge || diagonal) {  // wave-uniform: only the two edge query tiles are masked
+      // sacc[qh][r] = S[query 32 qh + 16 hl + r][key my_u]: the query lies before the key
+      // (masked in the diagonal tile, kept at the lower edge) exactly when r < my_u - 32 qh - 16 hl
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int query = 32 * qh + 16 * hl + r;  // sacc[qh][r] = S[query][key my_u]
-          const bool out = (lower_edge && my_u <= query) || (diagonal && my_u > query);
-          sacc[qh][r] = out ? -__builtin_inff() : sacc[qh][r];
-        }
+      for (int qh = 0; qh < 2; ++qh) mask_run(sacc[qh], my_u - 32 * qh - 16 * hl, lower_edge);
     }
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -2038,7 +2039,7 @@ __global__ __launch_bounds__(64) void fused_fwd_kernel(AttendParams p) {
     }
     const int64_t kt = kt0 + i;
     const bool lower_edge = kt == c.t - p.m, diagonal = kt == c.t;
-    if (lower_edge || diagonal) sw_mask(sacc, lower_edge, diagonal);
+    if (lower_edge || diagonal) sw_mask(sacc, diagonal);
     Frag<T> vf[4][2];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -2246,7 +2247,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd2_kernel(AttendParams p) {
     if (is_sw) {
       const int64_t kt = kt0 + i;
       const bool lower_edge = kt == c.t - p.m, diagonal = kt == c.t;
-      if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+      if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, diagonal);
       float mx = -__builtin_inff();
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
@@ -2466,7 +2467,7 @@ __global__ __launch_bounds__(kThreads) void fused_bwd_query_kernel(AttendParams 
       // the window's key tile kt: P = exp(z - lse_sw), dS = P (dP - D), masked on the edge tiles
       const int64_t kt = kt0 + (i - nslots);
       const bool lower_edge = kt == c.t - p.m, diagonal = kt == c.t;
-      if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, lower_edge, diagonal);
+      if (lower_edge || diagonal) sw_mask_keys_major(sacc, 32 * wave, diagonal);
       const float d_sw = d_all - d_gca;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
