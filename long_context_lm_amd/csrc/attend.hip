@@ -524,27 +524,46 @@ struct Wide {
   static constexpr int kThreads = 64 * kW;
 };
 
-// Fusion weight of slot k of one retrieval row, computed by every lane of the wave (lanes < K
-// read the row's scores; the softmax over valid slots is reduced across the wave).
-__device__ __forceinline__ float wave_slot_weight(const AttendParams& p, int64_t rowbase, int lane, int k,
-                                                  bool& valid_k, int32_t& j_k, uint32_t& valid_mask) {
-  int32_t j = -1;
-  float sc = -__builtin_inff();
-  if (lane < p.K) {
-    j = p.idx[rowbase + lane];
-    sc = p.score[rowbase + lane];
+// The slots of one retrieval row: lane s < K holds slot s's chunk and score (-1 and -inf on the
+// other lanes, and on every lane without a row).  One round trip for both.
+struct RowSlots {
+  int32_t j;
+  float sc;
+};
+
+__device__ __forceinline__ RowSlots load_row_slots(const AttendParams& p, int64_t rowbase, int lane, bool has_row) {
+  RowSlots r{-1, -__builtin_inff()};
+  if (has_row && lane < p.K) {
+    r.j = p.idx[rowbase + lane];
+    r.sc = p.score[rowbase + lane];
   }
-  const bool v = j >= 0 && j < p.n_kv;
+  // both have landed here: a later wait for them would be placed after the caller's untracked
+  // tile copies and wait for those as well
+  asm volatile("" ::"v"(r.j), "v"(r.sc));
+  return r;
+}
+
+// Chunk of slot k (k wave-uniform) and whether it is valid.
+__device__ __forceinline__ int32_t row_slot_chunk(const AttendParams& p, const RowSlots& r, int k, bool& valid) {
+  const int32_t j = __builtin_amdgcn_readlane(r.j, k);
+  valid = j >= 0 && j < p.n_kv;
+  return j;
+}
+
+// Fusion weight of slot k of the row, computed by every lane of the wave (the softmax over the
+// valid slots is reduced across lanes 0..15), and the row's valid-slot mask.  Callers issue the
+// slot's tile loads first, so that this runs while they are in flight.
+__device__ __forceinline__ float row_slot_weight(const AttendParams& p, const RowSlots& r, int k,
+                                                 uint32_t& valid_mask) {
+  const bool v = r.j >= 0 && r.j < p.n_kv;
   valid_mask = static_cast<uint32_t>(__ballot(v));
-  float mx = v ? sc : -__builtin_inff();
+  float mx = v ? r.sc : -__builtin_inff();
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));  // K <= 16 lanes
-  const float e = v ? expf(sc - mx) : 0.f;
+  const float e = v ? expf(r.sc - mx) : 0.f;
   float sum = e;
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 16);
-  valid_k = (valid_mask >> k) & 1u;
-  j_k = __shfl(j, k, 64);
   return __shfl(e, k, 64) / __shfl(sum, 0, 64);  // lanes 0..15 hold the row
 }
 
@@ -585,12 +604,10 @@ __global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(Atte
 
   f32x16_t oacc[2] = {zero16(), zero16()};
   const float c2 = p.attn_scale * kLog2e;
+  const RowSlots rs = load_row_slots(p, rowbase, lane, has_row);
   for (int k = wave; k < p.K; k += kW) {  // wave-uniform
-    bool valid = false;
-    int32_t j = -1;
-    uint32_t vmask = 0;
-    float w = 0.f;
-    if (has_row) w = wave_slot_weight(p, rowbase, lane, k, valid, j, vmask);
+    bool valid;
+    const int32_t j = row_slot_chunk(p, rs, k, valid);
     float* lse_k = p.lse ? p.lse + slot_vec_offset(p, c.gbh, c.t, k) + 32 * half : nullptr;
     if (!valid) {
       if (lse_k && lane < 32) lse_k[lane] = -__builtin_inff();
@@ -598,6 +615,9 @@ __global__ __launch_bounds__(Wide<T>::kThreads) void attend_fwd_wide_kernel(Atte
     }
     tile_load_async<T, 1>(kv_tile<T>(p.k, p, c.b, c.h, j), region, 0);
     tile_load_async<T, 1>(kv_tile<T>(p.v, p, c.b, c.h, j), region + TL::kBytes, 0);
+    uint32_t vmask;
+    float w = row_slot_weight(p, rs, k, vmask);  // while the tiles are in flight
+    asm volatile("" : "+v"(w));  // (computed here, not sunk past the wait below)
     wait_async_copies();  // this wave's own copies: visible to it once they have landed
     const char* Ks = region;
     const char* Vs = region + TL::kBytes;
@@ -996,12 +1016,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_tokens_kernel(Attend
   const T* q = static_cast<const T*>(p.q) + gbh * static_cast<int64_t>(n_tok) * kDim;
   T* o = static_cast<T*>(p.o) + gbh * static_cast<int64_t>(n_tok) * kDim;
   const int rounds = (p.K + kDecodeWaves - 1) / kDecodeWaves;
+  const RowSlots rs = load_row_slots(p, rowbase, lane, has_row);
   uint32_t vmask = 0;  // valid slots of the row (wave-uniform, the same in every wave)
-  if (has_row) {
-    bool v0;
-    int32_t j0;
-    (void)wave_slot_weight(p, rowbase, lane, 0, v0, j0, vmask);
-  }
+  if (has_row) (void)row_slot_weight(p, rs, 0, vmask);
 
   for (int t0 = 0; t0 < n_tok; t0 += kDecodeBatch) {  // uniform over the workgroup
     const int nb = n_tok - t0 < kDecodeBatch ? n_tok - t0 : kDecodeBatch;
@@ -1014,9 +1031,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_tokens_kernel(Attend
       const int k = rd * kDecodeWaves + wave;
       bool valid = false;
       int32_t j = -1;
-      uint32_t vm_k = 0;
-      float w = 0.f;
-      if (has_row && k < p.K) w = wave_slot_weight(p, rowbase, lane, k, valid, j, vm_k);
+      if (k < p.K) j = row_slot_chunk(p, rs, k, valid);
       if (!valid) continue;  // wave-uniform
       const T* kt = kv_tile<T>(p.k, p, b, h, j);
       const T* vt = kv_tile<T>(p.v, p, b, h, j);
@@ -1025,6 +1040,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_tokens_kernel(Attend
       for (int d = 0; d < kDim; ++d) krow[d] = to_f32(kt[lane * kDim + d]);
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) vcol[u] = to_f32(vt[u * kDim + lane]);
+      uint32_t vm_k;
+      float w = row_slot_weight(p, rs, k, vm_k);  // while the tile loads are in flight
+      asm volatile("" : "+v"(w));
       for (int t = 0; t < nb; ++t) {
         float z = 0.f;
 #pragma unroll
