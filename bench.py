@@ -32,6 +32,14 @@ METRIC = "GCA fwd+bwd tokens/s at 16K ctx; per-chunk retrieve+attend latency at 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 UNIT_FLOPS = 2 * 64 * 64 * 64  # one 64x64x64 matrix product (one slot, one head)
+# The third ceiling of the attention passes, the exponential pipe: every pass takes one v_exp_f32
+# per score element (4,096 per tile).  A probe of independent v_exp_f32 chains measured 8.3 cycles
+# per wave instruction per SIMD with two waves per SIMD (one wave: 8.7), i.e. 64 / 8.3 results per
+# cycle per SIMD; over 1,024 SIMDs at the 2.4 GHz peak clock that is 1.89e13 per second.  Reported
+# beside the HBM and matrix-core fractions, not used as the roofline denominator.
+EXP_CYCLES_PER_WAVE_INSTR = 8.3
+PEAK_EXP_PER_S = 1024 * 64 / EXP_CYCLES_PER_WAVE_INSTR * 2.4e9
+EXPS_PER_TILE = 64 * 64
 
 
 def log(*a):
@@ -87,14 +95,15 @@ def kernel_figures(shape, idx_cpu):
     lmk = G * B * (nq + nkv) * 64 * 2
     sel = G * B * nq * K * 8
     pairs = G * B * nq * (nq - 1) // 2
+    ex = EXPS_PER_TILE * tiles                 # one exponential per score element and pass
     return {
         "score_topk": {"flops": 2 * 64 * pairs, "bytes": lmk + sel, "tiles": 0},
         # forward: S and PV per tile; reads Q, K, V, writes O and LSE
-        "attend_fwd": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + 1 + 1 + G) * T + lse + sel, "tiles": tiles},
+        "attend_fwd": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + 1 + 1 + G) * T + lse + sel, "tiles": tiles, "exps": ex},
         # query-major backward: dP' and dQ per tile; reads Q, dO, K, V, LSE, writes dQ
-        "bwd_query": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + G) * T + lse + sel, "tiles": tiles},
+        "bwd_query": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + G) * T + lse + sel, "tiles": tiles, "exps": ex},
         # key-major backward: dK and dV per tile; reads Q, dO, K, V, LSE, writes dK, dV
-        "bwd_key": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + 1 + 1) * T + lse, "tiles": tiles},
+        "bwd_key": {"flops": 2 * UNIT_FLOPS * tiles, "bytes": (G + G + 1 + 1 + 1 + 1) * T + lse, "tiles": tiles, "exps": ex},
         "inverse_index": {"flops": 0, "bytes": sel // 2, "tiles": 0},
         "score_grad": {"flops": 0, "bytes": sel, "tiles": 0},
     }
@@ -184,6 +193,9 @@ def both_ceilings(fig, ms, peaks):
     tf = fig["flops"] / t / 1e12
     out = {"avg_ms": ms, "hbm_gbs": tb, "hbm_frac": tb / PEAK_HBM_GBS, "mfma_tflops": tf,
            "mfma_frac": tf / PEAK_BF16_TFLOPS}
+    if fig.get("exps"):
+        out["exp_per_s"] = fig["exps"] / t
+        out["exp_frac"] = out["exp_per_s"] / PEAK_EXP_PER_S
     if peaks:
         out["hbm_frac_measured_peak"] = tb / peaks["hbm_copy_gbs"]
         out["mfma_frac_measured_peak"] = tf / peaks["bf16_gemm_tflops"]
@@ -882,7 +894,15 @@ def main():
             backward_kernels[name] = both_ceilings(figs[name], kern[name][0] / kern[name][1], peaks)
             c = backward_kernels[name]
             log(f"  {name:12s} HBM {c['hbm_gbs']:.0f} GB/s ({c['hbm_frac']:.3f}), matrix cores "
-                f"{c['mfma_tflops']:.0f} TFLOP/s ({c['mfma_frac']:.3f})")
+                f"{c['mfma_tflops']:.0f} TFLOP/s ({c['mfma_frac']:.3f}), exponentials "
+                f"{c.get('exp_per_s', 0) / 1e12:.2f} T/s ({c.get('exp_frac', 0):.3f})")
+    # the step against the exponential pipe alone: three passes of one exponential per element
+    step_exps = 3 * EXPS_PER_TILE * sr["tiles"]
+    roof["step_exps"] = step_exps
+    roof["step_exp_floor_us"] = step_exps / PEAK_EXP_PER_S * 1e6
+    roof["step_exp_frac"] = roof["step_exp_floor_us"] / (ms * 1e3)
+    log(f"  exponentials: {step_exps / 1e9:.2f} G per step, {roof['step_exp_floor_us']:.1f} us at the pipe's "
+        f"rate -> {roof['step_exp_frac']:.3f} of the step")
 
     log("landmark gradients (gca_landmark_backward) on the step's indices and d(score)")
     lmk = landmark_timing(shape, cfg, dev, bufs)
