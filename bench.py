@@ -461,6 +461,34 @@ def _timed(fn, iters, warmup=3):
     return a.elapsed_time(b) / iters, kern
 
 
+def tiny_forward_latency(iters=50):
+    """The tiny fp32 problem (B=1, L=1024 in 16 chunks, H=2, K=4, one group, no Gumbel): retrieve +
+    forward with the LSE, per call.  At this size the call is launch- and latency-bound; warm is
+    queued behind a spin kernel (GPU time), warm_host_launch submitted to an idle GPU."""
+    import torch
+
+    from long_context_lm_amd import gca
+    from long_context_lm_amd import inputs as I
+
+    shape = I.TINY_FP32
+    cfg = gca.Config(B=shape.B, G=shape.G, H=shape.H, n_q=shape.n_q, n_kv=shape.n_kv, topk=shape.topk,
+                     dtype="f32", q_chunk_base=shape.q_chunk_base, shift=shape.shift)
+    host = I.make_inputs(shape, "f32", seed=0, names=("lq", "lk", "q", "k", "v"))
+    d = {n: t.cuda() for n, t in host.items()}
+    idx = torch.empty((shape.G, shape.B, shape.n_q, shape.topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty_like(idx, dtype=torch.float32)
+
+    def one():
+        gca.retrieve(cfg, d["lq"], d["lk"], idx, sc)
+        gca.forward(cfg, d["q"], d["k"], d["v"], idx, sc)
+
+    for _ in range(5):
+        one()
+    torch.cuda.synchronize()
+    return {"workload": "GCA retrieve+fwd (with LSE), B=1 L=1024 (16 chunks) H=2 d=64 K=4 G=1, no Gumbel, fp32",
+            "warm": _latency(one, iters, _queue_ahead), "warm_host_launch": _latency(one, iters)}
+
+
 def forward_timing(iters=20):
     """The bf16 forward at the training shape with one retrieval group and no Gumbel noise
     (B=8, L=16384, H=12, K=8, G=1, inputs N(0,1)/8): gca_retrieve + gca_forward without the
@@ -933,6 +961,10 @@ def main():
     fz = fused_timing()
     log(f"  fused {fz['fused_us']:.1f} us, separate {fz['separate_us']:.1f} us per fwd+bwd; fused: "
         + ", ".join(f"{k} {v:.1f}" for k, v in fz["kernels_us_fused"].items()))
+    log("tiny fp32 problem (B=1, L=1024, H=2, K=4): retrieve + forward per call")
+    tiny = tiny_forward_latency()
+    log(f"  {tiny['warm']['median_us']:.1f} us warm, {tiny['warm_host_launch']['median_us']:.1f} us with the "
+        "host's launch")
     log("forward only at the training shape (G=1, no Gumbel, no LSE)")
     fwd = forward_timing()
     log(f"  {fwd['us_per_call']:.1f} us per call ({fwd['tokens_per_s'] / 1e6:.1f} M tokens/s), "
@@ -1003,6 +1035,7 @@ def main():
         "fused_window_gca": fz,
         "skewed_retrieval": skew,
         "forward_only": fwd,
+        "tiny_fp32_forward": tiny,
         "length_scaling": scaling,
     }
     print(json.dumps(out), flush=True)
